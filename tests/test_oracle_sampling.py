@@ -1,0 +1,86 @@
+"""Pins for the Step draw and the corruption (CPU only): identities and
+chi-square tests against the distributions they must produce."""
+import numpy as np
+import scipy.special
+import scipy.stats
+
+from oracle import corrupt, gumbel_noise, step_select
+
+
+def _chi2_p(counts, probs):
+    exp = probs * counts.sum()
+    return scipy.stats.chisquare(counts, exp).pvalue
+
+
+def test_gumbel_max_frequencies_follow_softmax():
+    V, n = 8, 40000
+    s = np.array([0.3, -1.0, 1.2, 0.0, 0.7, -0.4, 2.0, 0.1])
+    g = gumbel_noise(seed=11, b=np.zeros(n, np.int64), i=np.arange(n), V=V)
+    y = np.argmax(s.astype(np.float32)[None, :] + g, axis=1)
+    counts = np.bincount(y, minlength=V)
+    assert _chi2_p(counts, scipy.special.softmax(s)) > 1e-4
+    # a sign slip in the noise (+log(-log U)) gives a different law and fails
+    y_bad = np.argmax(s.astype(np.float32)[None, :] - g, axis=1)
+    assert _chi2_p(np.bincount(y_bad, minlength=V), scipy.special.softmax(s)) < 1e-6
+
+
+def test_step_draws_follow_mixture():
+    V, B = 8, 30000
+    s_row = np.array([0.5, -0.5, 1.5, 0.0, 1.0, -1.0, 0.2, 0.9])
+    lam = 0.35
+    x_t = np.full((B, 1), 3, dtype=np.int32)
+    s = np.tile(s_row, (B, 1))
+    r = step_select(x_t, s, np.full(B, lam, np.float32), seed=5, canvas_ids=np.arange(B))
+    probs = lam * scipy.special.softmax(s_row)
+    probs[3] += 1 - lam
+    assert np.all(probs >= 0) and abs(probs.sum() - 1) < 1e-12
+    counts = np.bincount(r["x_out"].ravel(), minlength=V)
+    assert _chi2_p(counts, probs) > 1e-4
+    assert abs(r["resample"].mean() - lam) < 4 * np.sqrt(lam * (1 - lam) / B)
+
+
+def test_step_lambda_zero_is_identity_and_one_resamples_all():
+    rng = np.random.default_rng(3)
+    B, C, V = 3, 50, 16
+    x_t = rng.integers(0, V, (B, C)).astype(np.int32)
+    s = rng.standard_normal((B * C, V))
+    r0 = step_select(x_t, s, np.zeros(B, np.float32), seed=1, canvas_ids=np.arange(B))
+    assert not r0["resample"].any() and np.array_equal(r0["x_out"], x_t)
+    r1 = step_select(x_t, s, np.ones(B, np.float32), seed=1, canvas_ids=np.arange(B))
+    assert r1["resample"].all()
+    assert np.array_equal(r1["x_out"], r1["best"])
+
+
+def test_exact_tie_goes_to_lowest_id():
+    # identical noise on every vocab entry is impossible, so build a tie in the
+    # perturbed values directly through the logits
+    V = 4
+    g = gumbel_noise(seed=2, b=np.array([0]), i=np.array([0]), V=V)[0]
+    s = (10.0 - g).astype(np.float64)                  # s + g == 10 for all v (float32)
+    pert = s.astype(np.float32) + g
+    assert np.all(pert == pert[0])
+    r = step_select(np.zeros((1, 1), np.int32), s[None, :], np.ones(1, np.float32), seed=2,
+                    canvas_ids=[0])
+    assert r["best"][0, 0] == 0
+
+
+def test_corruption_marginal_chi_square():
+    V, C = 16, 200000
+    x0 = np.full((1, C), 5, dtype=np.int32)
+    for kappa in [0.0, 0.3, 0.8]:
+        xt = corrupt(x0, np.array([kappa], np.float32), seed=9, V=V)
+        probs = np.full(V, (1 - kappa) / V)
+        probs[5] += kappa
+        assert _chi2_p(np.bincount(xt.ravel(), minlength=V), probs) > 1e-4
+
+
+def test_corruption_identity_at_kappa_one_and_independence_of_seed():
+    rng = np.random.default_rng(4)
+    x0 = rng.integers(0, 64, (3, 40)).astype(np.int32)
+    assert np.array_equal(corrupt(x0, np.ones(3, np.float32), 1, 64), x0)
+    a = corrupt(x0, np.zeros(3, np.float32), 1, 64)
+    b = corrupt(x0, np.zeros(3, np.float32), 2, 64)
+    assert not np.array_equal(a, b)
+    # canvas ids select counters: corrupting canvas 2 alone equals row 2 of the batch
+    c = corrupt(x0[2:3], np.zeros(1, np.float32), 1, 64, canvas_ids=[2])
+    assert np.array_equal(c[0], a[2])

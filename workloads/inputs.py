@@ -1,0 +1,95 @@
+"""Seeded input generation.
+
+One PCG64 stream per tensor, spawned from SeedSequence(cfg.seed) in a fixed
+order, so any tensor can be regenerated alone. Values for bf16 workloads are
+drawn in float32 and rounded to bfloat16 (round to nearest, ties to even);
+both sides then consume the same bits.
+"""
+import numpy as np
+
+STREAMS = ["E", "Wq", "Wk", "Wv", "Wo", "K_pre", "V_pre", "x", "t", "z_mask", "z"]
+
+
+def bf16_bits_from_f32(a):
+    """float32 array -> uint16 bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    bias = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    return ((u + bias) >> 16).astype(np.uint16)
+
+
+def f32_from_bf16_bits(b):
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _rng(cfg, name):
+    ss = np.random.SeedSequence(cfg.seed).spawn(len(STREAMS))[STREAMS.index(name)]
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+def _normal(cfg, name, shape, std):
+    a = _rng(cfg, name).standard_normal(size=shape, dtype=np.float32)
+    a *= np.float32(std)
+    return a
+
+
+class Inputs(dict):
+    """Dict of named arrays. For bf16 configs each float tensor is stored as
+    float32 values that are exactly bf16-representable, plus `<name>_bits`."""
+
+
+def make_inputs(cfg, which=None):
+    """Return the seeded inputs of `cfg`.
+
+    Layouts (row-major): E [V, d]; Wq [Hq*hd, d]; Wk, Wv [Hkv*hd, d];
+    Wo [d, Hq*hd]; K_pre, V_pre [B, Hkv, P, hd]; x [B, C] int32;
+    z [B, C, d]; t [B] float32 (per-canvas t when the config asks for it).
+    """
+    names = which or ["E", "Wq", "Wk", "Wv", "Wo", "K_pre", "V_pre", "x", "t", "z"]
+    out = Inputs()
+    hq, hkv, hd = cfg.n_q_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim, cfg.head_dim
+    shapes = {
+        "E": ((cfg.V, cfg.d), cfg.w_std),
+        "Wq": ((hq, cfg.d), cfg.w_std),
+        "Wk": ((hkv, cfg.d), cfg.w_std),
+        "Wv": ((hkv, cfg.d), cfg.w_std),
+        "Wo": ((cfg.d, hq), cfg.w_std),
+        "K_pre": ((cfg.B, cfg.n_kv_heads, cfg.P, hd), cfg.kv_std),
+        "V_pre": ((cfg.B, cfg.n_kv_heads, cfg.P, hd), cfg.kv_std),
+    }
+    for n in names:
+        if n in shapes:
+            shape, std = shapes[n]
+            a = _normal(cfg, n, shape, std)
+            if cfg.dtype == "bf16":
+                bits = bf16_bits_from_f32(a)
+                out[n + "_bits"] = bits
+                a = f32_from_bf16_bits(bits).reshape(shape)
+            out[n] = a
+        elif n == "x":
+            out["x"] = _rng(cfg, "x").integers(0, cfg.V, size=(cfg.B, cfg.C), dtype=np.int64).astype(np.int32)
+        elif n == "t":
+            if cfg.per_canvas_t:
+                # uniform on (0, 1]: 1 - U[0, 1)
+                u = _rng(cfg, "t").random(cfg.B)
+                out["t"] = (1.0 - u).astype(np.float32)
+            else:
+                out["t"] = np.ones(cfg.B, dtype=np.float32)
+        elif n == "z":
+            # Self-conditioning input. Zero everywhere unless the config zeroes a
+            # seeded half: then the other half carries a synthetic previous-pass
+            # signal drawn at the scale of an embedding row.
+            z = np.zeros((cfg.B, cfg.C, cfg.d), dtype=np.float32)
+            if cfg.zero_z_half:
+                keep = np.zeros(cfg.B, dtype=bool)
+                keep[_rng(cfg, "z_mask").permutation(cfg.B)[: cfg.B // 2]] = True
+                zz = _normal(cfg, "z", (int(keep.sum()), cfg.C, cfg.d), cfg.w_std)
+                z[keep] = zz
+                out["z_nonzero"] = keep
+            if cfg.dtype == "bf16":
+                bits = bf16_bits_from_f32(z)
+                out["z_bits"] = bits
+                z = f32_from_bf16_bits(bits).reshape(z.shape)
+            out["z"] = z
+        else:
+            raise KeyError(n)
+    return out
