@@ -1,0 +1,185 @@
+"""ctypes binding of libdg (include/dg.h). Argument marshalling only.
+
+Tensors are torch tensors on the GPU; their data pointers cross the ABI. A
+missing library raises at import time: there is no fallback path.
+"""
+import ctypes
+import os
+
+DG_OK, DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_HIP, DG_ERR_OOM = 0, 1, 2, 3, 4
+DG_DTYPE_F32, DG_DTYPE_BF16 = 0, 1
+DG_SCHEDULE_LINEAR, DG_SCHEDULE_COSINE = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path():
+    return os.environ.get("DG_LIBRARY", os.path.join(_HERE, "libdg.so"))
+
+
+class dg_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ["B", "C", "P", "d", "n_q_heads", "n_kv_heads", "head_dim", "V", "dtype", "schedule"]]
+
+
+class dg_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ["E", "Wq", "Wk", "Wv", "Wo"]]
+
+
+class dg_taps(ctypes.Structure):
+    _fields_ = [("h0", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("o", ctypes.c_void_p), ("h1", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p), ("p0", ctypes.c_void_p), ("best", ctypes.c_void_p)]
+
+
+EXPORTS = ["dg_create", "dg_destroy", "dg_workspace_bytes", "dg_corrupt", "dg_corrupt_batch",
+           "dg_denoise_step", "dg_denoise_step_taps", "dg_generate_canvas", "dg_status_string",
+           "dg_last_error"]
+
+_lib = None
+
+
+def load_library():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"libdg.so not found at {path}: build it with "
+                          "`python -m discrete_diffusion_decoding_dg_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, u64, i32, f32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_float
+    lib.dg_create.argtypes = [ctypes.POINTER(dg_config), ctypes.POINTER(dg_weights), ctypes.POINTER(vp)]
+    lib.dg_destroy.argtypes = [vp]
+    lib.dg_workspace_bytes.argtypes = [ctypes.POINTER(dg_config), ctypes.POINTER(ctypes.c_size_t)]
+    lib.dg_corrupt.argtypes = [vp, vp, ctypes.POINTER(f32), u64, vp, vp]
+    lib.dg_corrupt_batch.argtypes = [vp, vp, i32, i32, i32, u64, vp, vp]
+    lib.dg_denoise_step.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(f32), f32, u64, vp, vp, vp, vp, vp]
+    lib.dg_denoise_step_taps.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(f32), f32, u64, vp, vp,
+                                         ctypes.POINTER(dg_taps), vp]
+    lib.dg_generate_canvas.argtypes = [vp, vp, vp, i32, u64, vp, vp, vp]
+    lib.dg_status_string.argtypes = [ctypes.c_int]
+    lib.dg_status_string.restype = ctypes.c_char_p
+    lib.dg_last_error.restype = ctypes.c_char_p
+    for n in EXPORTS:
+        if n not in ("dg_status_string", "dg_last_error"):
+            getattr(lib, n).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+class DgError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{dg_status_string(status)}: {message}")
+        self.status = status
+
+
+def dg_status_string(status):
+    return load_library().dg_status_string(int(status)).decode()
+
+
+def dg_last_error():
+    return load_library().dg_last_error().decode()
+
+
+def _check(status):
+    if status != DG_OK:
+        raise DgError(status, dg_last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _floats(values):
+    vals = [float(v) for v in values]
+    return (ctypes.c_float * max(1, len(vals)))(*vals)
+
+
+def make_config(B, C, P, d, n_q_heads, n_kv_heads, head_dim, V, dtype, schedule):
+    return dg_config(B, C, P, d, n_q_heads, n_kv_heads, head_dim, V, dtype, schedule)
+
+
+class Model:
+    """Owns a dg_model handle and keeps the weight tensors alive."""
+
+    def __init__(self, handle, cfg, weights):
+        self.handle = handle
+        self.cfg = cfg
+        self._weights = weights
+
+    def close(self):
+        if self.handle:
+            _check(load_library().dg_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def dg_workspace_bytes(cfg):
+    n = ctypes.c_size_t(0)
+    _check(load_library().dg_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def dg_create(cfg, E, Wq, Wk, Wv, Wo):
+    w = dg_weights(*[t.data_ptr() if t is not None else None for t in (E, Wq, Wk, Wv, Wo)])
+    h = ctypes.c_void_p()
+    _check(load_library().dg_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)))
+    return Model(h, cfg, (E, Wq, Wk, Wv, Wo))
+
+
+def dg_destroy(model):
+    model.close()
+
+
+def dg_corrupt(model, x0, kappa, seed, xt_out, stream=None):
+    _check(load_library().dg_corrupt(model.handle, _ptr(x0), _floats(kappa), int(seed),
+                                     _ptr(xt_out), _stream(stream)))
+
+
+def dg_corrupt_batch(x0, kappa_dev, B, C, V, seed, xt_out, stream=None):
+    _check(load_library().dg_corrupt_batch(_ptr(x0), _ptr(kappa_dev), int(B), int(C), int(V),
+                                           int(seed), _ptr(xt_out), _stream(stream)))
+
+
+def dg_denoise_step(model, x_t, z_t, K_pre, V_pre, t, dt, seed, x_out, z_out, lse_out=None,
+                    p0_out=None, stream=None):
+    _check(load_library().dg_denoise_step(model.handle, _ptr(x_t), _ptr(z_t), _ptr(K_pre),
+                                          _ptr(V_pre), _floats(t), float(dt), int(seed),
+                                          _ptr(x_out), _ptr(z_out), _ptr(lse_out), _ptr(p0_out),
+                                          _stream(stream)))
+
+
+def dg_denoise_step_taps(model, x_t, z_t, K_pre, V_pre, t, dt, seed, x_out, z_out, taps=None,
+                         stream=None):
+    """`taps` maps any of h0, q, k, v, o, h1, lse, p0, best to output tensors."""
+    tp = None
+    if taps:
+        tp = dg_taps(**{k: (v.data_ptr() if v is not None else None) for k, v in taps.items()})
+    _check(load_library().dg_denoise_step_taps(model.handle, _ptr(x_t), _ptr(z_t), _ptr(K_pre),
+                                               _ptr(V_pre), _floats(t), float(dt), int(seed),
+                                               _ptr(x_out), _ptr(z_out),
+                                               ctypes.byref(tp) if tp is not None else None,
+                                               _stream(stream)))
+
+
+def dg_generate_canvas(model, K_pre, V_pre, steps, seed, x_out, z_out=None, stream=None):
+    _check(load_library().dg_generate_canvas(model.handle, _ptr(K_pre), _ptr(V_pre), int(steps),
+                                             int(seed), _ptr(x_out), _ptr(z_out), _stream(stream)))
+
+
+load_library()

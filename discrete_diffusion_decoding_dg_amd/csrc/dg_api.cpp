@@ -1,0 +1,452 @@
+// libdg C ABI: argument checking, workspace ownership and launch order of the
+// denoising step. Declarations and the contract live in include/dg.h.
+#include "dg.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "dg_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+dg_status fail(dg_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+dg_status hip_fail(hipError_t e, const char *what) {
+  return fail(DG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define DG_HIP(call, what)                  \
+  do {                                      \
+    hipError_t e_ = (call);                 \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+constexpr int kMaxSteps = 4096;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void *a, size_t an, const void *b, size_t bn) {
+  const char *pa = static_cast<const char *>(a), *pb = static_cast<const char *>(b);
+  return pa < pb + bn && pb < pa + an;
+}
+
+dg::Shape shape_of(const dg_config &c) {
+  return dg::Shape{c.B, c.C, c.P, c.d, c.n_q_heads, c.n_kv_heads, c.head_dim, c.V};
+}
+
+// Workspace layout, in carve order.
+struct Layout {
+  size_t h0, q, k, v, o, h1, attn, lm, prm, kappa, genx, genz, total;
+};
+
+Layout layout_of(const dg_config &c) {
+  const dg::Shape s = shape_of(c);
+  const size_t es = c.dtype == DG_DTYPE_BF16 ? 2 : 4;
+  const size_t R = static_cast<size_t>(s.R());
+  Layout L;
+  L.h0 = align_up(R * s.d * es);
+  L.q = align_up(R * s.Hq * s.hd * es);
+  L.k = align_up(R * s.Hkv * s.hd * es);
+  L.v = L.k;
+  L.o = L.q;
+  L.h1 = L.h0;
+  if (c.dtype == DG_DTYPE_BF16) {
+    L.attn = align_up(dg::attention_workspace_bytes(s));
+    L.lm = align_up(dg::lmhead_workspace_bytes(s));
+  } else {
+    L.attn = 0;
+    L.lm = align_up(dg::lmhead_f32_workspace_bytes(s));
+  }
+  L.prm = align_up(static_cast<size_t>(kMaxSteps) * s.B * sizeof(dg::StepParams));
+  L.kappa = align_up(static_cast<size_t>(s.B) * sizeof(float));
+  L.genx = align_up(2 * R * sizeof(int32_t));
+  L.genz = align_up(2 * R * s.d * es);
+  L.total = L.h0 + L.q + L.k + L.v + L.o + L.h1 + L.attn + L.lm + L.prm + L.kappa + L.genx + L.genz;
+  return L;
+}
+
+dg_status check_config(const dg_config *c) {
+  if (!c) return fail(DG_ERR_INVALID_ARG, "config is NULL");
+  if (c->B < 1 || c->C < 1 || c->P < 0 || c->d < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
+      c->head_dim < 1 || c->V < 2)
+    return fail(DG_ERR_INVALID_ARG,
+                "sizes must be positive (B=%d C=%d P=%d d=%d Hq=%d Hkv=%d hd=%d V=%d; P may be 0, V >= 2)",
+                c->B, c->C, c->P, c->d, c->n_q_heads, c->n_kv_heads, c->head_dim, c->V);
+  if (c->n_q_heads % c->n_kv_heads != 0)
+    return fail(DG_ERR_INVALID_ARG, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
+                c->n_q_heads, c->n_kv_heads);
+  if (c->dtype != DG_DTYPE_F32 && c->dtype != DG_DTYPE_BF16)
+    return fail(DG_ERR_INVALID_ARG, "dtype %d is neither DG_DTYPE_F32 nor DG_DTYPE_BF16", c->dtype);
+  if (c->schedule != DG_SCHEDULE_LINEAR && c->schedule != DG_SCHEDULE_COSINE)
+    return fail(DG_ERR_INVALID_ARG, "schedule %d is unknown", c->schedule);
+  const int64_t R = static_cast<int64_t>(c->B) * c->C;
+  const int64_t lim = int64_t(1) << 31;
+  if (R * c->d >= lim || R * c->n_q_heads * c->head_dim >= lim ||
+      static_cast<int64_t>(c->V) * c->d >= (int64_t(1) << 40) ||
+      static_cast<int64_t>(c->P) + c->C >= lim)
+    return fail(DG_ERR_INVALID_ARG, "sizes overflow the 32-bit row indexing (B*C*d must be < 2^31)");
+  const dg::Shape s = shape_of(*c);
+  if (c->dtype == DG_DTYPE_BF16) {
+    if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 176)
+      return fail(DG_ERR_UNSUPPORTED, "bf16 kernels support head_dim 64, 128, 176 (got %d)",
+                  c->head_dim);
+    if (!dg::lmhead_supported(s))
+      return fail(DG_ERR_UNSUPPORTED,
+                  "bf16 LM head supports d in {256, 512, 1024, 2048, 2816} and V %% 16 == 0 "
+                  "(got d=%d V=%d)", c->d, c->V);
+  } else {
+    if (c->d > 4096)
+      return fail(DG_ERR_UNSUPPORTED, "fp32 kernels support d <= 4096 (got %d)", c->d);
+    if (static_cast<int64_t>(c->P) + c->C > 16384)
+      return fail(DG_ERR_UNSUPPORTED, "fp32 attention supports P + C <= 16384 (got %d)",
+                  c->P + c->C);
+  }
+  return DG_OK;
+}
+
+// Per-canvas step constants, fp64 on the host, rounded to fp32.
+// Schedules: linear kappa = 1 - t; cosine kappa = cos^2(pi t / 2). The Step
+// weight is lambda = dt (-dkappa/dt) / (1 - kappa) clamped to [0, 1]; the
+// temperature is tau = 0.4 + 0.4 t (linear anneal 0.8 -> 0.4).
+dg::StepParams step_params(double t, double dt, int schedule) {
+  double rate, one_minus;
+  if (schedule == DG_SCHEDULE_LINEAR) {
+    rate = 1.0;
+    one_minus = t;
+  } else {
+    const double c = std::cos(0.5 * M_PI * t), s = std::sin(0.5 * M_PI * t);
+    rate = M_PI * s * c;
+    one_minus = s * s;
+  }
+  double lam = one_minus > 0.0 ? dt * rate / one_minus : 1.0;
+  lam = lam < 0.0 ? 0.0 : (lam > 1.0 ? 1.0 : lam);
+  dg::StepParams p;
+  p.lam = static_cast<float>(lam);
+  p.inv_tau = static_cast<float>(1.0 / (0.4 + 0.4 * t));
+  return p;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------- model state --
+struct dg_model {
+  dg_config cfg;
+  dg_weights w;
+  dg::Shape s;
+  int device;
+  Layout L;
+  char *ws;
+  void *h0, *q, *k, *v, *o, *h1, *attn, *lm;
+  dg::StepParams *prm;
+  float *kappa;
+  int32_t *genx;
+  char *genz;
+};
+
+namespace {
+
+dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void *Kp,
+                   const void *Vp, const dg::StepParams *prm, uint64_t seed, int32_t *x_out,
+                   void *z_out, const dg_taps *taps, float *lse, float *p0, hipStream_t st) {
+  const dg::Shape &s = m->s;
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  void *h0 = taps && taps->h0 ? taps->h0 : m->h0;
+  void *q = taps && taps->q ? taps->q : m->q;
+  void *k = taps && taps->k ? taps->k : m->k;
+  void *v = taps && taps->v ? taps->v : m->v;
+  void *o = taps && taps->o ? taps->o : m->o;
+  void *h1 = taps && taps->h1 ? taps->h1 : m->h1;
+  int32_t *best = taps ? taps->best : nullptr;
+  DG_HIP(dg::launch_embed(bf16, m->w.E, x_t, z_t, s.R(), s.d, s.V, h0, st), "embed launch");
+  if (bf16) {
+    using u16 = uint16_t;
+    DG_HIP(dg::launch_qkv_bf16(static_cast<const u16 *>(h0), static_cast<const u16 *>(m->w.Wq),
+                               static_cast<const u16 *>(m->w.Wk), static_cast<const u16 *>(m->w.Wv),
+                               s, static_cast<u16 *>(q), static_cast<u16 *>(k),
+                               static_cast<u16 *>(v), st),
+           "qkv launch");
+    DG_HIP(dg::launch_attention_bf16(static_cast<const u16 *>(q), static_cast<const u16 *>(k),
+                                     static_cast<const u16 *>(v), static_cast<const u16 *>(Kp),
+                                     static_cast<const u16 *>(Vp), s, m->attn,
+                                     static_cast<u16 *>(o), st),
+           "attention launch");
+    DG_HIP(dg::launch_oproj_bf16(static_cast<const u16 *>(o), static_cast<const u16 *>(m->w.Wo),
+                                 static_cast<const u16 *>(h0), s, static_cast<u16 *>(h1), st),
+           "out-projection launch");
+    DG_HIP(dg::launch_lmhead_bf16(static_cast<const u16 *>(h1), static_cast<const u16 *>(m->w.E),
+                                  x_t, prm, s, seed, m->lm, p0, st),
+           "LM head launch");
+    DG_HIP(dg::launch_combine(true, m->lm, dg::lmhead_splits(s), x_t, prm, s, seed, x_out, z_out,
+                              lse, best, st),
+           "combine launch");
+  } else {
+    DG_HIP(dg::launch_qkv_f32(static_cast<const float *>(h0), static_cast<const float *>(m->w.Wq),
+                              static_cast<const float *>(m->w.Wk),
+                              static_cast<const float *>(m->w.Wv), s, static_cast<float *>(q),
+                              static_cast<float *>(k), static_cast<float *>(v), st),
+           "qkv launch");
+    DG_HIP(dg::launch_attention_f32(static_cast<const float *>(q), static_cast<const float *>(k),
+                                    static_cast<const float *>(v), static_cast<const float *>(Kp),
+                                    static_cast<const float *>(Vp), s, static_cast<float *>(o), st),
+           "attention launch");
+    DG_HIP(dg::launch_oproj_f32(static_cast<const float *>(o), static_cast<const float *>(m->w.Wo),
+                                static_cast<const float *>(h0), s, static_cast<float *>(h1), st),
+           "out-projection launch");
+    DG_HIP(dg::launch_lmhead_f32(static_cast<const float *>(h1), static_cast<const float *>(m->w.E),
+                                 prm, s, seed, m->lm, p0, st),
+           "LM head launch");
+    DG_HIP(dg::launch_combine(false, m->lm, 1, x_t, prm, s, seed, x_out, z_out, lse, best, st),
+           "combine launch");
+  }
+  if (p0) {
+    if (!lse) return fail(DG_ERR_INVALID_ARG, "internal: p0 requires lse");
+    DG_HIP(dg::launch_p0_from_logits(p0, lse, s.R(), s.V, st), "p0 launch");
+  }
+  return DG_OK;
+}
+
+dg_status check_model(const dg_model *m) {
+  if (!m) return fail(DG_ERR_INVALID_ARG, "model is NULL");
+  int dev = -1;
+  if (hipGetDevice(&dev) == hipSuccess && dev != m->device)
+    return fail(DG_ERR_INVALID_ARG, "current device %d is not the model's device %d", dev, m->device);
+  return DG_OK;
+}
+
+dg_status check_times(const float *t, int B, float dt) {
+  if (!t) return fail(DG_ERR_INVALID_ARG, "t is NULL");
+  if (!std::isfinite(dt) || !(dt > 0.f) || dt > 1.f)
+    return fail(DG_ERR_INVALID_ARG, "dt must be in (0, 1] (got %g)", static_cast<double>(dt));
+  for (int b = 0; b < B; ++b)
+    if (!std::isfinite(t[b]) || !(t[b] > 0.f) || t[b] > 1.f)
+      return fail(DG_ERR_INVALID_ARG, "t[%d] must be in (0, 1] (got %g)", b, static_cast<double>(t[b]));
+  return DG_OK;
+}
+
+dg_status upload_params(dg_model *m, dg::StepParams *dst, const std::vector<dg::StepParams> &p,
+                        hipStream_t st) {
+  DG_HIP(dg::launch_set_params(dst, p.data(), static_cast<int>(p.size()), st), "parameter upload");
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dg_status_string(dg_status s) {
+  switch (s) {
+    case DG_OK: return "DG_OK";
+    case DG_ERR_INVALID_ARG: return "DG_ERR_INVALID_ARG";
+    case DG_ERR_UNSUPPORTED: return "DG_ERR_UNSUPPORTED";
+    case DG_ERR_HIP: return "DG_ERR_HIP";
+    case DG_ERR_OOM: return "DG_ERR_OOM";
+  }
+  return "DG_ERR_UNKNOWN";
+}
+
+const char *dg_last_error(void) { return g_err.c_str(); }
+
+dg_status dg_workspace_bytes(const dg_config *cfg, size_t *bytes) {
+  g_err.clear();
+  if (dg_status s = check_config(cfg)) return s;
+  if (!bytes) return fail(DG_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = layout_of(*cfg).total;
+  return DG_OK;
+}
+
+dg_status dg_create(const dg_config *cfg, const dg_weights *w, dg_model **out) {
+  g_err.clear();
+  if (dg_status s = check_config(cfg)) return s;
+  if (!w) return fail(DG_ERR_INVALID_ARG, "weights is NULL");
+  if (!out) return fail(DG_ERR_INVALID_ARG, "out is NULL");
+  if (!w->E || !w->Wq || !w->Wk || !w->Wv || !w->Wo)
+    return fail(DG_ERR_INVALID_ARG, "a weight pointer is NULL");
+  if (!aligned16(w->E) || !aligned16(w->Wq) || !aligned16(w->Wk) || !aligned16(w->Wv) ||
+      !aligned16(w->Wo))
+    return fail(DG_ERR_INVALID_ARG, "weight pointers must be 16-byte aligned");
+  int dev = 0;
+  DG_HIP(hipGetDevice(&dev), "hipGetDevice");
+  const Layout L = layout_of(*cfg);
+  char *ws = nullptr;
+  hipError_t e = hipMalloc(&ws, L.total);
+  if (e != hipSuccess) return fail(DG_ERR_OOM, "workspace of %zu bytes: %s", L.total, hipGetErrorString(e));
+  dg_model *m = new dg_model;
+  m->cfg = *cfg;
+  m->w = *w;
+  m->s = shape_of(*cfg);
+  m->device = dev;
+  m->L = L;
+  m->ws = ws;
+  char *p = ws;
+  m->h0 = p; p += L.h0;
+  m->q = p; p += L.q;
+  m->k = p; p += L.k;
+  m->v = p; p += L.v;
+  m->o = p; p += L.o;
+  m->h1 = p; p += L.h1;
+  m->attn = p; p += L.attn;
+  m->lm = p; p += L.lm;
+  m->prm = reinterpret_cast<dg::StepParams *>(p); p += L.prm;
+  m->kappa = reinterpret_cast<float *>(p); p += L.kappa;
+  m->genx = reinterpret_cast<int32_t *>(p); p += L.genx;
+  m->genz = p; p += L.genz;
+  *out = m;
+  return DG_OK;
+}
+
+dg_status dg_destroy(dg_model *m) {
+  g_err.clear();
+  if (!m) return DG_OK;
+  hipError_t e = hipDeviceSynchronize();
+  hipError_t f = hipFree(m->ws);
+  delete m;
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  if (f != hipSuccess) return hip_fail(f, "hipFree");
+  return DG_OK;
+}
+
+dg_status dg_corrupt_batch(const int32_t *x0, const float *kappa_dev, int32_t B, int32_t C,
+                           int32_t V, uint64_t seed, int32_t *xt_out, void *stream) {
+  g_err.clear();
+  if (!x0 || !kappa_dev || !xt_out) return fail(DG_ERR_INVALID_ARG, "a pointer is NULL");
+  if (B < 0 || C < 0 || V < 1) return fail(DG_ERR_INVALID_ARG, "B, C >= 0 and V >= 1 required");
+  const size_t n = static_cast<size_t>(B) * C * sizeof(int32_t);
+  if (x0 != xt_out && overlap(x0, n, xt_out, n))
+    return fail(DG_ERR_INVALID_ARG, "xt_out partially overlaps x0");
+  DG_HIP(dg::launch_corrupt(x0, kappa_dev, B, C, V, seed, xt_out, static_cast<hipStream_t>(stream)),
+         "corrupt launch");
+  return DG_OK;
+}
+
+dg_status dg_corrupt(dg_model *m, const int32_t *x0, const float *kappa, uint64_t seed,
+                     int32_t *xt_out, void *stream) {
+  g_err.clear();
+  if (dg_status s = check_model(m)) return s;
+  if (!x0 || !kappa || !xt_out) return fail(DG_ERR_INVALID_ARG, "a pointer is NULL");
+  const int B = m->s.B, C = m->s.C;
+  for (int b = 0; b < B; ++b)
+    if (!std::isfinite(kappa[b]) || kappa[b] < 0.f || kappa[b] > 1.f)
+      return fail(DG_ERR_INVALID_ARG, "kappa[%d] must be in [0, 1] (got %g)", b,
+                  static_cast<double>(kappa[b]));
+  const size_t n = static_cast<size_t>(B) * C * sizeof(int32_t);
+  if (overlap(x0, n, xt_out, n)) return fail(DG_ERR_INVALID_ARG, "xt_out overlaps x0");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DG_HIP(dg::launch_set_floats(m->kappa, kappa, B, st), "kappa upload");
+  DG_HIP(dg::launch_corrupt(x0, m->kappa, B, C, m->s.V, seed, xt_out, st), "corrupt launch");
+  return DG_OK;
+}
+
+dg_status dg_denoise_step_taps(dg_model *m, const int32_t *x_t, const void *z_t,
+                               const void *K_pre, const void *V_pre, const float *t, float dt,
+                               uint64_t seed, int32_t *x_out, void *z_out, const dg_taps *taps,
+                               void *stream) {
+  g_err.clear();
+  if (dg_status s = check_model(m)) return s;
+  const dg::Shape &s = m->s;
+  if (!x_t || !z_t || !x_out || !z_out) return fail(DG_ERR_INVALID_ARG, "x_t, z_t, x_out and z_out must be non-NULL");
+  if (s.P > 0 && (!K_pre || !V_pre)) return fail(DG_ERR_INVALID_ARG, "K_pre and V_pre must be non-NULL when P > 0");
+  if (dg_status e = check_times(t, s.B, dt)) return e;
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  const size_t es = bf16 ? 2 : 4;
+  const size_t nx = static_cast<size_t>(s.R()) * sizeof(int32_t);
+  const size_t nz = static_cast<size_t>(s.R()) * s.d * es;
+  if (overlap(x_out, nx, x_t, nx)) return fail(DG_ERR_INVALID_ARG, "x_out overlaps x_t");
+  if (overlap(z_out, nz, z_t, nz)) return fail(DG_ERR_INVALID_ARG, "z_out overlaps z_t");
+  if (bf16 && (!aligned16(z_t) || !aligned16(z_out) || (K_pre && !aligned16(K_pre)) ||
+               (V_pre && !aligned16(V_pre))))
+    return fail(DG_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+  if (taps && taps->p0 && !taps->lse)
+    return fail(DG_ERR_INVALID_ARG, "taps->p0 requires taps->lse");
+  if (taps && bf16) {
+    const void *tp[6] = {taps->h0, taps->q, taps->k, taps->v, taps->o, taps->h1};
+    for (const void *p : tp)
+      if (p && !aligned16(p)) return fail(DG_ERR_INVALID_ARG, "bf16 taps must be 16-byte aligned");
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::vector<dg::StepParams> prm(s.B);
+  for (int b = 0; b < s.B; ++b) prm[b] = step_params(t[b], dt, m->cfg.schedule);
+  if (dg_status e = upload_params(m, m->prm, prm, st)) return e;
+  return run_step(m, x_t, z_t, K_pre, V_pre, m->prm, seed, x_out, z_out, taps,
+                  taps ? taps->lse : nullptr, taps ? taps->p0 : nullptr, st);
+}
+
+dg_status dg_denoise_step(dg_model *m, const int32_t *x_t, const void *z_t, const void *K_pre,
+                          const void *V_pre, const float *t, float dt, uint64_t seed,
+                          int32_t *x_out, void *z_out, float *lse_out, float *p0_out,
+                          void *stream) {
+  g_err.clear();
+  if (p0_out && !lse_out) return fail(DG_ERR_INVALID_ARG, "p0_out requires lse_out");
+  dg_taps taps;
+  std::memset(&taps, 0, sizeof(taps));
+  taps.lse = lse_out;
+  taps.p0 = p0_out;
+  return dg_denoise_step_taps(m, x_t, z_t, K_pre, V_pre, t, dt, seed, x_out, z_out, &taps, stream);
+}
+
+dg_status dg_generate_canvas(dg_model *m, const void *K_pre, const void *V_pre, int32_t steps,
+                             uint64_t seed, int32_t *x_out, void *z_out, void *stream) {
+  g_err.clear();
+  if (dg_status s = check_model(m)) return s;
+  const dg::Shape &s = m->s;
+  if (!x_out) return fail(DG_ERR_INVALID_ARG, "x_out is NULL");
+  if (s.P > 0 && (!K_pre || !V_pre)) return fail(DG_ERR_INVALID_ARG, "K_pre and V_pre must be non-NULL when P > 0");
+  if (steps < 1 || steps > kMaxSteps)
+    return fail(DG_ERR_INVALID_ARG, "steps must be in [1, %d] (got %d)", kMaxSteps, steps);
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  if (bf16 && ((K_pre && !aligned16(K_pre)) || (V_pre && !aligned16(V_pre)) ||
+               (z_out && !aligned16(z_out))))
+    return fail(DG_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+  const size_t es = bf16 ? 2 : 4;
+  const size_t R = static_cast<size_t>(s.R());
+  const size_t nz = R * s.d * es;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  // per-step constants for every canvas, uploaded once
+  std::vector<dg::StepParams> prm(static_cast<size_t>(steps) * s.B);
+  const float dt = static_cast<float>(1.0 / steps);
+  for (int k = 0; k < steps; ++k) {
+    const float tk = static_cast<float>(1.0 - static_cast<double>(k) / steps);
+    const dg::StepParams p = step_params(tk, dt, m->cfg.schedule);
+    for (int b = 0; b < s.B; ++b) prm[static_cast<size_t>(k) * s.B + b] = p;
+  }
+  if (dg_status e = upload_params(m, m->prm, prm, st)) return e;
+
+  int32_t *xb[2] = {m->genx, m->genx + R};
+  char *zb[2] = {m->genz, m->genz + nz};
+  // x_init: corruption of a zero canvas at kappa = 0 (every token uniform)
+  DG_HIP(dg::launch_fill_zero(m->kappa, align_up(s.B * sizeof(float)), st), "fill");
+  DG_HIP(dg::launch_fill_zero(xb[0], R * sizeof(int32_t), st), "fill");
+  DG_HIP(dg::launch_corrupt(xb[0], m->kappa, s.B, s.C, s.V, seed, xb[0], st), "corrupt launch");
+  DG_HIP(dg::launch_fill_zero(zb[0], nz, st), "fill");
+  for (int k = 0; k < steps; ++k) {
+    const int cur = k & 1, nxt = cur ^ 1;
+    const bool last = k == steps - 1;
+    int32_t *xo = last ? x_out : xb[nxt];
+    void *zo = (last && z_out) ? z_out : zb[nxt];
+    if (dg_status e = run_step(m, xb[cur], zb[cur], K_pre, V_pre, m->prm + static_cast<size_t>(k) * s.B,
+                               seed + static_cast<uint64_t>(k), xo, zo, nullptr, nullptr, nullptr, st))
+      return e;
+  }
+  return DG_OK;
+}
+
+}  // extern "C"

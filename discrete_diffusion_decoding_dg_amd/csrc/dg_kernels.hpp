@@ -1,0 +1,92 @@
+// Host-side launchers of the gfx950 kernels (internal to libdg).
+// Every launcher checks nothing: dg_api.cpp validates shapes and pointers
+// before calling them. All pointers are device pointers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+// Per-canvas constants of one step, computed on the host in fp64 and rounded
+// to fp32: lambda_b (Step mixing weight) and 1/tau_b (logit scale).
+struct StepParams {
+  float lam;
+  float inv_tau;
+};
+
+// Shapes of the decoder stand-in.
+struct Shape {
+  int B, C, P, d, Hq, Hkv, hd, V;
+  int R() const { return B * C; }
+  int G() const { return Hq / Hkv; }
+};
+
+// Partial results of the split-V LM head, one record per (split, row).
+struct RowPartial {
+  float m;        // reference max of the scaled logits in log2 units
+  float l;        // sum of exp2(s*log2e - m) over the split
+  float best;     // best Gumbel-perturbed logit (natural units), -inf if none
+  int32_t arg;    // its vocab id (lowest on ties), -1 if none
+};
+
+// ---- k_elementwise.hip ----
+hipError_t launch_corrupt(const int32_t *x0, const float *kappa, int B, int C, int V,
+                          uint64_t seed, int32_t *out, hipStream_t st);
+// h0 = round(E[x] + z); z may be null (treated as 0); tokens outside [0, V)
+// embed as a zero row.
+hipError_t launch_embed(bool bf16, const void *E, const int32_t *x, const void *z, int R, int d,
+                        int V, void *h0, hipStream_t st);
+// p0[r, v] = exp(p0[r, v] - lse[r]) in place (p0 holds scaled logits on entry).
+hipError_t launch_p0_from_logits(float *p0, const float *lse, int R, int V, hipStream_t st);
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
+// Copy small host arrays to device memory through kernel arguments.
+hipError_t launch_set_params(StepParams *dst, const StepParams *src, int n, hipStream_t st);
+hipError_t launch_set_floats(float *dst, const float *src, int n, hipStream_t st);
+
+// ---- k_gemm.hip (bf16 MFMA) ----
+// q [R, Hq*hd], k/v [B, Hkv, C, hd] = h0 W^T for the three weights.
+hipError_t launch_qkv_bf16(const uint16_t *h0, const uint16_t *Wq, const uint16_t *Wk,
+                           const uint16_t *Wv, const Shape &s, uint16_t *q, uint16_t *k,
+                           uint16_t *v, hipStream_t st);
+// h1 [R, d] = h0 + o Wo^T.
+hipError_t launch_oproj_bf16(const uint16_t *o, const uint16_t *Wo, const uint16_t *h0,
+                             const Shape &s, uint16_t *h1, hipStream_t st);
+
+// ---- k_attention.hip (bf16 MFMA) ----
+int attention_splits(const Shape &s);
+size_t attention_workspace_bytes(const Shape &s);
+hipError_t launch_attention_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                 const uint16_t *Kp, const uint16_t *Vp, const Shape &s,
+                                 void *work, uint16_t *o, hipStream_t st);
+
+// ---- k_lmhead.hip (bf16 MFMA) ----
+bool lmhead_supported(const Shape &s);
+int lmhead_splits(const Shape &s);
+size_t lmhead_workspace_bytes(const Shape &s);
+// Fused LM head over V splits; writes RowPartial [splits, R] and z partials
+// [splits, R, d] fp32 into `work`, and raw scaled logits into p0 when non-null.
+hipError_t launch_lmhead_bf16(const uint16_t *h1, const uint16_t *E, const int32_t *x_t,
+                              const StepParams *prm, const Shape &s, uint64_t seed, void *work,
+                              float *p0, hipStream_t st);
+
+// ---- k_fp32.hip (fp32 VALU path, any shape) ----
+hipError_t launch_qkv_f32(const float *h0, const float *Wq, const float *Wk, const float *Wv,
+                          const Shape &s, float *q, float *k, float *v, hipStream_t st);
+hipError_t launch_attention_f32(const float *q, const float *k, const float *v, const float *Kp,
+                                const float *Vp, const Shape &s, float *o, hipStream_t st);
+hipError_t launch_oproj_f32(const float *o, const float *Wo, const float *h0, const Shape &s,
+                            float *h1, hipStream_t st);
+size_t lmhead_f32_workspace_bytes(const Shape &s);
+hipError_t launch_lmhead_f32(const float *h1, const float *E, const StepParams *prm,
+                             const Shape &s, uint64_t seed, void *work, float *p0,
+                             hipStream_t st);
+
+// ---- k_combine.hip ----
+// Merge the split partials of the LM head, draw the Step and finish z:
+// x_out, z_out (act), lse, best (each optional except x_out/z_out).
+hipError_t launch_combine(bool bf16, const void *work, int splits, const int32_t *x_t,
+                          const StepParams *prm, const Shape &s, uint64_t seed, int32_t *x_out,
+                          void *z_out, float *lse, int32_t *best, hipStream_t st);
+
+}  // namespace dg

@@ -1,0 +1,206 @@
+// Bandwidth-bound kernels: forward corruption, embedding + self-conditioning,
+// p0 materialisation for checking, and a fill.
+#include "dg_device.hpp"
+#include "dg_kernels.hpp"
+
+namespace dg {
+
+// Forward corruption (DiffusionGemma Technical Report, hyper.ai summary,
+// Method, forward path equation): each token keeps x0 with probability kappa_b
+// and is otherwise a uniform token over [0, V). One Philox block serves the
+// token pair (2j, 2j+1) of a canvas: words 0/1 for the even token, 2/3 for the
+// odd one (keep draw, replacement word).
+__global__ void __launch_bounds__(256) corrupt_kernel(const int32_t *__restrict__ x0,
+                                                      const float *__restrict__ kappa, int B,
+                                                      int C, uint32_t V, uint32_t k0, uint32_t k1,
+                                                      int32_t *__restrict__ out, bool vec2) {
+  const uint32_t pairs = (static_cast<uint32_t>(C) + 1u) >> 1;
+  const uint64_t total = static_cast<uint64_t>(B) * pairs;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+  for (uint64_t p = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; p < total;
+       p += stride) {
+    const uint32_t b = static_cast<uint32_t>(p / pairs);
+    const uint32_t j = static_cast<uint32_t>(p - static_cast<uint64_t>(b) * pairs);
+    const u32x4 w = philox4x32_10(j, 0u, b, kStreamCorrupt, k0, k1);
+    const float kap = kappa[b];
+    const int64_t base = static_cast<int64_t>(b) * C + 2 * static_cast<int64_t>(j);
+    if (vec2) {  // C even and 8-byte aligned rows: one 8-byte load and store
+      const int2 xv = *reinterpret_cast<const int2 *>(x0 + base);
+      int2 r;
+      r.x = (u01(w.x) < kap) ? xv.x : static_cast<int32_t>(__umulhi(w.y, V));
+      r.y = (u01(w.z) < kap) ? xv.y : static_cast<int32_t>(__umulhi(w.w, V));
+      *reinterpret_cast<int2 *>(out + base) = r;
+    } else {
+      const int32_t xa = x0[base];
+      out[base] = (u01(w.x) < kap) ? xa : static_cast<int32_t>(__umulhi(w.y, V));
+      if (2 * j + 1 < static_cast<uint32_t>(C)) {
+        const int32_t xb = x0[base + 1];
+        out[base + 1] = (u01(w.z) < kap) ? xb : static_cast<int32_t>(__umulhi(w.w, V));
+      }
+    }
+  }
+}
+
+hipError_t launch_corrupt(const int32_t *x0, const float *kappa, int B, int C, int V,
+                          uint64_t seed, int32_t *out, hipStream_t st) {
+  const uint64_t pairs = static_cast<uint64_t>(B) * ((C + 1) / 2);
+  const bool vec2 = (C % 2 == 0) && (reinterpret_cast<uintptr_t>(x0) % 8 == 0) &&
+                    (reinterpret_cast<uintptr_t>(out) % 8 == 0);
+  uint64_t blocks = (pairs + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;  // grid-stride beyond 64 blocks per CU
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(corrupt_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, x0,
+                     kappa, B, C, static_cast<uint32_t>(V), static_cast<uint32_t>(seed),
+                     static_cast<uint32_t>(seed >> 32), out, vec2);
+  return hipGetLastError();
+}
+
+// h0 = round(E[x] + z): one block per row, 8 elements (16 bytes of bf16) per
+// thread and iteration when the row width allows it.
+// A token outside [0, V) reads as a zero embedding row instead of faulting.
+template <typename T>
+__global__ void __launch_bounds__(256) embed_kernel(const T *__restrict__ E,
+                                                    const int32_t *__restrict__ x,
+                                                    const T *__restrict__ z, int d, int V,
+                                                    T *__restrict__ h0) {
+  const int r = blockIdx.x;
+  const int32_t tok = x[r];
+  const bool in = tok >= 0 && tok < V;
+  const T *er = E + static_cast<int64_t>(in ? tok : 0) * d;
+  const T *zr = z ? z + static_cast<int64_t>(r) * d : nullptr;
+  T *hr = h0 + static_cast<int64_t>(r) * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+    float v = in ? Act<T>::load(er, c) : 0.f;
+    if (zr) v += Act<T>::load(zr, c);
+    Act<T>::store(hr, c, v);
+  }
+}
+
+__global__ void __launch_bounds__(256) embed_bf16_vec_kernel(const uint16_t *__restrict__ E,
+                                                             const int32_t *__restrict__ x,
+                                                             const uint16_t *__restrict__ z,
+                                                             int d, int V,
+                                                             uint16_t *__restrict__ h0) {
+  const int r = blockIdx.x;
+  const int32_t tok = x[r];
+  const bool in = tok >= 0 && tok < V;
+  const uint4 *er = reinterpret_cast<const uint4 *>(E + static_cast<int64_t>(in ? tok : 0) * d);
+  const uint4 *zr = z ? reinterpret_cast<const uint4 *>(z + static_cast<int64_t>(r) * d) : nullptr;
+  uint4 *hr = reinterpret_cast<uint4 *>(h0 + static_cast<int64_t>(r) * d);
+  for (int c = threadIdx.x; c < d / 8; c += blockDim.x) {
+    const uint4 e = in ? er[c] : make_uint4(0, 0, 0, 0);
+    uint4 o = e;
+    if (zr) {
+      const uint4 zz = zr[c];
+      const uint32_t ew[4] = {e.x, e.y, e.z, e.w};
+      const uint32_t zw[4] = {zz.x, zz.y, zz.z, zz.w};
+      uint32_t ow[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = bf16_to_f32(ew[i] & 0xFFFFu) + bf16_to_f32(zw[i] & 0xFFFFu);
+        const float hi = bf16_to_f32(ew[i] >> 16) + bf16_to_f32(zw[i] >> 16);
+        ow[i] = pack_bf16x2(lo, hi);
+      }
+      o = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    }
+    hr[c] = o;
+  }
+}
+
+hipError_t launch_embed(bool bf16, const void *E, const int32_t *x, const void *z, int R, int d,
+                        int V, void *h0, hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  if (bf16) {
+    if (d % 8 == 0)
+      hipLaunchKernelGGL(embed_bf16_vec_kernel, dim3(R), dim3(256), 0, st,
+                         static_cast<const uint16_t *>(E), x, static_cast<const uint16_t *>(z), d,
+                         V, static_cast<uint16_t *>(h0));
+    else
+      hipLaunchKernelGGL(embed_kernel<uint16_t>, dim3(R), dim3(256), 0, st,
+                         static_cast<const uint16_t *>(E), x, static_cast<const uint16_t *>(z), d,
+                         V, static_cast<uint16_t *>(h0));
+  } else {
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(R), dim3(256), 0, st,
+                       static_cast<const float *>(E), x, static_cast<const float *>(z), d,
+                       V, static_cast<float *>(h0));
+  }
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) p0_kernel(float *__restrict__ p0,
+                                                 const float *__restrict__ lse, int V) {
+  const int r = blockIdx.y;
+  const float l = lse[r];
+  float *row = p0 + static_cast<int64_t>(r) * V;
+  for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < V; v += gridDim.x * blockDim.x)
+    row[v] = expf(row[v] - l);
+}
+
+hipError_t launch_p0_from_logits(float *p0, const float *lse, int R, int V, hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  int bx = (V + 255) / 256;
+  if (bx > 64) bx = 64;
+  hipLaunchKernelGGL(p0_kernel, dim3(bx, R), dim3(256), 0, st, p0, lse, V);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(uint32_t *__restrict__ p, size_t n) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st) {
+  // bytes is a multiple of 4 for every caller (fp32 or bf16 pairs of even width)
+  const size_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st,
+                     static_cast<uint32_t *>(p), n);
+  return hipGetLastError();
+}
+
+// Small host arrays travel as kernel arguments (copied at launch), so no host
+// buffer has to outlive the call and no pinned memory is needed.
+struct ParamChunk {
+  StepParams p[256];
+};
+struct FloatChunk {
+  float f[512];
+};
+
+__global__ void set_params_kernel(StepParams *__restrict__ dst, ParamChunk c, int n) {
+  const int i = threadIdx.x;
+  if (i < n) dst[i] = c.p[i];
+}
+
+__global__ void set_floats_kernel(float *__restrict__ dst, FloatChunk c, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = c.f[i];
+}
+
+hipError_t launch_set_params(StepParams *dst, const StepParams *src, int n, hipStream_t st) {
+  for (int off = 0; off < n; off += 256) {
+    ParamChunk c;
+    const int k = (n - off < 256) ? n - off : 256;
+    for (int i = 0; i < k; ++i) c.p[i] = src[off + i];
+    hipLaunchKernelGGL(set_params_kernel, dim3(1), dim3(256), 0, st, dst + off, c, k);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_set_floats(float *dst, const float *src, int n, hipStream_t st) {
+  for (int off = 0; off < n; off += 512) {
+    FloatChunk c;
+    const int k = (n - off < 512) ? n - off : 512;
+    for (int i = 0; i < k; ++i) c.f[i] = src[off + i];
+    hipLaunchKernelGGL(set_floats_kernel, dim3(1), dim3(256), 0, st, dst + off, c, k);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace dg

@@ -1,0 +1,169 @@
+/*
+ * dg.h -- C ABI of libdg, the block-canvas denoising step on gfx950 (MI355X).
+ *
+ * The method is the one summarised on the hyper.ai page for the
+ * DiffusionGemma Technical Report ("TR summary" below), section Method:
+ *   - forward path: per coordinate kappa_t delta(x_t, x_0) + (1 - kappa_t)/V,
+ *     kappa_0 = 1 to kappa_1 = 0, smooth and decreasing (forward path eq.);
+ *   - decoder: L_t = Decoder(x_t, z_t, H), bidirectional attention inside the
+ *     canvas plus cross-attention to the KV cache H (decoder eq. and the
+ *     three-stage generation pipeline);
+ *   - iteration: p0 = Softmax(L_t / tau_t), z = FFW(p0 E),
+ *     x_{t-dt} ~ Step(x_t, p0) (three-line update);
+ *   - tau_t anneals linearly from 0.8 to 0.4 (sampler paragraph).
+ * Readings where the pages stop short: Step is the Euler step of the
+ * uniform-path CTMC, (1 - lambda) delta(y, x_t) + lambda p0(y) with
+ * lambda = clamp(dt (-dkappa/dt) / (1 - kappa_t), 0, 1); FFW is the identity;
+ * the decoder is one residual attention block (h0 = E[x] + z; q,k,v = h0 W^T;
+ * one joint unmasked softmax over [prefix ; canvas] keys, scale 1/sqrt(hd),
+ * query head h reads kv head h / (Hq/Hkv); h1 = h0 + o Wo^T) with the LM head
+ * tied to E; tau_t = 0.4 + 0.4 t.
+ *
+ * Random numbers: Philox4x32-10 (Salmon et al., SC'11), key = (lo32(seed),
+ * hi32(seed)), counter (c0, c1, c2, stream):
+ *   Gumbel noise   (v >> 2, i, b, 0), word v & 3;      G = -log(-log U)
+ *   Step Bernoulli (0, i, b, 1), word 0;              resample iff U < lambda_b
+ *   corruption     (i >> 1, 0, b, 2), words 2(i&1) (keep iff U < kappa_b)
+ *                  and 2(i&1)+1 (token floor(w V / 2^32))
+ * with U(w) = (2 (w >> 9) + 1) 2^-24, i the canvas position, b the canvas.
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never frees them. Arrays documented as "host" are read on the host
+ *     before the call returns.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream). Nothing synchronises the device.
+ *   - Every argument is checked on the host before any launch; on error
+ *     nothing is launched or written and dg_last_error() holds a message
+ *     (thread-local). No C++ exception crosses this boundary.
+ *   - A dg_model is not thread-safe: calls on one model must be ordered on
+ *     one stream or otherwise serialised by the caller.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARG = 1, /* null pointer, out-of-range value, aliasing   */
+  DG_ERR_UNSUPPORTED = 2, /* valid shape the kernels do not implement     */
+  DG_ERR_HIP = 3,         /* a HIP runtime call or a kernel launch failed */
+  DG_ERR_OOM = 4          /* device or pinned-host allocation failed      */
+} dg_status;
+
+enum { DG_DTYPE_F32 = 0, DG_DTYPE_BF16 = 1 };
+enum { DG_SCHEDULE_LINEAR = 0, /* kappa = 1 - t            */
+       DG_SCHEDULE_COSINE = 1  /* kappa = cos^2(pi t / 2)  */ };
+
+/* Shapes of one model instance.
+ *   B canvases of C tokens, prompt prefix of P tokens per canvas, width d,
+ *   n_q_heads query heads and n_kv_heads KV heads of head_dim each
+ *   (n_q_heads % n_kv_heads == 0), vocabulary V.
+ *   dtype: DG_DTYPE_F32 or DG_DTYPE_BF16 -- the storage type of weights, KV
+ *   cache, activations and z ("act" below); accumulation is always fp32.
+ *   Limits: all sizes >= 1; B*C*max(d, V) < 2^31 for the per-row tensors;
+ *   bf16 kernels need d % 32 == 0, head_dim % 16 == 0, head_dim <= 256,
+ *   (n_q_heads * head_dim) % 32 == 0 and V % 32 == 0 (DG_ERR_UNSUPPORTED
+ *   otherwise). The fp32 kernels take any size within the first limits. */
+typedef struct dg_config {
+  int32_t B, C, P, d, n_q_heads, n_kv_heads, head_dim, V;
+  int32_t dtype;
+  int32_t schedule;
+} dg_config;
+
+/* Weights, device pointers in act dtype, row-major, caller-owned and
+ * read-only for the model's lifetime:
+ *   E  [V, d]            token embedding, also the tied LM head
+ *   Wq [Hq*hd, d]        q = h0 Wq^T    (output-feature major)
+ *   Wk [Hkv*hd, d], Wv [Hkv*hd, d]
+ *   Wo [d, Hq*hd]        h1 = h0 + o Wo^T */
+typedef struct dg_weights {
+  const void *E, *Wq, *Wk, *Wv, *Wo;
+} dg_weights;
+
+/* Optional intermediate outputs of one step (all device pointers, each may be
+ * NULL). Rows r = b*C + i.
+ *   h0 [B,C,d] act; q [B,C,Hq,hd] act; k, v [B,Hkv,C,hd] act;
+ *   o [B,C,Hq,hd] act (attention output); h1 [B,C,d] act;
+ *   lse [B,C] f32 = logsumexp_v(s_v) of the scaled logits s = (h1 E^T)/tau_b;
+ *   p0 [B,C,V] f32 = exp(s - lse) (extra passes; for checking only);
+ *   best [B,C] int32 = Gumbel argmax for rows that resampled, -1 for kept rows. */
+typedef struct dg_taps {
+  void *h0, *q, *k, *v, *o, *h1;
+  float *lse, *p0;
+  int32_t *best;
+} dg_taps;
+
+typedef struct dg_model dg_model;
+
+/* Create a model over caller-owned weights. Allocates the library's own
+ * device workspace (activations, split partials, generation buffers) and a
+ * small pinned host ring for per-call step parameters. Selects the current
+ * HIP device at the time of the call; later calls must run with that device
+ * current. *out is set only on DG_OK. */
+dg_status dg_create(const dg_config *cfg, const dg_weights *w, dg_model **out);
+
+/* Frees the workspace; waits for the device to finish work already queued
+ * on the model's buffers. NULL is accepted. */
+dg_status dg_destroy(dg_model *m);
+
+/* Bytes of device workspace dg_create would allocate for cfg. */
+dg_status dg_workspace_bytes(const dg_config *cfg, size_t *bytes);
+
+/* Forward corruption x_t ~ kappa delta(., x0) + (1 - kappa)/V per token
+ * (TR summary, Method, forward path eq.).
+ *   x0 [B,C] int32 in [0, V); kappa host [B], each in [0, 1];
+ *   xt_out [B,C] int32, must not overlap x0. */
+dg_status dg_corrupt(dg_model *m, const int32_t *x0, const float *kappa, uint64_t seed,
+                     int32_t *xt_out, void *stream);
+
+/* The same corruption without a model, for any batch shape:
+ *   x0 [B,C] int32, kappa_dev DEVICE [B] f32 in [0,1] (not checked on the
+ *   host), xt_out [B,C] int32 (may equal x0: the kernel reads each token
+ *   before writing it). */
+dg_status dg_corrupt_batch(const int32_t *x0, const float *kappa_dev, int32_t B, int32_t C,
+                           int32_t V, uint64_t seed, int32_t *xt_out, void *stream);
+
+/* One denoising step for every canvas (TR summary, Method, decoder eq. and
+ * three-line update):
+ *   x_t [B,C] int32 in [0,V); z_t [B,C,d] act; K_pre, V_pre [B,Hkv,P,hd] act
+ *   (the prompt KV cache H); t host [B], each in (0, 1]; dt in (0, 1];
+ *   seed = the Philox key of this step.
+ *   Outputs: x_out [B,C] int32 (the Step draw), z_out [B,C,d] act
+ *   (z = p0 E), optional lse_out [B,C] f32, optional p0_out [B,C,V] f32.
+ *   x_out / z_out must not overlap x_t / z_t. The C x V logits are never
+ *   written unless p0_out is given. */
+dg_status dg_denoise_step(dg_model *m, const int32_t *x_t, const void *z_t, const void *K_pre,
+                          const void *V_pre, const float *t, float dt, uint64_t seed,
+                          int32_t *x_out, void *z_out, float *lse_out, float *p0_out,
+                          void *stream);
+
+/* dg_denoise_step with every intermediate exposed through `taps` (may be NULL). */
+dg_status dg_denoise_step_taps(dg_model *m, const int32_t *x_t, const void *z_t,
+                               const void *K_pre, const void *V_pre, const float *t, float dt,
+                               uint64_t seed, int32_t *x_out, void *z_out, const dg_taps *taps,
+                               void *stream);
+
+/* Generate B canvases from noise (TR summary, Method, three-line update
+ * iterated from t = 1; Experiments: about 12 and at most 48 steps).
+ *   x_init = corruption of any canvas at kappa = 0 with `seed` (uniform),
+ *   z = 0; for k = 0..steps-1: t_k = (float)(1 - k/steps), dt = (float)(1/steps),
+ *   step seed = seed + k (mod 2^64). steps in [1, 4096].
+ *   x_out [B,C] int32 final canvas; z_out [B,C,d] act final z (may be NULL). */
+dg_status dg_generate_canvas(dg_model *m, const void *K_pre, const void *V_pre, int32_t steps,
+                             uint64_t seed, int32_t *x_out, void *z_out, void *stream);
+
+const char *dg_status_string(dg_status s);
+/* Message of the last failed call on this thread ("" if none). */
+const char *dg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

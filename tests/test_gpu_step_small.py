@@ -1,0 +1,86 @@
+"""GPU parity of one denoising step at sizes the oracle finishes in seconds,
+stage by stage through the taps (fp32 and bf16 kernels, several tiles and
+ragged tails in rows, keys and heads)."""
+import numpy as np
+import pytest
+
+from oracle import denoise_step
+from tests.dg_harness import (LSE_RTOL, P0_ATOL, RTOL_BF16, RTOL_F32, GpuModel, assert_close,
+                              to_dev, token_gate)
+from workloads import get_config, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    # fp32 workload exactly as configured (C=16, P=8, d=32, MHA 2x16, V=64)
+    "c1": dict(base="c1"),
+    # bf16, ragged rows (C=40 vs 32-row LM-head blocks), ragged keys (P+C=140)
+    "bf16-hd64": dict(base="c2", B=2, C=40, P=100, d=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                      V=4096),
+    "bf16-hd128": dict(base="c2", B=1, C=72, P=130, d=512, n_q_heads=4, n_kv_heads=2,
+                       head_dim=128, V=2048),
+    # head_dim 176 and d = 2816 (the large-vocabulary model's widths), few rows
+    "bf16-hd176": dict(base="c4", B=1, C=24, P=40, d=2816, n_q_heads=16, n_kv_heads=8,
+                       head_dim=176, V=1024),
+    "bf16-linear-b3": dict(base="c5", B=3, C=33, P=64, d=1024, n_q_heads=8, n_kv_heads=4,
+                           head_dim=128, V=1024),
+}
+
+
+def _cfg(name):
+    spec = dict(SMALL[name])
+    base = spec.pop("base")
+    return get_config(base, **spec)
+
+
+def _run(cfg, t, dt, seed, p0=True):
+    import torch
+    inp = make_inputs(cfg)
+    m = GpuModel(cfg, inp)
+    x = torch.from_numpy(inp["x"]).cuda()
+    dev = {n: to_dev(inp, n, cfg) for n in ["z", "K_pre", "V_pre"]}
+    print(f"[gpu] step {cfg.name} B={cfg.B} C={cfg.C} P={cfg.P} d={cfg.d} V={cfg.V} seed={seed}", flush=True)
+    g = m.step(x, dev["z"], dev["K_pre"], dev["V_pre"], t, dt, seed, p0=p0)
+    m.close()
+    w = {k: inp[k] for k in ["E", "Wq", "Wk", "Wv", "Wo"]}
+    o = denoise_step(cfg, w, inp["x"], inp["z"], inp["K_pre"], inp["V_pre"], t, float(dt), seed,
+                     want_p0=p0)
+    return g, o, inp
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("tval", [1.0, 0.5, 1.0 / 12])
+def test_step_matches_oracle(name, tval):
+    cfg = _cfg(name)
+    dt = np.float32(1.0 / cfg.steps)
+    t = np.full(cfg.B, tval, np.float32)
+    if cfg.per_canvas_t:
+        t = make_inputs(cfg, ["t"])["t"]
+    g, o, _ = _run(cfg, t, dt, seed=11)
+    rt = RTOL_F32 if cfg.dtype == "f32" else RTOL_BF16
+    for name_ in ["h0", "q", "k", "v", "o", "h1"]:
+        assert_close(name_, g[name_], o[name_], rt)
+    assert_close("z", g["z_out"], o["z_out"], rt)
+    assert_close("lse", g["lse"].ravel(), o["lse"], RTOL_F32 if cfg.dtype == "f32" else LSE_RTOL)
+    p0g = g["p0"].reshape(o["p0"].shape)
+    assert np.abs(p0g - o["p0"]).max() <= P0_ATOL
+    assert np.abs(p0g - o["p0"]).max() / o["p0"].max() <= (1e-4 if cfg.dtype == "f32" else 2e-2)
+    # the Bernoulli decisions are exact; the draw of resampled rows is gated
+    assert np.array_equal(g["best"] >= 0, o["resample"])
+    token_gate(g["x_out"], o)
+
+
+def test_taps_do_not_change_results():
+    import torch
+    cfg = _cfg("bf16-hd64")
+    inp = make_inputs(cfg)
+    m = GpuModel(cfg, inp)
+    x = torch.from_numpy(inp["x"]).cuda()
+    dev = {n: to_dev(inp, n, cfg) for n in ["z", "K_pre", "V_pre"]}
+    t = np.full(cfg.B, 0.3, np.float32)
+    a = m.step(x, dev["z"], dev["K_pre"], dev["V_pre"], t, 1 / 12, 5, taps=True, p0=True)
+    b = m.step(x, dev["z"], dev["K_pre"], dev["V_pre"], t, 1 / 12, 5, taps=False)
+    c = m.step(x, dev["z"], dev["K_pre"], dev["V_pre"], t, 1 / 12, 5, taps=False)
+    m.close()
+    assert np.array_equal(a["x_out"], b["x_out"]) and np.array_equal(b["x_out"], c["x_out"])
+    assert np.array_equal(a["z_out"], b["z_out"]) and np.array_equal(b["z_out"], c["z_out"])
