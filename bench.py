@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Throughput of the block-canvas denoising step on one MI355X.
+
+A step is one dg_denoise_step call: schedule constants, embedding +
+self-conditioning, q/k/v projection, prefix + canvas attention, output
+projection, fused LM head with online softmax, z and Gumbel draw, split merge
+and Step select, for every canvas of the batch. Inputs are seeded synthetic
+tensors already resident in HBM; t cycles through the 12-step cosine grid,
+one Philox seed per step.
+
+Prints one JSON line. `roofline` reports the dominant kernel (the fused LM
+head) from HIP events recorded around its launches in the timed region;
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "canvas denoise steps/s & canvas tokens/s (C=256, 1 GPU); % MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+WORKLOADS = {
+    "c2": "standard canvas: B=1 C=256 P=512 d=2048 16q/8kv heads x 128 V=32768 bf16, cosine 12 steps",
+    "c3": "long prefix: B=1 C=256 P=32768 d=2048 16q/8kv heads x 128 V=32768 bf16, cosine 12 steps",
+    "c4": "large vocabulary: B=1 C=256 P=2048 d=2816 16q/8kv heads x 176 V=262144 bf16, cosine 12 steps",
+    "c5": "batched: B=32 C=256 P=4096 d=2048 16q/8kv heads x 128 V=131072 bf16, linear, per-canvas t",
+}
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "lmhead_counters.txt")
+LMHEAD_SRC = os.path.join(ROOT, "discrete_diffusion_decoding_dg_amd", "csrc", "k_lmhead.hip")
+
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(workload):
+    """HBM bytes per LM-head launch from committed rocprofv3 counters, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            lines = [l for l in f if l.strip() and not l.startswith("#")]
+        rec = json.loads(lines[-1]) if lines else {}
+        rec = rec.get(workload, rec if rec.get("workload") == workload else {})
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_source_sha") != _sha(LMHEAD_SRC):
+        return None
+    return (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"]) * 1024.0
+
+
+def cpu_baseline(cfg, inp, budget_s):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import denoise_step
+    w = {k: inp[k] for k in ["E", "Wq", "Wk", "Wv", "Wo"]}
+    t = np.full(cfg.B, 0.5, np.float32) if not cfg.per_canvas_t else inp["t"]
+    dt = float(np.float32(1.0 / cfg.steps))
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        denoise_step(cfg, w, inp["x"], inp["z"], inp["K_pre"], inp["V_pre"], t, dt, seed=runs)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    sps = runs / el
+    return {"value": sps, "unit": "denoise steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{runs} full oracle denoise step(s) of the same workload at t=0.5 "
+                      f"({el:.1f} s wall, float64 BLAS on {threads} threads)",
+            "canvas_tokens_per_s": sps * cfg.B * cfg.C}
+
+
+def corrupt_bandwidth(reps=20):
+    """dg_corrupt_batch over 2^28 tokens (1 GiB in, 1 GiB out), kappa = 0.5, V = 262144."""
+    import torch
+    import discrete_diffusion_decoding_dg_amd as dg
+    B, C, V = 1 << 20, 256, 262144
+    x0 = torch.randint(0, V, (B, C), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(x0)
+    kap = torch.full((B,), 0.5, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        dg.dg_corrupt_batch(x0, kap, B, C, V, 1, out)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for r in range(reps):
+        dg.dg_corrupt_batch(x0, kap, B, C, V, r, out)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    gbs = (8.0 * B * C) / (ms * 1e-3) / 1e9
+    del x0, out, kap
+    return {"tokens": B * C, "ms": ms, "GB_s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
+            "bytes_per_token": 8}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-corrupt", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the denoising step on exactly one GPU; this build has no "
+              "multi-GPU path (no sharding, no collectives). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import discrete_diffusion_decoding_dg_amd as dg
+    from workloads import get_config, make_inputs
+    from tests.dg_harness import config_args, to_dev
+
+    cfg = get_config(args.workload)
+    inp = make_inputs(cfg)
+    torch.cuda.set_device(0)
+    wdev = {n: to_dev(inp, n, cfg) for n in ["E", "Wq", "Wk", "Wv", "Wo"]}
+    model = dg.dg_create(config_args(cfg), wdev["E"], wdev["Wq"], wdev["Wk"], wdev["Wv"], wdev["Wo"])
+    Kp, Vp, z = (to_dev(inp, n, cfg) for n in ["K_pre", "V_pre", "z"])
+    x = torch.from_numpy(inp["x"]).cuda()
+    xs = [x, torch.empty_like(x)]
+    zs = [z, torch.empty_like(z)]
+    dt = float(np.float32(1.0 / cfg.steps))
+    grid = [np.float32(1.0 - k / cfg.steps) for k in range(cfg.steps)]
+
+    def tvec(k):
+        if cfg.per_canvas_t:
+            return inp["t"]
+        return np.full(cfg.B, grid[k % cfg.steps], np.float32)
+
+    def step(k):
+        a, b = k & 1, (k & 1) ^ 1
+        dg.dg_denoise_step(model, xs[a], zs[a], Kp, Vp, tvec(k), dt, 1000 + k, xs[b], zs[b])
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    dg.dg_profile_read(model)          # drop anything recorded so far
+    dg.dg_profile_enable(model, True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        step(args.warmup + k)
+    end.record()
+    torch.cuda.synchronize()
+    dg.dg_profile_enable(model, False)
+    prof = dg.dg_profile_read(model)
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    # generation of one canvas batch end to end (not part of the timed steps)
+    xo = torch.empty_like(x)
+    dg.dg_generate_canvas(model, Kp, Vp, cfg.steps, 7, xo, None)
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    dg.dg_generate_canvas(model, Kp, Vp, cfg.steps, 7, xo, None)
+    g1.record()
+    torch.cuda.synchronize()
+    gen_ms = g0.elapsed_time(g1)
+
+    fl = cfg.flops_per_step()
+    lm_ms, lm_n = prof["lmhead"]
+    lm_avg_ms = lm_ms / max(1, lm_n)
+    achieved = fl["lm"] / (lm_avg_ms * 1e-3) / 1e12
+    traffic = _traffic(args.workload)
+    kernels = {k: {"avg_ms": (v[0] / v[1]) if v[1] else None, "launches": v[1]}
+               for k, v in prof.items() if v[1]}
+    steps_per_s = 1000.0 / ms_per_step
+    result = {
+        "metric": METRIC,
+        "value": steps_per_s,
+        "unit": "denoise steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.workload], "B": cfg.B, "C": cfg.C, "P": cfg.P,
+                   "d": cfg.d, "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
+                   "head_dim": cfg.head_dim, "V": cfg.V, "schedule": cfg.schedule,
+                   "parallelism": "single GPU"},
+        "canvas_tokens_per_s": steps_per_s * cfg.B * cfg.C,
+        "step_tflops": fl["total"] / (ms_per_step * 1e-3) / 1e12,
+        "step_frac_mfma": fl["total"] / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "generate_canvas_ms": gen_ms,
+        "roofline": {"bound": "mfma", "kernel": "lmhead_kernel", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic, "avg_ms": lm_avg_ms,
+                     "algorithmic_flop_per_launch": fl["lm"]},
+        "kernels": kernels,
+    }
+    if not args.no_corrupt:
+        result["corrupt"] = corrupt_bandwidth()
+    model.close()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -32,9 +32,17 @@ class dg_taps(ctypes.Structure):
                 ("lse", ctypes.c_void_p), ("p0", ctypes.c_void_p), ("best", ctypes.c_void_p)]
 
 
+NUM_STAGES = 7
+STAGES = ["embed", "qkv", "attention", "oproj", "lmhead", "combine", "corrupt"]
+
+
+class dg_profile(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double * NUM_STAGES), ("count", ctypes.c_int64 * NUM_STAGES)]
+
+
 EXPORTS = ["dg_create", "dg_destroy", "dg_workspace_bytes", "dg_corrupt", "dg_corrupt_batch",
-           "dg_denoise_step", "dg_denoise_step_taps", "dg_generate_canvas", "dg_status_string",
-           "dg_last_error"]
+           "dg_denoise_step", "dg_denoise_step_taps", "dg_generate_canvas", "dg_profile_enable",
+           "dg_profile_read", "dg_status_string", "dg_last_error"]
 
 _lib = None
 
@@ -58,6 +66,8 @@ def load_library():
     lib.dg_denoise_step_taps.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(f32), f32, u64, vp, vp,
                                          ctypes.POINTER(dg_taps), vp]
     lib.dg_generate_canvas.argtypes = [vp, vp, vp, i32, u64, vp, vp, vp]
+    lib.dg_profile_enable.argtypes = [vp, ctypes.c_int]
+    lib.dg_profile_read.argtypes = [vp, ctypes.POINTER(dg_profile)]
     lib.dg_status_string.argtypes = [ctypes.c_int]
     lib.dg_status_string.restype = ctypes.c_char_p
     lib.dg_last_error.restype = ctypes.c_char_p
@@ -180,6 +190,17 @@ def dg_denoise_step_taps(model, x_t, z_t, K_pre, V_pre, t, dt, seed, x_out, z_ou
 def dg_generate_canvas(model, K_pre, V_pre, steps, seed, x_out, z_out=None, stream=None):
     _check(load_library().dg_generate_canvas(model.handle, _ptr(K_pre), _ptr(V_pre), int(steps),
                                              int(seed), _ptr(x_out), _ptr(z_out), _stream(stream)))
+
+
+def dg_profile_enable(model, on=True):
+    _check(load_library().dg_profile_enable(model.handle, 1 if on else 0))
+
+
+def dg_profile_read(model):
+    """Returns {stage: (total_ms, launches)} and clears the recorded events."""
+    p = dg_profile()
+    _check(load_library().dg_profile_read(model.handle, ctypes.byref(p)))
+    return {STAGES[i]: (p.ms[i], int(p.count[i])) for i in range(NUM_STAGES)}
 
 
 load_library()

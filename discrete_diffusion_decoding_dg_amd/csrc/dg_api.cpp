@@ -160,9 +160,34 @@ struct dg_model {
   float *kappa;
   int32_t *genx;
   char *genz;
+  // profiling: event pairs recorded around stage launches while enabled
+  bool prof_on = false;
+  struct Mark {
+    int stage;
+    hipEvent_t a, b;
+  };
+  std::vector<Mark> marks;
 };
 
 namespace {
+
+// Records an event pair around one stage when profiling is on.
+struct StageTimer {
+  dg_model *m;
+  int stage;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+  StageTimer(dg_model *m_, int stage_, hipStream_t st_) : m(m_), stage(stage_), st(st_) {
+    if (m->prof_on && hipEventCreate(&a) == hipSuccess && hipEventCreate(&b) == hipSuccess)
+      (void)hipEventRecord(a, st);
+  }
+  ~StageTimer() {
+    if (a && b) {
+      (void)hipEventRecord(b, st);
+      m->marks.push_back({stage, a, b});
+    }
+  }
+};
 
 dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void *Kp,
                    const void *Vp, const dg::StepParams *prm, uint64_t seed, int32_t *x_out,
@@ -176,46 +201,79 @@ dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void 
   void *o = taps && taps->o ? taps->o : m->o;
   void *h1 = taps && taps->h1 ? taps->h1 : m->h1;
   int32_t *best = taps ? taps->best : nullptr;
-  DG_HIP(dg::launch_embed(bf16, m->w.E, x_t, z_t, s.R(), s.d, s.V, h0, st), "embed launch");
+  {
+    StageTimer tm(m, 0, st);
+    DG_HIP(dg::launch_embed(bf16, m->w.E, x_t, z_t, s.R(), s.d, s.V, h0, st), "embed launch");
+  }
   if (bf16) {
     using u16 = uint16_t;
-    DG_HIP(dg::launch_qkv_bf16(static_cast<const u16 *>(h0), static_cast<const u16 *>(m->w.Wq),
+    {
+      StageTimer tm(m, 1, st);
+      DG_HIP(dg::launch_qkv_bf16(static_cast<const u16 *>(h0), static_cast<const u16 *>(m->w.Wq),
                                static_cast<const u16 *>(m->w.Wk), static_cast<const u16 *>(m->w.Wv),
                                s, static_cast<u16 *>(q), static_cast<u16 *>(k),
                                static_cast<u16 *>(v), st),
            "qkv launch");
-    DG_HIP(dg::launch_attention_bf16(static_cast<const u16 *>(q), static_cast<const u16 *>(k),
+    }
+    {
+      StageTimer tm(m, 2, st);
+      DG_HIP(dg::launch_attention_bf16(static_cast<const u16 *>(q), static_cast<const u16 *>(k),
                                      static_cast<const u16 *>(v), static_cast<const u16 *>(Kp),
                                      static_cast<const u16 *>(Vp), s, m->attn,
                                      static_cast<u16 *>(o), st),
            "attention launch");
-    DG_HIP(dg::launch_oproj_bf16(static_cast<const u16 *>(o), static_cast<const u16 *>(m->w.Wo),
+    }
+    {
+      StageTimer tm(m, 3, st);
+      DG_HIP(dg::launch_oproj_bf16(static_cast<const u16 *>(o), static_cast<const u16 *>(m->w.Wo),
                                  static_cast<const u16 *>(h0), s, static_cast<u16 *>(h1), st),
            "out-projection launch");
-    DG_HIP(dg::launch_lmhead_bf16(static_cast<const u16 *>(h1), static_cast<const u16 *>(m->w.E),
+    }
+    {
+      StageTimer tm(m, 4, st);
+      DG_HIP(dg::launch_lmhead_bf16(static_cast<const u16 *>(h1), static_cast<const u16 *>(m->w.E),
                                   x_t, prm, s, seed, m->lm, p0, st),
            "LM head launch");
-    DG_HIP(dg::launch_combine(true, m->lm, dg::lmhead_splits(s), x_t, prm, s, seed, x_out, z_out,
+    }
+    {
+      StageTimer tm(m, 5, st);
+      DG_HIP(dg::launch_combine(true, m->lm, dg::lmhead_splits(s), x_t, prm, s, seed, x_out, z_out,
                               lse, best, st),
            "combine launch");
+    }
   } else {
-    DG_HIP(dg::launch_qkv_f32(static_cast<const float *>(h0), static_cast<const float *>(m->w.Wq),
+    {
+      StageTimer tm(m, 1, st);
+      DG_HIP(dg::launch_qkv_f32(static_cast<const float *>(h0), static_cast<const float *>(m->w.Wq),
                               static_cast<const float *>(m->w.Wk),
                               static_cast<const float *>(m->w.Wv), s, static_cast<float *>(q),
                               static_cast<float *>(k), static_cast<float *>(v), st),
            "qkv launch");
-    DG_HIP(dg::launch_attention_f32(static_cast<const float *>(q), static_cast<const float *>(k),
+    }
+    {
+      StageTimer tm(m, 2, st);
+      DG_HIP(dg::launch_attention_f32(static_cast<const float *>(q), static_cast<const float *>(k),
                                     static_cast<const float *>(v), static_cast<const float *>(Kp),
                                     static_cast<const float *>(Vp), s, static_cast<float *>(o), st),
            "attention launch");
-    DG_HIP(dg::launch_oproj_f32(static_cast<const float *>(o), static_cast<const float *>(m->w.Wo),
+    }
+    {
+      StageTimer tm(m, 3, st);
+      DG_HIP(dg::launch_oproj_f32(static_cast<const float *>(o), static_cast<const float *>(m->w.Wo),
                                 static_cast<const float *>(h0), s, static_cast<float *>(h1), st),
            "out-projection launch");
-    DG_HIP(dg::launch_lmhead_f32(static_cast<const float *>(h1), static_cast<const float *>(m->w.E),
+    }
+    {
+      StageTimer tm(m, 4, st);
+      DG_HIP(dg::launch_lmhead_f32(static_cast<const float *>(h1), static_cast<const float *>(m->w.E),
                                  prm, s, seed, m->lm, p0, st),
            "LM head launch");
-    DG_HIP(dg::launch_combine(false, m->lm, 1, x_t, prm, s, seed, x_out, z_out, lse, best, st),
+    }
+    {
+      StageTimer tm(m, 5, st);
+      DG_HIP(dg::launch_combine(false, m->lm, 1, x_t, prm, s, seed, x_out, z_out, lse, best, st),
            "combine launch");
+    }
   }
   if (p0) {
     if (!lse) return fail(DG_ERR_INVALID_ARG, "internal: p0 requires lse");
@@ -313,10 +371,42 @@ dg_status dg_create(const dg_config *cfg, const dg_weights *w, dg_model **out) {
   return DG_OK;
 }
 
+dg_status dg_profile_enable(dg_model *m, int on) {
+  g_err.clear();
+  if (!m) return fail(DG_ERR_INVALID_ARG, "model is NULL");
+  m->prof_on = on != 0;
+  return DG_OK;
+}
+
+dg_status dg_profile_read(dg_model *m, dg_profile *out) {
+  g_err.clear();
+  if (!m || !out) return fail(DG_ERR_INVALID_ARG, "model or out is NULL");
+  std::memset(out, 0, sizeof(*out));
+  dg_status st = DG_OK;
+  for (auto &mk : m->marks) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(mk.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, mk.a, mk.b);
+    if (e != hipSuccess && st == DG_OK) st = hip_fail(e, "profile event");
+    if (mk.stage >= 0 && mk.stage < DG_NUM_STAGES) {
+      out->ms[mk.stage] += ms;
+      out->count[mk.stage] += 1;
+    }
+    (void)hipEventDestroy(mk.a);
+    (void)hipEventDestroy(mk.b);
+  }
+  m->marks.clear();
+  return st;
+}
+
 dg_status dg_destroy(dg_model *m) {
   g_err.clear();
   if (!m) return DG_OK;
   hipError_t e = hipDeviceSynchronize();
+  for (auto &mk : m->marks) {
+    (void)hipEventDestroy(mk.a);
+    (void)hipEventDestroy(mk.b);
+  }
   hipError_t f = hipFree(m->ws);
   delete m;
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
@@ -351,7 +441,10 @@ dg_status dg_corrupt(dg_model *m, const int32_t *x0, const float *kappa, uint64_
   if (overlap(x0, n, xt_out, n)) return fail(DG_ERR_INVALID_ARG, "xt_out overlaps x0");
   hipStream_t st = static_cast<hipStream_t>(stream);
   DG_HIP(dg::launch_set_floats(m->kappa, kappa, B, st), "kappa upload");
-  DG_HIP(dg::launch_corrupt(x0, m->kappa, B, C, m->s.V, seed, xt_out, st), "corrupt launch");
+  {
+    StageTimer tm(m, 6, st);
+    DG_HIP(dg::launch_corrupt(x0, m->kappa, B, C, m->s.V, seed, xt_out, st), "corrupt launch");
+  }
   return DG_OK;
 }
 

@@ -67,10 +67,11 @@ enum { DG_SCHEDULE_LINEAR = 0, /* kappa = 1 - t            */
  *   (n_q_heads % n_kv_heads == 0), vocabulary V.
  *   dtype: DG_DTYPE_F32 or DG_DTYPE_BF16 -- the storage type of weights, KV
  *   cache, activations and z ("act" below); accumulation is always fp32.
- *   Limits: all sizes >= 1; B*C*max(d, V) < 2^31 for the per-row tensors;
- *   bf16 kernels need d % 32 == 0, head_dim % 16 == 0, head_dim <= 256,
- *   (n_q_heads * head_dim) % 32 == 0 and V % 32 == 0 (DG_ERR_UNSUPPORTED
- *   otherwise). The fp32 kernels take any size within the first limits. */
+ *   Limits (DG_ERR_INVALID_ARG): B, C, d, heads, head_dim >= 1, P >= 0,
+ *   V >= 2, B*C*d and B*C*n_q_heads*head_dim < 2^31.
+ *   Kernel coverage (DG_ERR_UNSUPPORTED otherwise): bf16 needs head_dim in
+ *   {64, 128, 176}, d in {256, 512, 1024, 2048, 2816} and V % 16 == 0; fp32
+ *   needs d <= 4096 and P + C <= 16384. */
 typedef struct dg_config {
   int32_t B, C, P, d, n_q_heads, n_kv_heads, head_dim, V;
   int32_t dtype;
@@ -103,10 +104,11 @@ typedef struct dg_taps {
 typedef struct dg_model dg_model;
 
 /* Create a model over caller-owned weights. Allocates the library's own
- * device workspace (activations, split partials, generation buffers) and a
- * small pinned host ring for per-call step parameters. Selects the current
- * HIP device at the time of the call; later calls must run with that device
- * current. *out is set only on DG_OK. */
+ * device workspace (activations, split partials, per-step constants,
+ * generation buffers); per-call host arrays reach the device as kernel
+ * arguments, so no host memory outlives a call. Binds to the HIP device that
+ * is current at the time of the call; later calls must run with that device
+ * current. Weight pointers must be 16-byte aligned. *out is set only on DG_OK. */
 dg_status dg_create(const dg_config *cfg, const dg_weights *w, dg_model **out);
 
 /* Frees the workspace; waits for the device to finish work already queued
@@ -136,9 +138,10 @@ dg_status dg_corrupt_batch(const int32_t *x0, const float *kappa_dev, int32_t B,
  *   (the prompt KV cache H); t host [B], each in (0, 1]; dt in (0, 1];
  *   seed = the Philox key of this step.
  *   Outputs: x_out [B,C] int32 (the Step draw), z_out [B,C,d] act
- *   (z = p0 E), optional lse_out [B,C] f32, optional p0_out [B,C,V] f32.
- *   x_out / z_out must not overlap x_t / z_t. The C x V logits are never
- *   written unless p0_out is given. */
+ *   (z = p0 E), optional lse_out [B,C] f32, optional p0_out [B,C,V] f32
+ *   (p0_out requires lse_out). x_out / z_out must not overlap x_t / z_t;
+ *   bf16 tensors must be 16-byte aligned. The C x V logits are never written
+ *   unless p0_out is given. Tokens outside [0, V) embed as a zero row. */
 dg_status dg_denoise_step(dg_model *m, const int32_t *x_t, const void *z_t, const void *K_pre,
                           const void *V_pre, const float *t, float dt, uint64_t seed,
                           int32_t *x_out, void *z_out, float *lse_out, float *p0_out,
@@ -158,6 +161,21 @@ dg_status dg_denoise_step_taps(dg_model *m, const int32_t *x_t, const void *z_t,
  *   x_out [B,C] int32 final canvas; z_out [B,C,d] act final z (may be NULL). */
 dg_status dg_generate_canvas(dg_model *m, const void *K_pre, const void *V_pre, int32_t steps,
                              uint64_t seed, int32_t *x_out, void *z_out, void *stream);
+
+/* Per-stage GPU time of the calls made while profiling is on, measured with a
+ * HIP event pair recorded on the call's stream around each stage's launches.
+ * Stages: 0 embed, 1 q/k/v projection, 2 attention (+ split merge),
+ * 3 output projection, 4 LM head (logits, softmax statistics, z partials,
+ * Gumbel argmax), 5 split merge + Step select, 6 corruption.
+ * dg_profile_read waits for the recorded events, returns the summed
+ * milliseconds and the number of timed launches per stage, and clears them. */
+#define DG_NUM_STAGES 7
+typedef struct dg_profile {
+  double ms[DG_NUM_STAGES];
+  int64_t count[DG_NUM_STAGES];
+} dg_profile;
+dg_status dg_profile_enable(dg_model *m, int on);
+dg_status dg_profile_read(dg_model *m, dg_profile *out);
 
 const char *dg_status_string(dg_status s);
 /* Message of the last failed call on this thread ("" if none). */

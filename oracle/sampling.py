@@ -13,10 +13,12 @@ import numpy as np
 from .philox import philox4x32_10, uniform01
 
 
-def bernoulli_uniforms(seed, canvas_ids, C):
-    """u[b, i] in (0, 1), float32, for canvases `canvas_ids` and positions 0..C-1."""
+def bernoulli_uniforms(seed, canvas_ids, C, positions=None):
+    """u[b, i] in (0, 1), float32, for canvases `canvas_ids` and positions 0..C-1
+    (or the canvas positions listed in `positions`)."""
     b = np.asarray(canvas_ids, dtype=np.uint64)[:, None]
-    i = np.arange(C, dtype=np.uint64)[None, :]
+    pos = np.arange(C) if positions is None else np.asarray(positions)
+    i = pos.astype(np.uint64)[None, :]
     w0, _, _, _ = philox4x32_10(0, i, b, 1, seed)
     return uniform01(w0)
 
@@ -34,17 +36,20 @@ def gumbel_noise(seed, b, i, V):
     return (-e2).astype(np.float32)
 
 
-def step_select(x_t, s, lam, seed, canvas_ids):
+def step_select(x_t, s, lam, seed, canvas_ids, positions=None):
     """One Step draw for every row.
 
-    x_t [B, C] int, s [B*C, V] scaled logits (float64), lam [B] float32.
+    x_t [B, C] int, s [B*C, V] scaled logits (float64), lam [B] float32;
+    `positions` gives the canvas positions of the C columns when they are a
+    subset of a canvas (default 0..C-1).
     Returns x_out, the per-row resample mask, the Gumbel argmax (or -1) and,
     for resampled rows, the top-1 perturbed value and the gap to the top-2
     value (for near-tie accounting).
     """
     B, C = x_t.shape
     V = s.shape[1]
-    u = bernoulli_uniforms(seed, canvas_ids, C)                        # [B, C]
+    pos = np.arange(C) if positions is None else np.asarray(positions)
+    u = bernoulli_uniforms(seed, canvas_ids, C, pos)                   # [B, C]
     resample = u < np.asarray(lam, dtype=np.float32)[:, None]
     x_out = np.array(x_t, dtype=np.int64, copy=True)
     best = np.full((B, C), -1, dtype=np.int64)
@@ -53,7 +58,7 @@ def step_select(x_t, s, lam, seed, canvas_ids):
     rb, ri = np.nonzero(resample)
     if rb.size:
         cid = np.asarray(canvas_ids)[rb]
-        g = gumbel_noise(seed, cid, ri, V)
+        g = gumbel_noise(seed, cid, pos[ri], V)
         pert = s.reshape(B, C, V)[rb, ri].astype(np.float32) + g        # float32 add
         y = np.argmax(pert, axis=1)                                       # first max = lowest id
         best[rb, ri] = y

@@ -1,0 +1,67 @@
+"""GPU canvas generation: equals the step-by-step calls bit for bit, and the
+oracle's trajectory up to Gumbel near-ties."""
+import numpy as np
+import pytest
+
+from oracle import corrupt, denoise_step
+from tests.dg_harness import GpuModel, act_tensor, to_dev, token_gate
+from workloads import get_config, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "c1": dict(base="c1"),
+    "bf16-small": dict(base="c2", B=2, C=40, P=100, d=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                       V=512),
+}
+
+
+def _cfg(name):
+    spec = dict(CASES[name])
+    return get_config(spec.pop("base"), **spec)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_generate_matches_steps_and_oracle(name):
+    import torch
+    import discrete_diffusion_decoding_dg_amd as dg
+    cfg = _cfg(name)
+    inp = make_inputs(cfg)
+    m = GpuModel(cfg, inp)
+    Kp, Vp = to_dev(inp, "K_pre", cfg), to_dev(inp, "V_pre", cfg)
+    seed, steps = 31, cfg.steps
+    print(f"[gpu] generate {name} steps={steps}", flush=True)
+    x_gen = torch.empty((cfg.B, cfg.C), dtype=torch.int32, device="cuda")
+    z_gen = act_tensor((cfg.B, cfg.C, cfg.d), cfg)
+    dg.dg_generate_canvas(m.model, Kp, Vp, steps, seed, x_gen, z_gen)
+    # the same path, one library call per step
+    x = torch.zeros((cfg.B, cfg.C), dtype=torch.int32, device="cuda")
+    kap = torch.zeros((cfg.B,), dtype=torch.float32, device="cuda")
+    dg.dg_corrupt_batch(x, kap, cfg.B, cfg.C, cfg.V, seed, x)
+    z = act_tensor((cfg.B, cfg.C, cfg.d), cfg).zero_()
+    traj = [x.cpu().numpy()]
+    dt = float(np.float32(1.0 / steps))
+    for k in range(steps):
+        t = np.full(cfg.B, np.float32(1.0 - k / steps), np.float32)
+        xn, zn = torch.empty_like(x), torch.empty_like(z)
+        dg.dg_denoise_step(m.model, x, z, Kp, Vp, t, dt, seed + k, xn, zn)
+        x, z = xn, zn
+        traj.append(x.cpu().numpy())
+    torch.cuda.synchronize()
+    assert np.array_equal(x_gen.cpu().numpy(), traj[-1])
+    assert torch.equal(z_gen.view(torch.int16) if z_gen.dtype == torch.bfloat16 else z_gen,
+                       z.view(torch.int16) if z.dtype == torch.bfloat16 else z)
+    m.close()
+    # oracle: same start, then step by step from the GPU-independent oracle state
+    assert np.array_equal(traj[0], corrupt(np.zeros((cfg.B, cfg.C), np.int32),
+                                           np.zeros(cfg.B, np.float32), seed, cfg.V))
+    w = {k: inp[k] for k in ["E", "Wq", "Wk", "Wv", "Wo"]}
+    xo, zo = traj[0], np.zeros((cfg.B, cfg.C, cfg.d))
+    for k in range(steps):
+        t = np.full(cfg.B, np.float32(1.0 - k / steps), np.float32)
+        r = denoise_step(cfg, w, xo, zo, inp["K_pre"], inp["V_pre"], t, dt, seed + k)
+        if not np.array_equal(r["x_out"], traj[k + 1]):
+            # trajectories may part only at a Gumbel near-tie of the oracle
+            token_gate(traj[k + 1], r, name=f"step {k}")
+            return
+        xo, zo = r["x_out"], r["z_out"]

@@ -84,3 +84,17 @@ def test_corruption_identity_at_kappa_one_and_independence_of_seed():
     # canvas ids select counters: corrupting canvas 2 alone equals row 2 of the batch
     c = corrupt(x0[2:3], np.zeros(1, np.float32), 1, 64, canvas_ids=[2])
     assert np.array_equal(c[0], a[2])
+
+
+def test_step_on_a_subset_of_positions_matches_the_full_canvas():
+    rng = np.random.default_rng(12)
+    B, C, V = 2, 20, 32
+    x_t = rng.integers(0, V, (B, C)).astype(np.int32)
+    s = rng.standard_normal((B * C, V))
+    lam = np.array([0.6, 0.9], np.float32)
+    full = step_select(x_t, s, lam, seed=4, canvas_ids=[3, 5])
+    sel = np.array([1, 7, 19])
+    sub = step_select(x_t[:, sel], s.reshape(B, C, V)[:, sel].reshape(-1, V), lam, seed=4,
+                      canvas_ids=[3, 5], positions=sel)
+    assert np.array_equal(sub["x_out"], full["x_out"][:, sel])
+    assert np.array_equal(sub["u"], full["u"][:, sel])
