@@ -51,6 +51,12 @@ def load_library():
     global _lib
     if _lib is not None:
         return _lib
+    # One HIP runtime per process: torch bundles its own libamdhip64 (same
+    # SONAME as the system one). Importing torch first makes libdg bind to the
+    # runtime torch already loaded, so device pointers and stream handles
+    # coming from torch are valid in libdg. Loading libdg first would pull in
+    # the system runtime and torch would then load a second, separate one.
+    import torch  # noqa: F401
     path = library_path()
     if not os.path.exists(path):
         raise ImportError(f"libdg.so not found at {path}: build it with "

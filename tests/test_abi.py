@@ -100,3 +100,11 @@ def test_status_strings():
     assert dg.dg_status_string(0) == "DG_OK"
     assert dg.dg_status_string(2) == "DG_ERR_UNSUPPORTED"
     assert dg.dg_status_string(99) == "DG_ERR_UNKNOWN"
+
+
+def test_single_hip_runtime_in_process():
+    """libdg must resolve libamdhip64 to the copy torch loaded (one runtime)."""
+    _lib.load_library()
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(paths) == 1, paths
