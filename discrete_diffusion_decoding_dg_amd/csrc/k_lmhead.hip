@@ -271,17 +271,360 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Version for d = 8 * DW with DW <= 256 (32-row vocabulary tiles).
+//
+// Each of the 8 waves owns a DW-wide slice of d for both contractions. Its
+// slice of the 32 x d E tile lives in a private LDS region, chunk-major
+// (chunks of 32 columns, 32 rows x 64 B each, 16-byte pieces XOR-swizzled by
+// row), and is filled by direct global->LDS loads. Chunk c of the next tile
+// is requested as soon as the z contraction of this tile is done with it, so
+// the loads overlap the rest of the tile's work.
+//   S^T partial: A = E chunk (ds_read_b128), B = h1 slice in registers.
+//   Partials of the 8 slices meet in LDS; wave w reduces rows 4w..4w+3 (its
+//   rows for the whole kernel: their running max, sum and best draw stay in
+//   its registers) and writes P (bf16) and the rescale factor back in place,
+//   into the positions of its own partial slot that only it reads.
+//   z += P E: A = P (4 ds_read_b32 per 16 rows), B = E chunk read transposed
+//   with ds_read_b64_tr_b16 (lane (q, n) gets 4 consecutive vocab rows of
+//   column n), v_mfma_f32_16x16x32_bf16 with K = 32 vocabulary rows.
+namespace v2 {
+
+constexpr int NW = 8, MT = 32, VT = 32;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their
+// maxima). The builtin is visible to the compiler's own wait insertion.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");   // no memory access moves across the wait
+}
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
+// physical 16-byte piece of logical piece q in row r of a chunk
+__device__ __forceinline__ int swz(int r, int q) { return q ^ ((r >> 2) & 3); }
+
+// Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at
+// lds + 16 i (lds must be wave-uniform). Issued through inline asm so that
+// the compiler does not add conservative waits before unrelated LDS reads;
+// every read of DMA'd data is preceded by an explicit vmcnt wait instead.
+// The instruction has no register result: its address registers are read at
+// issue.
+// `base` is wave-uniform (scalar registers), `voff` the lane's byte offset.
+__device__ __forceinline__ void lds_dma16(const void *base, uint32_t voff, uint16_t *lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint16_t *)lds)));
+  // readfirstlane returns a signed int: go through uint32_t so that the low
+  // half is zero-extended (a sign-extended low half would corrupt the upper
+  // address bits whenever bit 31 is set)
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+  const uint64_t sb = (static_cast<uint64_t>(hi) << 32) | lo;
+  uint32_t saved;
+  // M0 is reserved by the compiler: keep its value across the block
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(voff), "s"(sb)
+      : "memory");
+}
+
+template <int DW>
+__global__ void __launch_bounds__(512) lmhead_v2_kernel(LmArgs a, int rblocks) {
+  constexpr int NKS = DW / 32;           // 32-column chunks per slice
+  constexpr int NB = DW / 16;            // 16-column z blocks per slice
+  constexpr int CHUNK = 32 * 32;         // elements per chunk
+  __shared__ __attribute__((aligned(16))) uint16_t Es[NW * NKS * CHUNK];
+  __shared__ __attribute__((aligned(16))) f32x4 red[NW][2][2][64];   // [wave][vb][rb][lane]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // XCD-aware order: consecutive blocks land on different XCDs, so regroup
+  // them to give each XCD a contiguous run of (split, row block) pairs: the
+  // row blocks that share a vocabulary range then share that XCD's L2.
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int split = bid / rblocks;
+  const int row0 = (bid - split * rblocks) * MT;
+  const int dcol0 = wave * DW;
+  uint16_t *es = Es + wave * NKS * CHUNK;
+  auto chunk = [&](int c) -> uint16_t * { return es + c * CHUNK; };
+
+  const int total_tiles = a.V / VT;
+  const int t_begin = split * a.tiles_per_split;
+  int t_end = t_begin + a.tiles_per_split;
+  if (t_end > total_tiles) t_end = total_tiles;
+
+  // DMA of chunk c of tile `tile` into this wave's slice: 2 x 64 lanes x 16 B.
+  // Lane i fills LDS piece i of the half: row 16 h + i / 4, physical piece
+  // i % 4, which holds the row's logical piece swz(row, i % 4); the swizzle
+  // depends only on row / 4 mod 4 = (i / 16) mod 4, the same for both halves.
+  const uint32_t dma_off = static_cast<uint32_t>(
+      ((lane >> 2) * a.d + ((lane & 3) ^ ((lane >> 4) & 3)) * 8) * 2);
+  auto dma_chunk = [&](int tile, int c) {
+    const uint16_t *tb = a.E + static_cast<int64_t>(tile * VT) * a.d + dcol0 + c * 32;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) lds_dma16(tb + static_cast<int64_t>(16 * h) * a.d, dma_off, chunk(c) + h * 16 * 32);
+  };
+  if (t_begin < t_end)
+#pragma unroll
+    for (int c = 0; c < NKS; ++c) dma_chunk(t_begin, c);
+
+  // h1 slice as the B operand of S^T: lane holds canvas row 16 rb + (lane & 15),
+  // columns dcol0 + 32 c + 8 (lane >> 4) + [0, 8)
+  bf16x8 hreg[2][NKS];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = row0 + rb * 16 + (lane & 15);
+    const uint16_t *hrow = a.h1 + static_cast<int64_t>(r) * a.d + dcol0 + (lane >> 4) * 8;
+#pragma unroll
+    for (int c = 0; c < NKS; ++c)
+      hreg[rb][c] = (r < a.R) ? *reinterpret_cast<const bf16x8 *>(hrow + c * 32) : bf16x8{};
+  }
+
+  // the rows this wave reduces: M = 4 wave + (lane >> 4); lane pair index j2
+  const int erow = 4 * wave + (lane >> 4);
+  const int j2 = lane & 15;                  // vocab 2 j2, 2 j2 + 1 of the tile
+  const int grow = row0 + erow;
+  const bool rvalid = grow < a.R;
+  const int gb = rvalid ? grow / a.C : 0;
+  const int gi = rvalid ? grow - gb * a.C : 0;
+  const float inv_tau = rvalid ? a.prm[gb].inv_tau : 0.f;
+  bool resample = false;
+  if (rvalid) {
+    const u32x4 w = philox4x32_10(0u, static_cast<uint32_t>(gi), static_cast<uint32_t>(gb),
+                                  kStreamBernoulli, a.k0, a.k1);
+    resample = u01(w.x) < a.prm[gb].lam;
+  }
+  float m_ref = -INFINITY, l_run = 0.f, best_v = -INFINITY;
+  int best_i = -1;
+  // where this lane's pair sits in a partial slot
+  const int e_vb = j2 >> 3;
+  const int e_rb = erow >> 4;
+  const int e_lc = ((j2 & 7) >> 1) * 16 + (erow & 15);
+  const int e_el = 2 * (j2 & 1);
+
+  f32x4 zacc[2][NB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) zacc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // everything issued so far (the first tile's chunks, h1, step constants)
+  // has landed: the loop below tracks only its own chunk loads
+  wait_vmcnt<0>();
+
+  for (int tile = t_begin; tile < t_end; ++tile) {
+    const int v0 = tile * VT;
+    const bool more = tile + 1 < t_end;
+    if (a.p0) wait_vmcnt<0>();   // checking mode: p0 stores share the counter
+    // ---- S^T partial over this wave's slice
+    f32x4 sacc[2][2];
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) sacc[vb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NKS; ++c) {
+      wait_vmcnt_le(2 * (NKS - 1 - c));
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb) {
+        const int r = vb * 16 + (lane & 15);
+        const bf16x8 ef = *reinterpret_cast<const bf16x8 *>(chunk(c) + r * 32 + swz(r, lane >> 4) * 8);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          sacc[vb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ef, hreg[rb][c], sacc[vb][rb], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) red[wave][vb][rb][lane] = sacc[vb][rb];
+    __syncthreads();
+
+    // ---- epilogue for rows 4 wave .. 4 wave + 3
+    {
+      float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float2 pr = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(&red[w][e_vb][e_rb][e_lc]) + e_el);
+        acc0 += pr.x;
+        acc1 += pr.y;
+      }
+      const int v = v0 + 2 * j2;
+      const float s0 = acc0 * inv_tau, s1 = acc1 * inv_tau;
+      if (a.p0 && rvalid) {
+        float *prow = a.p0 + static_cast<int64_t>(grow) * a.V + v;
+        prow[0] = s0;
+        prow[1] = s1;
+      }
+      float bv = -INFINITY;
+      int bi = -1;
+      if (resample) {
+        const u32x4 w = philox4x32_10(static_cast<uint32_t>(v >> 2), static_cast<uint32_t>(gi),
+                                      static_cast<uint32_t>(gb), kStreamGumbel, a.k0, a.k1);
+        const uint32_t w0 = (v & 2) ? w.z : w.x, w1 = (v & 2) ? w.w : w.y;
+        const float p0v = s0 + gumbel(w0), p1v = s1 + gumbel(w1);
+        bv = p0v;
+        bi = v;
+        if (p1v > bv) { bv = p1v; bi = v + 1; }
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (ov > bv || (ov == bv && oi >= 0 && (bi < 0 || oi < bi))) { bv = ov; bi = oi; }
+      }
+      if (bi >= 0 && bv > best_v) { best_v = bv; best_i = bi; }
+      const float t0 = s0 * kLog2e, t1 = s1 * kLog2e;
+      float tmax = fmaxf(t0, t1);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 64));
+      float sc = 1.f;
+      if (tmax > m_ref + kRescaleSlack) {
+        sc = exp2f(m_ref - tmax);   // 0 on the first tile
+        m_ref = tmax;
+      }
+      const float p0f = exp2f(t0 - m_ref), p1f = exp2f(t1 - m_ref);
+      float ps = p0f + p1f;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) ps += __shfl_xor(ps, o, 64);
+      l_run = l_run * sc + ps;
+      float *slot = reinterpret_cast<float *>(&red[wave][e_vb][e_rb][e_lc]);
+      slot[e_el] = __uint_as_float(pack_bf16x2(p0f, p1f));
+      if (j2 == 0) slot[1] = sc;
+    }
+    __syncthreads();
+
+    // ---- z += P E over this wave's slice
+    bf16x8 pa[2];
+    float scl[2][4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int m = rb * 16 + (lane & 15);
+      const int q = lane >> 4;
+      const float *s0p = reinterpret_cast<const float *>(&red[m >> 2][0][rb][q * 16 + (lane & 15)]);
+      const float *s1p = reinterpret_cast<const float *>(&red[m >> 2][1][rb][q * 16 + (lane & 15)]);
+      const uint32_t w4[4] = {__float_as_uint(s0p[0]), __float_as_uint(s0p[2]),
+                              __float_as_uint(s1p[0]), __float_as_uint(s1p[2])};
+      pa[rb] = *reinterpret_cast<const bf16x8 *>(w4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int mr = rb * 16 + q * 4 + i;
+        scl[rb][i] = reinterpret_cast<const float *>(&red[mr >> 2][0][rb][mr & 15])[1];
+      }
+    }
+    __syncthreads();   // every wave holds its P and factors: the slots may be reused
+    bool rescale = false;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rescale |= scl[rb][i] != 1.f;
+    if (__builtin_amdgcn_ballot_w64(rescale)) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) zacc[rb][nb][i] *= scl[rb][i];
+    }
+    // transposed read addresses: source lane supplies row 4 (lane>>4) + ((lane&15)>>2)
+    // (+16 for the second read), columns 16 (nb&1) + 4 (lane&3) of chunk nb>>1
+    const int tr_row = 4 * (lane >> 4) + ((lane & 15) >> 2);
+    const int tr_col = 4 * (lane & 3);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int c = nb >> 1;
+      const int col = 16 * (nb & 1) + tr_col;             // element column within the chunk
+      s16x4 lo, hi;
+      {
+        const int r = tr_row;
+        const uint16_t *p = chunk(c) + r * 32 + swz(r, col >> 3) * 8 + (col & 7);
+        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p);
+      }
+      {
+        const int r = tr_row + 16;
+        const uint16_t *p = chunk(c) + r * 32 + swz(r, col >> 3) * 8 + (col & 7);
+        hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p);
+      }
+      bf16x8 eb;
+      {
+        const s16x4 ls = lo, hs = hi;
+        const uint16_t w8[8] = {(uint16_t)ls[0], (uint16_t)ls[1], (uint16_t)ls[2], (uint16_t)ls[3],
+                                (uint16_t)hs[0], (uint16_t)hs[1], (uint16_t)hs[2], (uint16_t)hs[3]};
+        eb = *reinterpret_cast<const bf16x8 *>(w8);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        zacc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[rb], eb, zacc[rb][nb], 0, 0, 0);
+      if ((nb & 1) && more) dma_chunk(tile + 1, c);
+    }
+  }
+
+  // ---- write the split partials
+  if (rvalid && j2 == 0) {
+    RowPartial p;
+    p.m = m_ref;
+    p.l = l_run;
+    p.best = best_v;
+    p.arg = best_i;
+    a.part[static_cast<int64_t>(split) * a.R + grow] = p;
+  }
+  float *zs = a.zpart + static_cast<int64_t>(split) * a.R * a.d;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = row0 + rb * 16 + (lane >> 4) * 4 + i;
+      if (r >= a.R) continue;
+      float *zr = zs + static_cast<int64_t>(r) * a.d + dcol0 + (lane & 15);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) zr[nb * 16] = zacc[rb][nb][i];
+    }
+}
+
+}  // namespace v2
+
 struct Plan {
   int MT, DW, splits, tps;
+  bool v2;
 };
 
 bool plan(const Shape &s, Plan &p) {
   if (s.V % VT != 0 || s.d % (NW * 32) != 0) return false;
   p.DW = s.d / NW;
   if (p.DW != 32 && p.DW != 64 && p.DW != 128 && p.DW != 256 && p.DW != 352) return false;
-  p.MT = (p.DW <= 256) ? 32 : 16;
+  p.v2 = p.DW <= 256 && s.V % v2::VT == 0;
+  p.MT = p.v2 ? v2::MT : ((p.DW <= 256) ? 32 : 16);
+  const int vt = p.v2 ? v2::VT : VT;
   const int rblocks = (s.R() + p.MT - 1) / p.MT;
-  const int tiles = s.V / VT;
+  const int tiles = s.V / vt;
   int want = (256 + rblocks - 1) / rblocks;
   if (want < 1) want = 1;
   if (want > 64) want = 64;          // the combine kernel merges at most 64 splits
@@ -324,7 +667,19 @@ hipError_t launch_lmhead_bf16(const uint16_t *h1, const uint16_t *E, const int32
   a.part = static_cast<RowPartial *>(work);
   a.zpart = reinterpret_cast<float *>(static_cast<char *>(work) +
                                       static_cast<size_t>(p.splits) * s.R() * sizeof(RowPartial));
-  dim3 grid((s.R() + p.MT - 1) / p.MT, p.splits);
+  const int rblocks = (s.R() + p.MT - 1) / p.MT;
+  if (p.v2) {
+    const dim3 grid(rblocks * p.splits);
+    switch (p.DW) {
+      case 32: hipLaunchKernelGGL(v2::lmhead_v2_kernel<32>, grid, dim3(512), 0, st, a, rblocks); break;
+      case 64: hipLaunchKernelGGL(v2::lmhead_v2_kernel<64>, grid, dim3(512), 0, st, a, rblocks); break;
+      case 128: hipLaunchKernelGGL(v2::lmhead_v2_kernel<128>, grid, dim3(512), 0, st, a, rblocks); break;
+      case 256: hipLaunchKernelGGL(v2::lmhead_v2_kernel<256>, grid, dim3(512), 0, st, a, rblocks); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  dim3 grid(rblocks, p.splits);
 #define DG_LM(MT_, DW_)                                                                  \
   if (p.MT == MT_ && p.DW == DW_) {                                                      \
     hipLaunchKernelGGL((lmhead_kernel<MT_, DW_>), grid, dim3(512), 0, st, a);            \
