@@ -322,8 +322,19 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
   }
 }
 
-// physical 16-byte piece of logical piece q in row r of a chunk
-__device__ __forceinline__ int swz(int r, int q) { return q ^ ((r >> 2) & 3); }
+// Physical 16-byte piece of logical piece q in row r of a chunk (64-byte
+// rows). The XOR pattern keeps the three access patterns free of LDS bank
+// conflicts for both 32 and 64 banks of 4 bytes: DMA writes (contiguous),
+// 16-byte operand reads of 16 rows, and transposed 8-byte reads of 4 rows.
+__device__ __forceinline__ int swz(int r, int q) {
+  return q ^ (((r >> 2) & 1) | ((((r >> 1) ^ (r >> 2) ^ (r >> 3)) & 1) << 1));
+}
+// Position of the 16-byte vocabulary group g (4 fp32) in row r of a 32 x 32
+// fp32 tile of the reduction buffer: conflict-free partial writes (16-byte,
+// 16 rows x 4 groups) and epilogue reads (8-byte, 4 rows x 32 values).
+__device__ __forceinline__ int rswz(int r, int g) {
+  return g ^ (((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r ^ (r >> 3)) & 1) << 2));
+}
 
 // Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at
 // lds + 16 i (lds must be wave-uniform). Issued through inline asm so that
@@ -361,7 +372,7 @@ __global__ void __launch_bounds__(512) lmhead_v2_kernel(LmArgs a, int rblocks) {
   constexpr int NB = DW / 16;            // 16-column z blocks per slice
   constexpr int CHUNK = 32 * 32;         // elements per chunk
   __shared__ __attribute__((aligned(16))) uint16_t Es[NW * NKS * CHUNK];
-  __shared__ __attribute__((aligned(16))) f32x4 red[NW][2][2][64];   // [wave][vb][rb][lane]
+  __shared__ __attribute__((aligned(16))) float red[NW][MT][VT];   // [wave][row][vocab], swizzled groups
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -384,10 +395,9 @@ __global__ void __launch_bounds__(512) lmhead_v2_kernel(LmArgs a, int rblocks) {
 
   // DMA of chunk c of tile `tile` into this wave's slice: 2 x 64 lanes x 16 B.
   // Lane i fills LDS piece i of the half: row 16 h + i / 4, physical piece
-  // i % 4, which holds the row's logical piece swz(row, i % 4); the swizzle
-  // depends only on row / 4 mod 4 = (i / 16) mod 4, the same for both halves.
-  const uint32_t dma_off = static_cast<uint32_t>(
-      ((lane >> 2) * a.d + ((lane & 3) ^ ((lane >> 4) & 3)) * 8) * 2);
+  // i % 4, which holds the row's logical piece swz(row, i % 4) (an XOR, so
+  // its own inverse); the swizzle ignores row bit 4, so both halves share it.
+  const uint32_t dma_off = static_cast<uint32_t>(((lane >> 2) * a.d + swz(lane >> 2, lane & 3) * 8) * 2);
   auto dma_chunk = [&](int tile, int c) {
     const uint16_t *tb = a.E + static_cast<int64_t>(tile * VT) * a.d + dcol0 + c * 32;
 #pragma unroll
@@ -425,11 +435,8 @@ __global__ void __launch_bounds__(512) lmhead_v2_kernel(LmArgs a, int rblocks) {
   }
   float m_ref = -INFINITY, l_run = 0.f, best_v = -INFINITY;
   int best_i = -1;
-  // where this lane's pair sits in a partial slot
-  const int e_vb = j2 >> 3;
-  const int e_rb = erow >> 4;
-  const int e_lc = ((j2 & 7) >> 1) * 16 + (erow & 15);
-  const int e_el = 2 * (j2 & 1);
+  // where this lane's pair (vocab 2 j2, 2 j2 + 1 of row erow) sits in a slot
+  const int e_off = erow * VT + rswz(erow, j2 >> 1) * 4 + 2 * (j2 & 1);
 
   f32x4 zacc[2][NB];
 #pragma unroll
@@ -462,10 +469,14 @@ __global__ void __launch_bounds__(512) lmhead_v2_kernel(LmArgs a, int rblocks) {
           sacc[vb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ef, hreg[rb][c], sacc[vb][rb], 0, 0, 0);
       }
     }
+    // lane (q, m) of block (vb, rb) holds row 16 rb + m, vocab 16 vb + 4 q + [0, 4)
 #pragma unroll
     for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) red[wave][vb][rb][lane] = sacc[vb][rb];
+      for (int rb = 0; rb < 2; ++rb) {
+        const int r = rb * 16 + (lane & 15);
+        *reinterpret_cast<f32x4 *>(&red[wave][r][rswz(r, vb * 4 + (lane >> 4)) * 4]) = sacc[vb][rb];
+      }
     __syncthreads();
 
     // ---- epilogue for rows 4 wave .. 4 wave + 3
@@ -473,7 +484,7 @@ __global__ void __launch_bounds__(512) lmhead_v2_kernel(LmArgs a, int rblocks) {
       float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float2 pr = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(&red[w][e_vb][e_rb][e_lc]) + e_el);
+        const float2 pr = *reinterpret_cast<const float2 *>(&red[w][0][0] + e_off);
         acc0 += pr.x;
         acc1 += pr.y;
       }
@@ -516,9 +527,11 @@ __global__ void __launch_bounds__(512) lmhead_v2_kernel(LmArgs a, int rblocks) {
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) ps += __shfl_xor(ps, o, 64);
       l_run = l_run * sc + ps;
-      float *slot = reinterpret_cast<float *>(&red[wave][e_vb][e_rb][e_lc]);
-      slot[e_el] = __uint_as_float(pack_bf16x2(p0f, p1f));
-      if (j2 == 0) slot[1] = sc;
+      // P and the rescale factor go back into positions of this wave's own
+      // slot that only this wave reads (its rows)
+      float *slot = &red[wave][0][0] + e_off;
+      slot[0] = __uint_as_float(pack_bf16x2(p0f, p1f));
+      if (j2 == 0) slot[1] = sc;            // vocab 1 of the row: group 0, element 1
     }
     __syncthreads();
 
@@ -527,17 +540,18 @@ __global__ void __launch_bounds__(512) lmhead_v2_kernel(LmArgs a, int rblocks) {
     float scl[2][4];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      const int m = rb * 16 + (lane & 15);
+      const int M = rb * 16 + (lane & 15);          // A-operand row of this lane
       const int q = lane >> 4;
-      const float *s0p = reinterpret_cast<const float *>(&red[m >> 2][0][rb][q * 16 + (lane & 15)]);
-      const float *s1p = reinterpret_cast<const float *>(&red[m >> 2][1][rb][q * 16 + (lane & 15)]);
-      const uint32_t w4[4] = {__float_as_uint(s0p[0]), __float_as_uint(s0p[2]),
-                              __float_as_uint(s1p[0]), __float_as_uint(s1p[2])};
+      const float *rowp = &red[M >> 2][M][0];
+      const uint32_t w4[4] = {__float_as_uint(rowp[rswz(M, q) * 4]),
+                              __float_as_uint(rowp[rswz(M, q) * 4 + 2]),
+                              __float_as_uint(rowp[rswz(M, 4 + q) * 4]),
+                              __float_as_uint(rowp[rswz(M, 4 + q) * 4 + 2])};
       pa[rb] = *reinterpret_cast<const bf16x8 *>(w4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int mr = rb * 16 + q * 4 + i;
-        scl[rb][i] = reinterpret_cast<const float *>(&red[mr >> 2][0][rb][mr & 15])[1];
+        const int mr = rb * 16 + q * 4 + i;         // z-accumulator rows of this lane
+        scl[rb][i] = red[mr >> 2][mr][rswz(mr, 0) * 4 + 1];
       }
     }
     __syncthreads();   // every wave holds its P and factors: the slots may be reused
