@@ -198,8 +198,13 @@ def dg_generate_canvas(model, K_pre, V_pre, steps, seed, x_out, z_out=None, stre
                                              int(seed), _ptr(x_out), _ptr(z_out), _stream(stream)))
 
 
-def dg_profile_enable(model, on=True):
-    _check(load_library().dg_profile_enable(model.handle, 1 if on else 0))
+def dg_profile_enable(model, stages=None):
+    """Time the named stages (all when None; nothing for an empty list)."""
+    names = STAGES if stages is None else stages
+    mask = 0
+    for n in names:
+        mask |= 1 << STAGES.index(n)
+    _check(load_library().dg_profile_enable(model.handle, mask))
 
 
 def dg_profile_read(model):

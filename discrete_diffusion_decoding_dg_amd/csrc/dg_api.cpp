@@ -161,7 +161,7 @@ struct dg_model {
   int32_t *genx;
   char *genz;
   // profiling: event pairs recorded around stage launches while enabled
-  bool prof_on = false;
+  int prof_mask = 0;
   struct Mark {
     int stage;
     hipEvent_t a, b;
@@ -178,7 +178,7 @@ struct StageTimer {
   hipStream_t st;
   hipEvent_t a = nullptr, b = nullptr;
   StageTimer(dg_model *m_, int stage_, hipStream_t st_) : m(m_), stage(stage_), st(st_) {
-    if (m->prof_on && hipEventCreate(&a) == hipSuccess && hipEventCreate(&b) == hipSuccess)
+    if (((m->prof_mask >> stage) & 1) && hipEventCreate(&a) == hipSuccess && hipEventCreate(&b) == hipSuccess)
       (void)hipEventRecord(a, st);
   }
   ~StageTimer() {
@@ -371,10 +371,10 @@ dg_status dg_create(const dg_config *cfg, const dg_weights *w, dg_model **out) {
   return DG_OK;
 }
 
-dg_status dg_profile_enable(dg_model *m, int on) {
+dg_status dg_profile_enable(dg_model *m, int mask) {
   g_err.clear();
   if (!m) return fail(DG_ERR_INVALID_ARG, "model is NULL");
-  m->prof_on = on != 0;
+  m->prof_mask = mask & ((1 << DG_NUM_STAGES) - 1);
   return DG_OK;
 }
 

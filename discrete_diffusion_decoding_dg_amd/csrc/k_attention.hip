@@ -212,6 +212,209 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Second version: K and V tiles stay row-major in LDS (rows padded so that the
+// 16-row operand reads of K and the 4-row transposed reads of V hit distinct
+// banks), V reaches the O contraction through ds_read_b64_tr_b16, and the
+// next tile is fetched into registers while the current one is computed.
+template <int HD> struct AttnPitch;
+template <> struct AttnPitch<64> { static constexpr int K = 72, V = 80; };
+template <> struct AttnPitch<128> { static constexpr int K = 136, V = 144; };
+template <> struct AttnPitch<176> { static constexpr int K = 200, V = 208; };
+
+template <int HD>
+__global__ void __launch_bounds__(256) attn_fwd_v2_kernel(AttnArgs a) {
+  constexpr int HDP = round_up32(HD);
+  constexpr int KP = AttnPitch<HD>::K, VP = AttnPitch<HD>::V;
+  static_assert(KP >= HDP, "score operand reads stay inside a K row");
+  constexpr int NKS = HDP / 32;
+  constexpr int NB = HD / 16;
+  constexpr int CH = HD / 8;                       // 16-byte chunks per key row
+  constexpr int PER = (BKV * CH + 255) / 256;      // chunks per thread per tile and tensor
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BKV * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[BKV * VP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qb = blockIdx.x, g = blockIdx.y;
+  const int b = blockIdx.z / a.splits, split = blockIdx.z - b * a.splits;
+  const int GC = a.G * a.C;
+  const int Lk = a.P + a.C;
+  const int64_t hd_stride = HD;
+  const int qcols = a.Hq * HD;
+
+  if (KP > HD)   // pad columns of K are read (against zero q) and must be finite
+    for (int c = tid; c < BKV * (KP - HD); c += 256)
+      Ks[(c / (KP - HD)) * KP + HD + c % (KP - HD)] = 0;
+
+  const int qr = qb * BQ + wave * 16 + (lane & 15);
+  const bool qvalid = qr < GC;
+  const int qh = qvalid ? g * a.G + qr / a.C : 0;
+  const int qi = qvalid ? qr % a.C : 0;
+  bf16x8 qreg[NKS];
+  {
+    const uint16_t *qrow = a.q + (static_cast<int64_t>(b) * a.C + qi) * qcols + qh * hd_stride;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int e = ks * 32 + (lane >> 4) * 8;
+      qreg[ks] = (qvalid && e < HD) ? *reinterpret_cast<const bf16x8 *>(qrow + e) : bf16x8{};
+    }
+  }
+
+  f32x4 oacc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int64_t kvp_base = (static_cast<int64_t>(b) * a.Hkv + g) * a.P * hd_stride;
+  const int64_t kvc_base = (static_cast<int64_t>(b) * a.Hkv + g) * a.C * hd_stride;
+  const int tile0 = split * a.tiles_per_split;
+  const int total_tiles = (Lk + BKV - 1) / BKV;
+  int tile_end = tile0 + a.tiles_per_split;
+  if (tile_end > total_tiles) tile_end = total_tiles;
+
+  uint4 kreg[PER], vreg[PER];
+  auto fetch = [&](int tile) {
+    const int kv0 = tile * BKV;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + 256 * u;
+      uint4 kk = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (c < BKV * CH) {
+        const int key = c / CH, col = (c - key * CH) * 8;
+        const int j = kv0 + key;
+        if (j < a.P) {
+          kk = *reinterpret_cast<const uint4 *>(a.Kp + kvp_base + j * hd_stride + col);
+          vv = *reinterpret_cast<const uint4 *>(a.Vp + kvp_base + j * hd_stride + col);
+        } else if (j < Lk) {
+          kk = *reinterpret_cast<const uint4 *>(a.k + kvc_base + (j - a.P) * hd_stride + col);
+          vv = *reinterpret_cast<const uint4 *>(a.v + kvc_base + (j - a.P) * hd_stride + col);
+        }
+      }
+      kreg[u] = kk;
+      vreg[u] = vv;
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + 256 * u;
+      if (c < BKV * CH) {
+        const int key = c / CH, col = (c - key * CH) * 8;
+        *reinterpret_cast<uint4 *>(&Ks[key * KP + col]) = kreg[u];
+        *reinterpret_cast<uint4 *>(&Vs[key * VP + col]) = vreg[u];
+      }
+    }
+  };
+
+  if (tile0 < tile_end) {
+    fetch(tile0);
+    __syncthreads();            // pad zeroing done before rows land
+    stash();
+    if (tile0 + 1 < tile_end) fetch(tile0 + 1);
+    __syncthreads();
+  }
+  // transposed-read source address of this lane (see the LM head for the
+  // lane mapping of ds_read_b64_tr_b16)
+  const int tr_row = 4 * (lane >> 4) + ((lane & 15) >> 2);
+  const int tr_col = 4 * (lane & 3);
+
+  for (int tile = tile0; tile < tile_end; ++tile) {
+    const int kv0 = tile * BKV;
+    f32x4 s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint16_t *krow = &Ks[(kb * 16 + (lane & 15)) * KP + (lane >> 4) * 8];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(krow + ks * 32);
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qreg[ks], s[kb], 0, 0, 0);
+      }
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = kv0 + kb * 16 + (lane >> 4) * 4 + r;
+        const float val = (j < Lk) ? s[kb][r] * a.scale_log2 : -INFINITY;
+        s[kb][r] = val;
+        tmax = fmaxf(tmax, val);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = exp2f(m_run - m_new);
+    float psum = 0.f;
+    bf16x8 pa[2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = exp2f(s[kb][r] - m_new);
+        psum += p;
+        pa[kb >> 1][(kb & 1) * 4 + r] = static_cast<__bf16>(p);
+      }
+    }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    float arow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) arow[i] = __shfl(alpha, (lane >> 4) * 4 + i, 64);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[nb][i] *= arow[i];
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        const int col = nb * 16 + tr_col;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)&Vs[(ks2 * 32 + tr_row) * VP + col]);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)&Vs[(ks2 * 32 + 16 + tr_row) * VP + col]);
+        const uint16_t w8[8] = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
+                                (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
+        const bf16x8 vb = *reinterpret_cast<const bf16x8 *>(w8);
+        oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[ks2], vb, oacc[nb], 0, 0, 0);
+      }
+    }
+    if (tile + 1 < tile_end) {
+      __syncthreads();          // everyone is done with this tile's K and V
+      stash();                  // the next tile, fetched during this one
+      if (tile + 2 < tile_end) fetch(tile + 2);
+      __syncthreads();
+    }
+  }
+
+  float lrow[4], mrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lrow[i] = __shfl(l_run, (lane >> 4) * 4 + i, 64);
+    mrow[i] = __shfl(m_run, (lane >> 4) * 4 + i, 64);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = qb * BQ + wave * 16 + (lane >> 4) * 4 + i;
+    if (row >= GC) continue;
+    const int h = g * a.G + row / a.C, ii = row % a.C;
+    const int64_t r = static_cast<int64_t>(b) * a.C + ii;
+    if (a.splits == 1) {
+      const float inv = 1.f / lrow[i];
+      uint16_t *orow = a.o + r * qcols + h * hd_stride;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) orow[nb * 16 + (lane & 15)] = f32_to_bf16(oacc[nb][i] * inv);
+    } else {
+      const int64_t R = static_cast<int64_t>(a.B) * a.C;
+      float *prow = a.opart + ((split * R + r) * a.Hq + h) * hd_stride;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) prow[nb * 16 + (lane & 15)] = oacc[nb][i];
+      if ((lane & 15) == 0) a.ml[(split * R + r) * a.Hq + h] = make_float2(mrow[i], lrow[i]);
+    }
+  }
+}
+
 // o[r, h, e] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
 __global__ void __launch_bounds__(256) attn_combine_kernel(const float *__restrict__ opart,
                                                            const float2 *__restrict__ ml,
@@ -274,9 +477,9 @@ hipError_t launch_attention_bf16(const uint16_t *q, const uint16_t *k, const uin
   a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(s.hd)));
   dim3 grid((s.G() * s.C + BQ - 1) / BQ, s.Hkv, s.B * a.splits);
   switch (s.hd) {
-    case 64: hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(256), 0, st, a); break;
-    case 128: hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(256), 0, st, a); break;
-    case 176: hipLaunchKernelGGL(attn_fwd_kernel<176>, grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(attn_fwd_v2_kernel<64>, grid, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL(attn_fwd_v2_kernel<128>, grid, dim3(256), 0, st, a); break;
+    case 176: hipLaunchKernelGGL(attn_fwd_v2_kernel<176>, grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();

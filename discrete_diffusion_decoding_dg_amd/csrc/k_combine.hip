@@ -6,11 +6,17 @@
 // keep x_t unless the row's Bernoulli u < lambda_b, in which case take the
 // Gumbel argmax over the whole vocabulary (ties: lowest id, i.e. the lowest
 // split wins an exact tie between splits).
+//
+// Grid: (row, strip of 1024 columns). The first wave of each block merges
+// the row's split statistics (one split per lane, wave-wide max / sum /
+// argmax); then every thread streams 4 consecutive columns of all splits.
 #include "dg_device.hpp"
 #include "dg_kernels.hpp"
 
 namespace dg {
 namespace {
+
+constexpr int kMaxSplits = 64;
 
 template <typename T>
 __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restrict__ part,
@@ -22,38 +28,74 @@ __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restri
                                                       T *__restrict__ z_out,
                                                       float *__restrict__ lse,
                                                       int32_t *__restrict__ best) {
-  __shared__ float wsh[64];
+  __shared__ float wsh[kMaxSplits];
   __shared__ float inv_l;
   const int r = blockIdx.x;
-  if (splits > 64) return;  // the host never plans more than 64 splits
-  if (threadIdx.x == 0) {
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, part[static_cast<int64_t>(s) * R + r].m);
-    float L = 0.f, bv = -INFINITY;
-    int bi = -1;
-    for (int s = 0; s < splits; ++s) {
-      const RowPartial p = part[static_cast<int64_t>(s) * R + r];
-      const float w = exp2f(p.m - M);
-      wsh[s] = w;
-      L += w * p.l;
-      if (p.arg >= 0 && p.best > bv) { bv = p.best; bi = p.arg; }
+  if (threadIdx.x < 64) {
+    const int s = threadIdx.x;
+    RowPartial p;
+    p.m = -INFINITY;
+    p.l = 0.f;
+    p.best = -INFINITY;
+    p.arg = -1;
+    if (s < splits) p = part[static_cast<int64_t>(s) * R + r];
+    const float M = wave_max(p.m);
+    const float w = (s < splits) ? exp2f(p.m - M) : 0.f;
+    const float L = wave_sum(w * p.l);
+    wsh[s] = w;
+    // argmax of the best draw over splits; an exact tie goes to the lower split
+    float bv = p.arg >= 0 ? p.best : -INFINITY;
+    int bs = p.arg >= 0 ? s : kMaxSplits;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int os = __shfl_xor(bs, o, 64);
+      if (ov > bv || (ov == bv && os < bs)) { bv = ov; bs = os; }
     }
-    inv_l = 1.f / L;
-    const int b = r / C, i = r - b * C;
-    const u32x4 w = philox4x32_10(0u, static_cast<uint32_t>(i), static_cast<uint32_t>(b),
-                                  kStreamBernoulli, k0, k1);
-    const bool rs = u01(w.x) < prm[b].lam;
-    x_out[r] = rs ? bi : x_t[r];
-    if (lse) lse[r] = (M + log2f(L)) * 0.6931471805599453f;
-    if (best) best[r] = rs ? bi : -1;
+    const int bi = __shfl(p.arg, bs < kMaxSplits ? bs : 0, 64);
+    if (s == 0) {
+      inv_l = 1.f / L;
+      if (blockIdx.y == 0) {
+        const int b = r / C, i = r - b * C;
+        const u32x4 u = philox4x32_10(0u, static_cast<uint32_t>(i), static_cast<uint32_t>(b),
+                                      kStreamBernoulli, k0, k1);
+        const bool rs = u01(u.x) < prm[b].lam;
+        const int y = bs < kMaxSplits ? bi : -1;
+        x_out[r] = rs ? y : x_t[r];
+        if (lse) lse[r] = (M + log2f(L)) * 0.6931471805599453f;
+        if (best) best[r] = rs ? y : -1;
+      }
+    }
   }
   __syncthreads();
   const float il = inv_l;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < splits; ++s)
-      acc += wsh[s] * zpart[(static_cast<int64_t>(s) * R + r) * d + c];
-    Act<T>::store(z_out, static_cast<int64_t>(r) * d + c, acc * il);
+  const int c0 = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
+  if (c0 >= d) return;
+  const int64_t rowoff = static_cast<int64_t>(r) * d;
+  if (c0 + 4 <= d && (d & 3) == 0) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float *zp = zpart + rowoff + c0;
+    const int64_t sstride = static_cast<int64_t>(R) * d;
+#pragma unroll 8
+    for (int s = 0; s < splits; ++s) {
+      const float4 v = *reinterpret_cast<const float4 *>(zp + s * sstride);
+      const float w = wsh[s];
+      acc.x += w * v.x;
+      acc.y += w * v.y;
+      acc.z += w * v.z;
+      acc.w += w * v.w;
+    }
+    Act<T>::store(z_out, rowoff + c0, acc.x * il);
+    Act<T>::store(z_out, rowoff + c0 + 1, acc.y * il);
+    Act<T>::store(z_out, rowoff + c0 + 2, acc.z * il);
+    Act<T>::store(z_out, rowoff + c0 + 3, acc.w * il);
+  } else {
+    for (int c = c0; c < d && c < c0 + 4; ++c) {
+      float acc = 0.f;
+      for (int s = 0; s < splits; ++s)
+        acc += wsh[s] * zpart[(static_cast<int64_t>(s) * R + r) * d + c];
+      Act<T>::store(z_out, rowoff + c, acc * il);
+    }
   }
 }
 
@@ -64,17 +106,18 @@ hipError_t launch_combine(bool bf16, const void *work, int splits, const int32_t
                           void *z_out, float *lse, int32_t *best, hipStream_t st) {
   const int R = s.R();
   if (R == 0) return hipSuccess;
-  if (splits < 1 || splits > 64) return hipErrorInvalidValue;
+  if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
   const RowPartial *part = static_cast<const RowPartial *>(work);
   const float *zpart = reinterpret_cast<const float *>(static_cast<const char *>(work) +
                                                        static_cast<size_t>(splits) * R * sizeof(RowPartial));
   const uint32_t k0 = static_cast<uint32_t>(seed), k1 = static_cast<uint32_t>(seed >> 32);
+  const dim3 grid(R, (s.d + 1023) / 1024);
   if (bf16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(R), dim3(256), 0, st, part, zpart, splits,
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, st, part, zpart, splits,
                        x_t, prm, R, s.C, s.d, k0, k1, x_out, static_cast<uint16_t *>(z_out), lse,
                        best);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(R), dim3(256), 0, st, part, zpart, splits, x_t,
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, st, part, zpart, splits, x_t,
                        prm, R, s.C, s.d, k0, k1, x_out, static_cast<float *>(z_out), lse, best);
   return hipGetLastError();
 }

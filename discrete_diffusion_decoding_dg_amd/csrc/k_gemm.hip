@@ -136,6 +136,137 @@ __global__ void __launch_bounds__(256) gemm_tn_bf16_kernel(const uint16_t *__res
   }
 }
 
+// ---------------------------------------------------------------------------
+// Deep-pipelined variant for K % 64 == 0: NS stages of 64-wide A and B slabs
+// (8 KB each) are requested NS-1 slabs ahead with direct global->LDS loads,
+// so about 80 KB per block is in flight -- what it takes to cover the memory
+// latency at the rate the matrix cores consume slabs. Rows of a slab are 128
+// bytes; the 16-byte piece p of row r sits at p ^ ((r ^ (r >> 3)) & 7), which
+// keeps the 32-row operand reads free of bank conflicts (32 or 64 banks).
+constexpr int NS = 6;
+constexpr int SLAB = 64 * 64;            // elements per operand slab
+
+__device__ __forceinline__ int gswz(int r, int p) { return p ^ ((r ^ (r >> 3)) & 7); }
+
+// 16 bytes per lane from base + voff into LDS at lds + 16 * lane (see the LM
+// head for why this is issued through inline asm).
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, const uint16_t *lds) {
+  const uint32_t m0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint16_t *)lds))));
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+  const uint64_t sb = (static_cast<uint64_t>(hi) << 32) | lo;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(voff), "s"(sb)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void vm_wait_le(int n) {
+  switch (n) {
+    case 0: vm_wait<0>(); break;
+    case 4: vm_wait<4>(); break;
+    case 8: vm_wait<8>(); break;
+    case 2: vm_wait<2>(); break;
+    case 6: vm_wait<6>(); break;
+    case 10: vm_wait<10>(); break;
+    case 12: vm_wait<12>(); break;
+    case 16: vm_wait<16>(); break;
+    default: vm_wait<0>(); break;
+  }
+}
+
+// 8 waves: wave (wk, wm, wn) computes the 32 x 32 quadrant (wm, wn) over the
+// k-steps 2 wk, 2 wk + 1 of every slab; the two k-halves meet in LDS at the
+// end. Two waves per SIMD and two independent accumulation chains per
+// quadrant keep the matrix cores fed while slabs stream in.
+template <class Epi>
+__global__ void __launch_bounds__(512) gemm_tn_bf16_dma_kernel(const uint16_t *__restrict__ A,
+                                                               int M, int N, int K, Epi epi) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[NS * SLAB];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[NS * SLAB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wk = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int nk = K / 64;
+
+  // wave w loads slab rows 8 w .. 8 w + 7 of A and of B: one DMA instruction
+  // each, lane i -> row 8 w + i / 8, physical piece i % 8. A lane's row is
+  // clamped to the last valid one, so rows past M (or N) re-read a valid row
+  // and every access stays inside the matrix; their results are never
+  // stored. Offsets are bytes from the matrix (A) or tile (B) base and fit
+  // in 32 bits (rows * K * 2 < 2^32). The rows of a tile come from one
+  // weight matrix (N-sections are multiples of 64), whose row n0 is the base.
+  const uint16_t *bbase = epi.brow(n0, K);
+  const int r = 8 * wave + (lane >> 3);                // slab row of this lane
+  const int piece = gswz(r, lane & 7);                 // logical piece kept at piece lane & 7
+  const int am = (m0 + r < M) ? m0 + r : M - 1;
+  const int bn = (n0 + r < N) ? r : N - 1 - n0;
+  const uint32_t voff_a = static_cast<uint32_t>((static_cast<int64_t>(am) * K + piece * 8) * 2);
+  const uint32_t voff_b = static_cast<uint32_t>((static_cast<int64_t>(bn) * K + piece * 8) * 2);
+  auto issue = [&](int it) {
+    const int buf = it % NS;
+    dma16(A + it * 64, voff_a, As + buf * SLAB + 8 * wave * 64);
+    dma16(bbase + it * 64, voff_b, Bs + buf * SLAB + 8 * wave * 64);
+  };
+  for (int it = 0; it < NS - 1 && it < nk; ++it) issue(it);
+
+  f32x16 acc = {};
+  const int ar = wm * 32 + (lane & 31), br = wn * 32 + (lane & 31);
+  for (int it = 0; it < nk; ++it) {
+    int younger = nk - 1 - it;                      // slabs issued after this one
+    if (younger > NS - 2) younger = NS - 2;
+    vm_wait_le(2 * younger);
+    __syncthreads();                                // every wave's part of slab `it` landed
+    if (it + NS - 1 < nk) issue(it + NS - 1);       // refill the slab computed last iteration
+    const uint16_t *as = As + (it % NS) * SLAB;
+    const uint16_t *bs = Bs + (it % NS) * SLAB;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int p = 2 * (2 * wk + kk) + (lane >> 5);
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(as + ar * 64 + gswz(ar, p) * 8);
+      const bf16x8 b = *reinterpret_cast<const bf16x8 *>(bs + br * 64 + gswz(br, p) * 8);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    }
+  }
+
+  // k-halves meet in LDS (the stage buffers are free once everyone is here)
+  __syncthreads();
+  float *part = reinterpret_cast<float *>(As) + ((wm * 2 + wn) * 16) * 64;
+  if (wk == 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part[i * 64 + lane] = acc[i];
+  }
+  __syncthreads();
+  if (wk == 1) return;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] += part[i * 64 + lane];
+
+  const int n = n0 + wn * 32 + (lane & 31);
+  if (n < N) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * 32 + 8 * j + 4 * (lane >> 5) + i;
+        if (m < M) epi.store(m, n, acc[4 * j + i]);
+      }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_qkv_bf16(const uint16_t *h0, const uint16_t *Wq, const uint16_t *Wk,
@@ -145,7 +276,10 @@ hipError_t launch_qkv_bf16(const uint16_t *h0, const uint16_t *Wq, const uint16_
   const int M = s.R(), N = s.Hq * s.hd + 2 * s.Hkv * s.hd;
   if (M == 0) return hipSuccess;
   dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
-  hipLaunchKernelGGL(gemm_tn_bf16_kernel<QkvEpi>, grid, dim3(256), 0, st, h0, M, N, s.d, epi);
+  if (s.d % 64 == 0 && (s.Hq * s.hd) % 64 == 0 && (s.Hkv * s.hd) % 64 == 0)
+    hipLaunchKernelGGL(gemm_tn_bf16_dma_kernel<QkvEpi>, grid, dim3(512), 0, st, h0, M, N, s.d, epi);
+  else
+    hipLaunchKernelGGL(gemm_tn_bf16_kernel<QkvEpi>, grid, dim3(256), 0, st, h0, M, N, s.d, epi);
   return hipGetLastError();
 }
 
@@ -155,7 +289,10 @@ hipError_t launch_oproj_bf16(const uint16_t *o, const uint16_t *Wo, const uint16
   const int M = s.R(), N = s.d, K = s.Hq * s.hd;
   if (M == 0) return hipSuccess;
   dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
-  hipLaunchKernelGGL(gemm_tn_bf16_kernel<ResidualEpi>, grid, dim3(256), 0, st, o, M, N, K, epi);
+  if (K % 64 == 0)
+    hipLaunchKernelGGL(gemm_tn_bf16_dma_kernel<ResidualEpi>, grid, dim3(512), 0, st, o, M, N, K, epi);
+  else
+    hipLaunchKernelGGL(gemm_tn_bf16_kernel<ResidualEpi>, grid, dim3(256), 0, st, o, M, N, K, epi);
   return hipGetLastError();
 }
 

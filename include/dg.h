@@ -167,6 +167,9 @@ dg_status dg_generate_canvas(dg_model *m, const void *K_pre, const void *V_pre, 
  * Stages: 0 embed, 1 q/k/v projection, 2 attention (+ split merge),
  * 3 output projection, 4 LM head (logits, softmax statistics, z partials,
  * Gumbel argmax), 5 split merge + Step select, 6 corruption.
+ * dg_profile_enable(m, mask) times the stages whose bit (1 << stage) is set
+ * in mask (0 turns profiling off; every event pair adds a few microseconds of
+ * queue time between kernels, so time only the stages you need).
  * dg_profile_read waits for the recorded events, returns the summed
  * milliseconds and the number of timed launches per stage, and clears them. */
 #define DG_NUM_STAGES 7
@@ -174,7 +177,7 @@ typedef struct dg_profile {
   double ms[DG_NUM_STAGES];
   int64_t count[DG_NUM_STAGES];
 } dg_profile;
-dg_status dg_profile_enable(dg_model *m, int on);
+dg_status dg_profile_enable(dg_model *m, int mask);
 dg_status dg_profile_read(dg_model *m, dg_profile *out);
 
 const char *dg_status_string(dg_status s);
