@@ -110,6 +110,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-corrupt", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB device to device three times (a plain copy kernel "
+                         "of known size, to scale HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -127,6 +130,13 @@ def main():
     cfg = get_config(args.workload)
     inp = make_inputs(cfg)
     torch.cuda.set_device(0)
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wdev = {n: to_dev(inp, n, cfg) for n in ["E", "Wq", "Wk", "Wv", "Wo"]}
     model = dg.dg_create(config_args(cfg), wdev["E"], wdev["Wq"], wdev["Wk"], wdev["Wv"], wdev["Wo"])
     Kp, Vp, z = (to_dev(inp, n, cfg) for n in ["K_pre", "V_pre", "z"])
