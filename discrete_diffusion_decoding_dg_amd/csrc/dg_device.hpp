@@ -86,6 +86,14 @@ __device__ __forceinline__ float gumbel(uint32_t w) {
 
 enum : uint32_t { kStreamGumbel = 0, kStreamBernoulli = 1, kStreamCorrupt = 2 };
 
+// Gumbel-stream counter layout: vocabulary id v uses word (v >> 4) & 3 of
+// block 16 (v >> 6) + (v & 15), so block j of each aligned group of 64 ids
+// serves ids j, j + 16, j + 32, j + 48.
+__device__ __forceinline__ uint32_t gumbel_block_of(int v) {
+  return 16u * static_cast<uint32_t>(v >> 6) + static_cast<uint32_t>(v & 15);
+}
+__device__ __forceinline__ int gumbel_word_of(int v) { return (v >> 4) & 3; }
+
 // ------------------------------------------------------ small reductions ---
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -163,10 +163,10 @@ __global__ void __launch_bounds__(256) lmhead_f32_kernel(const float *__restrict
       const float s = acc * inv_tau;
       if (p0) p0[static_cast<int64_t>(r) * V + v] = s;
       if (rs) {
-        const u32x4 w = philox4x32_10(static_cast<uint32_t>(v >> 2), static_cast<uint32_t>(i),
+        const u32x4 w = philox4x32_10(gumbel_block_of(v), static_cast<uint32_t>(i),
                                       static_cast<uint32_t>(b), kStreamGumbel, k0, k1);
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-        const float pv = s + gumbel(ws[v & 3]);
+        const float pv = s + gumbel(ws[gumbel_word_of(v)]);
         if (pv > bv) { bv = pv; bi = v; }
       }
       s2 = s * kLog2e;

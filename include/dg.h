@@ -21,7 +21,8 @@
  *
  * Random numbers: Philox4x32-10 (Salmon et al., SC'11), key = (lo32(seed),
  * hi32(seed)), counter (c0, c1, c2, stream):
- *   Gumbel noise   (v >> 2, i, b, 0), word v & 3;      G = -log(-log U)
+ *   Gumbel noise   (16 (v >> 6) + (v & 15), i, b, 0), word (v >> 4) & 3;
+ *                  G = -log(-log U)
  *   Step Bernoulli (0, i, b, 1), word 0;              resample iff U < lambda_b
  *   corruption     (i >> 1, 0, b, 2), words 2(i&1) (keep iff U < kappa_b)
  *                  and 2(i&1)+1 (token floor(w V / 2^32))

@@ -11,7 +11,9 @@ the library and this oracle both implement this published generator.
 Counter map (ours; the pages are silent):
   key     = (low 32 bits of seed, high 32 bits of seed)
   counter = (c0, c1, c2, c3), c3 selects the stream:
-    stream 0, Gumbel noise:  (v >> 2, i, b, 0), word v & 3   (vocab id v)
+    stream 0, Gumbel noise:  (16 (v >> 6) + (v & 15), i, b, 0), word (v >> 4) & 3
+                             (vocab id v: block j of each aligned group of 64
+                             ids holds ids j, j+16, j+32, j+48)
     stream 1, Step Bernoulli: (0, i, b, 1), word 0
     stream 2, corruption:    (i >> 1, 0, b, 2), words 2*(i&1) (keep draw)
                              and 2*(i&1)+1 (replacement token)

@@ -23,13 +23,19 @@ def bernoulli_uniforms(seed, canvas_ids, C, positions=None):
     return uniform01(w0)
 
 
+def gumbel_block(v):
+    """(counter word 0, word index) of vocab id v in the Gumbel stream."""
+    v = np.asarray(v, dtype=np.uint64)
+    return ((v >> np.uint64(6)) << np.uint64(4)) | (v & np.uint64(15)), (v >> np.uint64(4)) & np.uint64(3)
+
+
 def gumbel_noise(seed, b, i, V):
     """G[n, v] = -log(-log U) in float32 for rows (b[n], i[n]) and all v < V."""
     b = np.asarray(b, dtype=np.uint64)[:, None]
     i = np.asarray(i, dtype=np.uint64)[:, None]
-    blk = np.arange((V + 3) // 4, dtype=np.uint64)[None, :]
-    words = philox4x32_10(blk, i, b, 0, seed)
-    w = np.stack(words, axis=-1).reshape(b.shape[0], -1)[:, :V]   # word v & 3 of block v >> 2
+    c0, word = gumbel_block(np.arange(V))
+    words = philox4x32_10(c0[None, :], i, b, 0, seed)       # 4 x [N, V]
+    w = np.choose(word.astype(np.int64)[None, :], words)    # word (v >> 4) & 3 of v's block
     u = uniform01(w)
     e1 = np.log(u)                      # float32, < 0
     e2 = np.log(-e1)                    # float32
