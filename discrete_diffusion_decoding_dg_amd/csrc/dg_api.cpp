@@ -189,9 +189,12 @@ struct StageTimer {
   }
 };
 
+// prm: device step constants of every canvas; when n_inline > 0 the embedding
+// launch first stores them there from the host array `inline_prm`.
 dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void *Kp,
-                   const void *Vp, const dg::StepParams *prm, uint64_t seed, int32_t *x_out,
-                   void *z_out, const dg_taps *taps, float *lse, float *p0, hipStream_t st) {
+                   const void *Vp, dg::StepParams *prm, const dg::StepParams *inline_prm,
+                   int n_inline, uint64_t seed, int32_t *x_out, void *z_out,
+                   const dg_taps *taps, float *lse, float *p0, hipStream_t st) {
   const dg::Shape &s = m->s;
   const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
   void *h0 = taps && taps->h0 ? taps->h0 : m->h0;
@@ -203,7 +206,9 @@ dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void 
   int32_t *best = taps ? taps->best : nullptr;
   {
     StageTimer tm(m, 0, st);
-    DG_HIP(dg::launch_embed(bf16, m->w.E, x_t, z_t, s.R(), s.d, s.V, h0, st), "embed launch");
+    DG_HIP(dg::launch_embed(bf16, m->w.E, x_t, z_t, s.R(), s.d, s.V, h0, prm, inline_prm, n_inline,
+                            st),
+           "embed launch");
   }
   if (bf16) {
     using u16 = uint16_t;
@@ -477,9 +482,12 @@ dg_status dg_denoise_step_taps(dg_model *m, const int32_t *x_t, const void *z_t,
   hipStream_t st = static_cast<hipStream_t>(stream);
   std::vector<dg::StepParams> prm(s.B);
   for (int b = 0; b < s.B; ++b) prm[b] = step_params(t[b], dt, m->cfg.schedule);
-  if (dg_status e = upload_params(m, m->prm, prm, st)) return e;
-  return run_step(m, x_t, z_t, K_pre, V_pre, m->prm, seed, x_out, z_out, taps,
-                  taps ? taps->lse : nullptr, taps ? taps->p0 : nullptr, st);
+  // a few canvases: the constants ride along with the embedding launch
+  const int n_inline = s.B <= dg::kInlineParams ? s.B : 0;
+  if (!n_inline)
+    if (dg_status e = upload_params(m, m->prm, prm, st)) return e;
+  return run_step(m, x_t, z_t, K_pre, V_pre, m->prm, prm.data(), n_inline, seed, x_out, z_out,
+                  taps, taps ? taps->lse : nullptr, taps ? taps->p0 : nullptr, st);
 }
 
 dg_status dg_denoise_step(dg_model *m, const int32_t *x_t, const void *z_t, const void *K_pre,
@@ -536,7 +544,8 @@ dg_status dg_generate_canvas(dg_model *m, const void *K_pre, const void *V_pre, 
     int32_t *xo = last ? x_out : xb[nxt];
     void *zo = (last && z_out) ? z_out : zb[nxt];
     if (dg_status e = run_step(m, xb[cur], zb[cur], K_pre, V_pre, m->prm + static_cast<size_t>(k) * s.B,
-                               seed + static_cast<uint64_t>(k), xo, zo, nullptr, nullptr, nullptr, st))
+                               nullptr, 0, seed + static_cast<uint64_t>(k), xo, zo, nullptr, nullptr,
+                               nullptr, st))
       return e;
   }
   return DG_OK;

@@ -35,8 +35,12 @@ hipError_t launch_corrupt(const int32_t *x0, const float *kappa, int B, int C, i
                           uint64_t seed, int32_t *out, hipStream_t st);
 // h0 = round(E[x] + z); z may be null (treated as 0); tokens outside [0, V)
 // embed as a zero row.
+// h0 = E[x] + z; also stores `np` (<= kInlineParams) step constants from host
+// memory into prm (they travel as a kernel argument)
+constexpr int kInlineParams = 32;
 hipError_t launch_embed(bool bf16, const void *E, const int32_t *x, const void *z, int R, int d,
-                        int V, void *h0, hipStream_t st);
+                        int V, void *h0, StepParams *prm, const StepParams *prm_src, int np,
+                        hipStream_t st);
 // p0[r, v] = exp(p0[r, v] - lse[r]) in place (p0 holds scaled logits on entry).
 hipError_t launch_p0_from_logits(float *p0, const float *lse, int R, int V, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);

@@ -57,12 +57,25 @@ hipError_t launch_corrupt(const int32_t *x0, const float *kappa, int B, int C, i
 
 // h0 = round(E[x] + z): one block per row, 8 elements (16 bytes of bf16) per
 // thread and iteration when the row width allows it.
+// Step constants of up to kInlineParams canvases ride along with the embedding
+// launch as a kernel argument: block 0 stores them for the later kernels of
+// the step, which run after this one on the same stream.
+struct InlineParams {
+  StepParams p[kInlineParams];
+};
+
+__device__ __forceinline__ void store_inline_params(StepParams *dst, const InlineParams &c, int n) {
+  if (blockIdx.x == 0 && static_cast<int>(threadIdx.x) < n) dst[threadIdx.x] = c.p[threadIdx.x];
+}
+
 // A token outside [0, V) reads as a zero embedding row instead of faulting.
 template <typename T>
 __global__ void __launch_bounds__(256) embed_kernel(const T *__restrict__ E,
                                                     const int32_t *__restrict__ x,
                                                     const T *__restrict__ z, int d, int V,
-                                                    T *__restrict__ h0) {
+                                                    T *__restrict__ h0, StepParams *prm,
+                                                    InlineParams pc, int np) {
+  store_inline_params(prm, pc, np);
   const int r = blockIdx.x;
   const int32_t tok = x[r];
   const bool in = tok >= 0 && tok < V;
@@ -80,7 +93,10 @@ __global__ void __launch_bounds__(256) embed_bf16_vec_kernel(const uint16_t *__r
                                                              const int32_t *__restrict__ x,
                                                              const uint16_t *__restrict__ z,
                                                              int d, int V,
-                                                             uint16_t *__restrict__ h0) {
+                                                             uint16_t *__restrict__ h0,
+                                                             StepParams *prm, InlineParams pc,
+                                                             int np) {
+  store_inline_params(prm, pc, np);
   const int r = blockIdx.x;
   const int32_t tok = x[r];
   const bool in = tok >= 0 && tok < V;
@@ -108,21 +124,26 @@ __global__ void __launch_bounds__(256) embed_bf16_vec_kernel(const uint16_t *__r
 }
 
 hipError_t launch_embed(bool bf16, const void *E, const int32_t *x, const void *z, int R, int d,
-                        int V, void *h0, hipStream_t st) {
-  if (R == 0) return hipSuccess;
+                        int V, void *h0, StepParams *prm, const StepParams *prm_src, int np,
+                        hipStream_t st) {
+  if (np < 0 || np > kInlineParams || (np > 0 && (!prm || !prm_src))) return hipErrorInvalidValue;
+  if (R == 0) return np ? launch_set_params(prm, prm_src, np, st) : hipSuccess;
+  InlineParams pc;
+  for (int i = 0; i < np; ++i) pc.p[i] = prm_src[i];
+  for (int i = np; i < kInlineParams; ++i) pc.p[i] = StepParams{0.f, 0.f};
   if (bf16) {
     if (d % 8 == 0)
       hipLaunchKernelGGL(embed_bf16_vec_kernel, dim3(R), dim3(256), 0, st,
                          static_cast<const uint16_t *>(E), x, static_cast<const uint16_t *>(z), d,
-                         V, static_cast<uint16_t *>(h0));
+                         V, static_cast<uint16_t *>(h0), prm, pc, np);
     else
       hipLaunchKernelGGL(embed_kernel<uint16_t>, dim3(R), dim3(256), 0, st,
                          static_cast<const uint16_t *>(E), x, static_cast<const uint16_t *>(z), d,
-                         V, static_cast<uint16_t *>(h0));
+                         V, static_cast<uint16_t *>(h0), prm, pc, np);
   } else {
     hipLaunchKernelGGL(embed_kernel<float>, dim3(R), dim3(256), 0, st,
                        static_cast<const float *>(E), x, static_cast<const float *>(z), d,
-                       V, static_cast<float *>(h0));
+                       V, static_cast<float *>(h0), prm, pc, np);
   }
   return hipGetLastError();
 }

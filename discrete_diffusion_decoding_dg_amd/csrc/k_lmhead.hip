@@ -24,9 +24,10 @@
 //      (16x16x16 for 16-row blocks), E read transposed from LDS by
 //      ds_read_b64_tr_b16.
 // E tiles reach LDS by direct global->LDS loads (no register staging). With
-// two tile buffers (d <= 2048) the next tile is requested when the current
-// one starts, so its transfer overlaps a whole tile of work; a single buffer
-// (d = 2816) refills chunk by chunk behind the z contraction.
+// two tile buffers (d <= 2048) the next tile is requested in small batches
+// spread over the current tile, so its transfer overlaps a whole tile of work
+// without ever filling the load queue; a single buffer (d = 2816) refills
+// chunk by chunk behind the z contraction.
 //
 // Gumbel noise: the Philox block of lane (row, position j) for the aligned
 // group of four tiles g holds the noise of ids 64 g + j + {0, 16, 32, 48}, one
@@ -156,6 +157,7 @@ template <int MT, int DW, int NBUF>
 __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
   static_assert(MT == 16 || MT == 32, "row block");
   static_assert(DW % 32 == 0, "slice width");
+  static_assert(NW == 8, "the epilogue sums eight slice partials");
   constexpr int NKS = DW / 32;              // 32-column chunks per slice
   constexpr int RB = MT / 16;               // 16-row blocks of the score contraction
   constexpr int CHUNK_B = VT * 64;          // bytes per chunk
@@ -264,17 +266,13 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
     const int v0 = tile * VT;
     const bool more = tile + 1 < t_end;
     if (a.p0) wait_vmcnt<0>();   // checking mode: p0 stores share the counter
-    if constexpr (NBUF == 2) {
-      if (more) {
-        // the other buffer was last read by this wave's own z contraction of
-        // the previous tile, whose reads have all returned
-        wait_lgkm0();
-#pragma unroll
-        for (int c = 0; c < NKS; ++c) dma_chunk(tile + 1, c);
-      } else {
-        wait_vmcnt<0>();
-      }
-    }
+    // With two buffers the next tile streams into the other buffer in small
+    // batches spread over this tile (after the scores, after the epilogue and
+    // through the z contraction): the per-CU direct-load path moves about one
+    // tile per tile period, and a burst would stall the issuing waves.
+    // Each batch goes into the buffer of the previous tile, whose reads by
+    // this wave's own z contraction have all returned (they fed its MFMAs).
+    constexpr int kB1 = NKS / 4, kB2 = NKS / 2;   // chunk ranges [0,kB1) [kB1,kB2) [kB2,NKS)
     const uint8_t *eb = ebuf(tile);
 
     // ---- S^T partial over this wave's slice (two accumulator sets break the
@@ -286,10 +284,9 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
       for (int rb = 0; rb < RB; ++rb) sacc[s][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NKS; ++c) {
-      // chunk c of this tile has landed once at most the loads issued after
-      // it are outstanding
-      if constexpr (NBUF == 2) wait_vmcnt_le_rt<63>(NKS + NKS - 1 - c);
-      else wait_vmcnt_le_rt<63>(NKS - 1 - c);
+      // chunk c of this tile has landed once at most its NKS-1-c younger
+      // siblings are outstanding (no load of the next tile is issued yet)
+      wait_vmcnt_le_rt<63>(NKS - 1 - c);
       const bf16x8 ef = *reinterpret_cast<const bf16x8 *>(eb + c * CHUNK_B + eoff(lane & 15, 8 * (lane >> 4)));
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
@@ -302,13 +299,21 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
       const f32x4 s = sacc[0][rb] + sacc[1][rb];
       *reinterpret_cast<f32x4 *>(&red[wave * MT * VT + roff(r, 4 * (lane >> 4))]) = s;
     }
+    if constexpr (NBUF == 2) {
+      if (more) {
+        wait_lgkm0();
+#pragma unroll
+        for (int c = 0; c < kB1; ++c) dma_chunk(tile + 1, c);
+      }
+    }
     __syncthreads();
 
     // ---- epilogue: one lane per (row er, id v0 + j)
     if (epi) {
-      float acc = 0.f;
+      float pr[NW];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) acc += red[w * MT * VT + roff(er, j)];
+      for (int w = 0; w < NW; ++w) pr[w] = red[w * MT * VT + roff(er, j)];
+      const float acc = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
       const float s = acc * inv_tau;
       const int v = v0 + j;
       if (a.p0 && rvalid) a.p0[static_cast<int64_t>(grow) * a.V + v] = s;
@@ -326,15 +331,23 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
         if (mx > m_ref + kRescaleSlack) {
-          sc = exp2f(m_ref - mx);   // 0 on the first tile
+          sc = __builtin_amdgcn_exp2f(m_ref - mx);   // 0 on the first tile
           m_ref = mx;
         }
         if (__builtin_amdgcn_ballot_w64(sc != 1.f) && lane == 0) last_resc = tile;
       }
-      const float p = exp2f(t2 - m_ref);
+      // hardware exp2: results below 2^-126 flush to zero, far below what a
+      // bf16 probability times an embedding row can contribute to z
+      const float p = __builtin_amdgcn_exp2f(t2 - m_ref);
       l_lane = l_lane * sc + p;
       *reinterpret_cast<uint16_t *>(Pb + poff<MT>(er, j)) = f32_to_bf16(p);
       if (j == 0) scl[er] = sc;
+    }
+    if constexpr (NBUF == 2) {
+      if (more) {
+#pragma unroll
+        for (int c = kB1; c < kB2; ++c) dma_chunk(tile + 1, c);
+      }
     }
     __syncthreads();
 
@@ -376,6 +389,8 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
             wait_lgkm0();
             dma_chunk(tile + 1, c);
           }
+        } else {
+          if (c >= kB2 && more) dma_chunk(tile + 1, c);
         }
       }
     } else {
@@ -393,6 +408,8 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
             wait_lgkm0();
             dma_chunk(tile + 1, n >> 1);
           }
+        } else {
+          if ((n & 1) && (n >> 1) >= kB2 && more) dma_chunk(tile + 1, n >> 1);
         }
       }
     }
