@@ -6,27 +6,51 @@
 // here as one joint, unmasked softmax over [prefix ; canvas] keys, scale
 // 1/sqrt(hd), query head h using kv head h / G.
 //
-// One block = 64 query rows of one kv head (the G query heads of a kv head
-// share its K/V, so their rows are stacked: row qr = (h - g G) C + i), 4 waves
-// of 16 rows. K/V tiles of 64 keys are staged in LDS: K row-major, V
-// transposed ([e][key]) so both MFMA operands read contiguous 8-byte runs.
-// Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16:
-// a lane then owns one query row and 4 consecutive keys per 16-key block,
-// which is exactly the A-operand layout of O += P V (keys as K dimension), so
-// P never leaves registers. The online softmax runs in log2 units.
+// One block = 256 query rows of one kv head (the G query heads of a kv head
+// share its K/V, so their rows are stacked: row qr = (h - g G) C + i), 8 waves
+// of 32 rows. Keys stream through LDS in tiles of 64 by direct global->LDS
+// loads, NS tiles in flight. Per tile and wave:
+//   S^T[key, query] = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as the
+//   A operand, the wave's Q rows held in registers as B). A lane then holds 16
+//   keys of one query, and the k-slot order of the O += P V contraction is
+//   chosen to match, so P goes from the score accumulators to the A operand
+//   without leaving registers; V is read transposed from LDS
+//   (ds_read_b64_tr_b16) as the B operand.
+// The online softmax runs in log2 units with a reference maximum that moves
+// only when a score exceeds it by more than 2^8 (one ballot per tile; the
+// rare move rescales O), so P <= 2^8 and no per-tile O rescale is needed.
 // Long key ranges are split across blocks; partial (m, l, O) are merged by a
 // second kernel.
+//
+// LDS layout of a K or V tile: piece-major, [16-byte piece p of the row]
+// [64 keys], key k of piece p stored at slot k ^ 4 (p & 3). One direct load
+// fills one piece for all 64 keys; the XOR keeps the score-operand reads (32
+// keys of one piece) and the transposed 4-key reads of V free of bank
+// conflicts for 32 and 64 banks, for any head dimension.
 #include "dg_device.hpp"
 #include "dg_kernels.hpp"
 
 namespace dg {
 namespace {
 
-constexpr int BQ = 64;     // query rows per block
-constexpr int BKV = 64;    // keys per tile
-constexpr int VT_PITCH = BKV + 8;
+constexpr int NWA = 8;              // waves per block
+constexpr int BQ = NWA * 32;        // query rows per block
+constexpr int BK = 64;              // keys per tile
+constexpr int kLdsBudget = 160 * 1024;
+constexpr float kSlack = 8.0f;      // log2 units
 
-constexpr int round_up32(int x) { return (x + 31) / 32 * 32; }
+template <int HD>
+struct Geo {
+  static constexpr int HDP = (HD + 31) / 32 * 32;   // padded head dim
+  static constexpr int NPC = HDP / 8;               // 16-byte pieces per row incl. padding
+  static constexpr int NPR = HD / 8;                // pieces carrying data
+  static constexpr int KS = HDP / 16;               // k-steps of the score contraction
+  static constexpr int NB = HDP / 32;               // 32-column blocks of O
+  static constexpr int TILE_B = NPC * BK * 16;      // bytes per tensor and stage
+  static constexpr int NS = (2 * TILE_B * 4 <= kLdsBudget) ? 4 : 3;   // stages
+  static constexpr int NDMA = 2 * NPR;              // direct loads per tile (K and V)
+  static_assert(2 * TILE_B * NS <= kLdsBudget, "LDS");
+};
 
 struct AttnArgs {
   const uint16_t *q, *k, *v, *Kp, *Vp;
@@ -37,380 +61,258 @@ struct AttnArgs {
   float scale_log2;   // log2(e) / sqrt(hd)
 };
 
-template <int HD>
-__global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
-  constexpr int HDP = round_up32(HD);
-  constexpr int KPITCH = HDP + 8;
-  constexpr int NKS = HDP / 32;     // k-steps of the score contraction
-  constexpr int NB = HD / 16;       // 16-wide column blocks of O
-  constexpr int CH = HD / 8;        // 16-byte chunks per key row
+__device__ __forceinline__ int kslot(int key, int piece) { return key ^ (4 * (piece & 3)); }
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BKV * KPITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[HD * VT_PITCH];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qb = blockIdx.x, g = blockIdx.y;
-  const int b = blockIdx.z / a.splits, split = blockIdx.z - b * a.splits;
-  const int GC = a.G * a.C;
-  const int Lk = a.P + a.C;
-  const int64_t hd_stride = HD;
-  const int qcols = a.Hq * HD;
-
-  // zero the score padding columns once (never written by tile loads)
-  if (HDP > HD) {
-    for (int c = tid; c < BKV * (HDP - HD); c += 256) {
-      const int key = c / (HDP - HD), col = HD + c % (HDP - HD);
-      Ks[key * KPITCH + col] = 0;
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le_rt(int n) {
+  if constexpr (N > 0) {
+    if (n >= N) {
+      wait_vmcnt<N>();
+      return;
     }
-  }
-
-  // this lane's query row in the S^T layout
-  const int qr = qb * BQ + wave * 16 + (lane & 15);
-  const bool qvalid = qr < GC;
-  const int qh = qvalid ? g * a.G + qr / a.C : 0;
-  const int qi = qvalid ? qr % a.C : 0;
-  bf16x8 qreg[NKS];
-  {
-    const uint16_t *qrow = a.q + (static_cast<int64_t>(b) * a.C + qi) * qcols + qh * hd_stride;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int e = ks * 32 + (lane >> 4) * 8;
-      if (qvalid && e < HD)
-        qreg[ks] = *reinterpret_cast<const bf16x8 *>(qrow + e);
-      else
-        qreg[ks] = bf16x8{};
-    }
-  }
-
-  f32x4 oacc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  const int64_t kvp_base = (static_cast<int64_t>(b) * a.Hkv + g) * a.P * hd_stride;
-  const int64_t kvc_base = (static_cast<int64_t>(b) * a.Hkv + g) * a.C * hd_stride;
-  const int tile0 = split * a.tiles_per_split;
-  const int total_tiles = (Lk + BKV - 1) / BKV;
-  int tile_end = tile0 + a.tiles_per_split;
-  if (tile_end > total_tiles) tile_end = total_tiles;
-
-  for (int tile = tile0; tile < tile_end; ++tile) {
-    const int kv0 = tile * BKV;
-    __syncthreads();   // previous tile fully consumed
-    for (int c = tid; c < BKV * CH; c += 256) {
-      const int key = c / CH, col = (c - key * CH) * 8;
-      const int j = kv0 + key;
-      uint4 kk = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (j < a.P) {
-        kk = *reinterpret_cast<const uint4 *>(a.Kp + kvp_base + j * hd_stride + col);
-        vv = *reinterpret_cast<const uint4 *>(a.Vp + kvp_base + j * hd_stride + col);
-      } else if (j < Lk) {
-        kk = *reinterpret_cast<const uint4 *>(a.k + kvc_base + (j - a.P) * hd_stride + col);
-        vv = *reinterpret_cast<const uint4 *>(a.v + kvc_base + (j - a.P) * hd_stride + col);
-      }
-      *reinterpret_cast<uint4 *>(&Ks[key * KPITCH + col]) = kk;
-      const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        Vt[(col + 2 * t) * VT_PITCH + key] = static_cast<uint16_t>(w4[t] & 0xFFFFu);
-        Vt[(col + 2 * t + 1) * VT_PITCH + key] = static_cast<uint16_t>(w4[t] >> 16);
-      }
-    }
-    __syncthreads();
-
-    // S^T for 4 blocks of 16 keys: lane owns query row (lane & 15) and keys
-    // 16 kb + 4 (lane >> 4) + [0, 4)
-    f32x4 s[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t *krow = &Ks[(kb * 16 + (lane & 15)) * KPITCH + (lane >> 4) * 8];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(krow + ks * 32);
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qreg[ks], s[kb], 0, 0, 0);
-      }
-    }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = kv0 + kb * 16 + (lane >> 4) * 4 + r;
-        const float val = (j < Lk) ? s[kb][r] * a.scale_log2 : -INFINITY;
-        s[kb][r] = val;
-        tmax = fmaxf(tmax, val);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);   // 0 on the first tile
-    float psum = 0.f;
-    bf16x8 pa[2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = exp2f(s[kb][r] - m_new);
-        psum += p[r];
-      }
-      // keys 16 kb + 4 (lane>>4) + r map to k-slots 8 (lane>>4) + 4 (kb & 1) + r
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pa[kb >> 1][(kb & 1) * 4 + r] = static_cast<__bf16>(p[r]);
-    }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-
-    // O rows in the C layout are 4 (lane >> 4) + i; their alpha lives in lane row
-    float arow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) arow[i] = __shfl(alpha, (lane >> 4) * 4 + i, 64);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[nb][i] *= arow[i];
-      const uint16_t *vrow = &Vt[(nb * 16 + (lane & 15)) * VT_PITCH + (lane >> 4) * 4];
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + ks2 * 32);
-        const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + ks2 * 32 + 16);
-        const uint4 w = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        const bf16x8 vb = *reinterpret_cast<const bf16x8 *>(&w);
-        oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[ks2], vb, oacc[nb], 0, 0, 0);
-      }
-    }
-  }
-
-  // epilogue: lane holds O[row 4 (lane>>4) + i][col 16 nb + (lane & 15)]
-  float lrow[4], mrow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lrow[i] = __shfl(l_run, (lane >> 4) * 4 + i, 64);
-    mrow[i] = __shfl(m_run, (lane >> 4) * 4 + i, 64);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = qb * BQ + wave * 16 + (lane >> 4) * 4 + i;
-    if (row >= GC) continue;
-    const int h = g * a.G + row / a.C, ii = row % a.C;
-    const int64_t r = static_cast<int64_t>(b) * a.C + ii;
-    if (a.splits == 1) {
-      const float inv = 1.f / lrow[i];
-      uint16_t *orow = a.o + r * qcols + h * hd_stride;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) orow[nb * 16 + (lane & 15)] = f32_to_bf16(oacc[nb][i] * inv);
-    } else {
-      const int64_t R = static_cast<int64_t>(a.B) * a.C;
-      float *prow = a.opart + ((split * R + r) * a.Hq + h) * hd_stride;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) prow[nb * 16 + (lane & 15)] = oacc[nb][i];
-      if ((lane & 15) == 0) a.ml[(split * R + r) * a.Hq + h] = make_float2(mrow[i], lrow[i]);
-    }
+    wait_vmcnt_le_rt<N - 1>(n);
+  } else {
+    wait_vmcnt<0>();
   }
 }
 
-// ---------------------------------------------------------------------------
-// Second version: K and V tiles stay row-major in LDS (rows padded so that the
-// 16-row operand reads of K and the 4-row transposed reads of V hit distinct
-// banks), V reaches the O contraction through ds_read_b64_tr_b16, and the
-// next tile is fetched into registers while the current one is computed.
-template <int HD> struct AttnPitch;
-template <> struct AttnPitch<64> { static constexpr int K = 72, V = 80; };
-template <> struct AttnPitch<128> { static constexpr int K = 136, V = 144; };
-template <> struct AttnPitch<176> { static constexpr int K = 200, V = 208; };
+// Direct global -> LDS load of 16 bytes per lane from a per-lane 64-bit
+// address; lane i's bytes land at lds + 16 i (lds wave-uniform). Inline asm
+// keeps the compiler from adding waits before unrelated LDS reads; reads of
+// the loaded data follow an explicit vmcnt wait and a barrier. The
+// instruction has no register result: its address registers are read at
+// issue.
+__device__ __forceinline__ void lds_dma16_va(const void *src, void *lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds)));
+  const uint64_t addr = reinterpret_cast<uint64_t>(src);
+  uint32_t saved;
+  // M0 is reserved by the compiler: keep its value across the block
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(addr)
+      : "memory");
+}
 
 template <int HD>
-__global__ void __launch_bounds__(256) attn_fwd_v2_kernel(AttnArgs a) {
-  constexpr int HDP = round_up32(HD);
-  constexpr int KP = AttnPitch<HD>::K, VP = AttnPitch<HD>::V;
-  static_assert(KP >= HDP, "score operand reads stay inside a K row");
-  constexpr int NKS = HDP / 32;
-  constexpr int NB = HD / 16;
-  constexpr int CH = HD / 8;                       // 16-byte chunks per key row
-  constexpr int PER = (BKV * CH + 255) / 256;      // chunks per thread per tile and tensor
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BKV * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BKV * VP];
+__global__ void __launch_bounds__(512) attn_fwd_kernel(AttnArgs a) {
+  using G_ = Geo<HD>;
+  constexpr int HDP = G_::HDP, NPC = G_::NPC, NPR = G_::NPR, KS = G_::KS, NB = G_::NB;
+  constexpr int TILE_B = G_::TILE_B, NS = G_::NS, NDMA = G_::NDMA;
+  constexpr int MAXL = (NDMA + NWA - 1) / NWA;   // loads per wave and tile, at most
+  __shared__ __attribute__((aligned(16))) uint8_t stage_mem[NS * 2 * TILE_B];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qb = blockIdx.x, g = blockIdx.y;
   const int b = blockIdx.z / a.splits, split = blockIdx.z - b * a.splits;
   const int GC = a.G * a.C;
   const int Lk = a.P + a.C;
-  const int64_t hd_stride = HD;
   const int qcols = a.Hq * HD;
 
-  if (KP > HD)   // pad columns of K are read (against zero q) and must be finite
-    for (int c = tid; c < BKV * (KP - HD); c += 256)
-      Ks[(c / (KP - HD)) * KP + HD + c % (KP - HD)] = 0;
+  // padding pieces (head dims that are not a multiple of 32) are read by the
+  // contractions against zero Q / into discarded O columns and must be finite
+  if constexpr (NPC > NPR) {
+    for (int c = tid; c < NS * 2 * (NPC - NPR) * BK; c += 512) {
+      const int key = c % BK, rest = c / BK;
+      const int p = NPR + rest % (NPC - NPR), tens = rest / (NPC - NPR);
+      *reinterpret_cast<uint4 *>(stage_mem + tens * TILE_B + p * BK * 16 + key * 16) = make_uint4(0, 0, 0, 0);
+    }
+  }
 
-  const int qr = qb * BQ + wave * 16 + (lane & 15);
+  // this wave's 32 query rows; lane holds query lane & 31 and the k-slots
+  // 8 (lane >> 5) + [0, 8) of every 16-wide step
+  const int hl = lane >> 5;
+  const int qr = qb * BQ + wave * 32 + (lane & 31);
   const bool qvalid = qr < GC;
   const int qh = qvalid ? g * a.G + qr / a.C : 0;
   const int qi = qvalid ? qr % a.C : 0;
-  bf16x8 qreg[NKS];
+  bf16x8 qreg[KS];
   {
-    const uint16_t *qrow = a.q + (static_cast<int64_t>(b) * a.C + qi) * qcols + qh * hd_stride;
+    const uint16_t *qrow = a.q + (static_cast<int64_t>(b) * a.C + qi) * qcols + qh * HD;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int e = ks * 32 + (lane >> 4) * 8;
+    for (int ks = 0; ks < KS; ++ks) {
+      const int e = ks * 16 + hl * 8;
       qreg[ks] = (qvalid && e < HD) ? *reinterpret_cast<const bf16x8 *>(qrow + e) : bf16x8{};
     }
   }
 
-  f32x4 oacc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  const int64_t kvp_base = (static_cast<int64_t>(b) * a.Hkv + g) * a.P * hd_stride;
-  const int64_t kvc_base = (static_cast<int64_t>(b) * a.Hkv + g) * a.C * hd_stride;
+  const int64_t kvp_base = (static_cast<int64_t>(b) * a.Hkv + g) * a.P * HD;
+  const int64_t kvc_base = (static_cast<int64_t>(b) * a.Hkv + g) * a.C * HD;
   const int tile0 = split * a.tiles_per_split;
-  const int total_tiles = (Lk + BKV - 1) / BKV;
+  const int total_tiles = (Lk + BK - 1) / BK;
   int tile_end = tile0 + a.tiles_per_split;
   if (tile_end > total_tiles) tile_end = total_tiles;
 
-  uint4 kreg[PER], vreg[PER];
-  auto fetch = [&](int tile) {
-    const int kv0 = tile * BKV;
+  // direct loads of one tile: load u in [0, NDMA) fills piece u % NPR of K
+  // (u < NPR) or of V; wave w issues loads w, w + 8, ...
+  const int my_loads = (NDMA - wave + NWA - 1) / NWA;
+  auto issue_tile = [&](int tile) {
+    uint8_t *st = stage_mem + (tile % NS) * 2 * TILE_B;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int c = tid + 256 * u;
-      uint4 kk = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (c < BKV * CH) {
-        const int key = c / CH, col = (c - key * CH) * 8;
-        const int j = kv0 + key;
-        if (j < a.P) {
-          kk = *reinterpret_cast<const uint4 *>(a.Kp + kvp_base + j * hd_stride + col);
-          vv = *reinterpret_cast<const uint4 *>(a.Vp + kvp_base + j * hd_stride + col);
-        } else if (j < Lk) {
-          kk = *reinterpret_cast<const uint4 *>(a.k + kvc_base + (j - a.P) * hd_stride + col);
-          vv = *reinterpret_cast<const uint4 *>(a.v + kvc_base + (j - a.P) * hd_stride + col);
-        }
-      }
-      kreg[u] = kk;
-      vreg[u] = vv;
-    }
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int c = tid + 256 * u;
-      if (c < BKV * CH) {
-        const int key = c / CH, col = (c - key * CH) * 8;
-        *reinterpret_cast<uint4 *>(&Ks[key * KP + col]) = kreg[u];
-        *reinterpret_cast<uint4 *>(&Vs[key * VP + col]) = vreg[u];
+    for (int n = 0; n < MAXL; ++n) {
+      const int u = wave + n * NWA;
+      if (u < NDMA) {
+        const int tensor = u >= NPR, p = tensor ? u - NPR : u;
+        // lane i fills slot i of the piece: key i ^ 4 (p & 3) of the tile,
+        // clamped to the last key (keys past the end are masked in the scores)
+        int j = tile * BK + kslot(lane, p);
+        if (j > Lk - 1) j = Lk - 1;
+        const uint16_t *src = (j < a.P)
+                                  ? (tensor ? a.Vp : a.Kp) + kvp_base + static_cast<int64_t>(j) * HD + p * 8
+                                  : (tensor ? a.v : a.k) + kvc_base + static_cast<int64_t>(j - a.P) * HD + p * 8;
+        lds_dma16_va(src, st + tensor * TILE_B + p * BK * 16);
       }
     }
   };
+  for (int t = tile0; t < tile_end && t < tile0 + NS - 1; ++t) issue_tile(t);
 
-  if (tile0 < tile_end) {
-    fetch(tile0);
-    __syncthreads();            // pad zeroing done before rows land
-    stash();
-    if (tile0 + 1 < tile_end) fetch(tile0 + 1);
-    __syncthreads();
-  }
-  // transposed-read source address of this lane (see the LM head for the
-  // lane mapping of ds_read_b64_tr_b16)
-  const int tr_row = 4 * (lane >> 4) + ((lane & 15) >> 2);
-  const int tr_col = 4 * (lane & 3);
+  f32x16 oacc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x16{};
+  float m_ref = -INFINITY, l_lane = 0.f;
+  const int g4 = lane >> 4;
+  const int tr_key = 4 * (g4 >> 1) + ((lane & 15) >> 2);
+  const int tr_col = 16 * (g4 & 1) + 4 * (lane & 3);
 
   for (int tile = tile0; tile < tile_end; ++tile) {
-    const int kv0 = tile * BKV;
-    f32x4 s[4];
+    // this wave's loads of `tile` have landed once at most those of the
+    // tiles issued after it are outstanding; the barrier makes every wave's
+    // loads visible and frees the stage read during the previous tile
+    int after = tile_end - 1 - tile;
+    if (after > NS - 2) after = NS - 2;
+    wait_vmcnt_le_rt<63>(after * my_loads);
+    __syncthreads();
+    if (tile + NS - 1 < tile_end) issue_tile(tile + NS - 1);
+    const uint8_t *Ks = stage_mem + (tile % NS) * 2 * TILE_B;
+    const uint8_t *Vs = Ks + TILE_B;
+
+    // ---- S^T for 64 keys (two 32-key blocks); SCH accumulator chains per
+    // block shorten the MFMA dependency chains where registers allow
+    constexpr int SCH = (HD > 128) ? 1 : 2;
+    f32x16 sacc[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t *krow = &Ks[(kb * 16 + (lane & 15)) * KP + (lane >> 4) * 8];
+    for (int mb = 0; mb < 2; ++mb) {
+      sacc[mb][0] = f32x16{};
+      sacc[mb][1] = f32x16{};
+    }
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(krow + ks * 32);
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qreg[ks], s[kb], 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) {
+      const int p = 2 * ks + hl;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8 *>(Ks + p * BK * 16 + kslot(mb * 32 + (lane & 31), p) * 16);
+        sacc[mb][ks % SCH] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], sacc[mb][ks % SCH], 0, 0, 0);
       }
     }
+    // element e = 4 jj + i of block mb: key 32 mb + 8 jj + 4 hl + i of this tile
+    float sv[2][16];
     float tmax = -INFINITY;
+    const int kv0 = tile * BK;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = kv0 + kb * 16 + (lane >> 4) * 4 + r;
-        const float val = (j < Lk) ? s[kb][r] * a.scale_log2 : -INFINITY;
-        s[kb][r] = val;
-        tmax = fmaxf(tmax, val);
+      for (int e = 0; e < 16; ++e) {
+        const int key = kv0 + mb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
+        const float sum = (SCH == 2) ? sacc[mb][0][e] + sacc[mb][1][e] : sacc[mb][0][e];
+        const float v = (key < Lk) ? sum * a.scale_log2 : -INFINITY;
+        sv[mb][e] = v;
+        tmax = fmaxf(tmax, v);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));   // both halves of the query
+    if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kSlack)) {
+      float alpha = 1.f;
+      if (tmax > m_ref + kSlack) {
+        alpha = __builtin_amdgcn_exp2f(m_ref - tmax);   // 0 on the first tile
+        m_ref = tmax;
+      }
+      l_lane *= alpha;
+      // O rows of this lane are queries 8 jj + 4 hl + i; their factors live
+      // in lanes 0..31 (one per query)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float f = __shfl(alpha, 8 * (e >> 2) + 4 * hl + (e & 3), 64);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) oacc[nb][e] *= f;
+      }
+    }
+    // P in the k-slot order of the PV contraction: for the 16-key step kk
+    // (block mb = kk / 2, half kk2 = kk % 2) the A operand is elements
+    // 8 kk2 .. 8 kk2 + 7 of block mb, i.e. keys 16 kk + 4 hl + [0, 4) and
+    // 16 kk + 8 + 4 hl + [0, 4)
+    bf16x8 pa[4];
     float psum = 0.f;
-    bf16x8 pa[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(s[kb][r] - m_new);
+      for (int e = 0; e < 16; ++e) {
+        const float p = __builtin_amdgcn_exp2f(sv[mb][e] - m_ref);
         psum += p;
-        pa[kb >> 1][(kb & 1) * 4 + r] = static_cast<__bf16>(p);
+        pa[2 * mb + (e >> 3)][e & 7] = static_cast<__bf16>(p);
       }
-    }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    float arow[4];
+    l_lane += psum;
+
+    // ---- O += P V; the B operand of column block nb and step kk is read
+    // transposed: source lane S supplies key 16 kk + 4 (g / 2) + j (+ 8 for
+    // the second read) at columns 32 nb + 16 (g % 2) + 4 q, with g = S / 16,
+    // j = (S % 16) / 4, q = S % 4
 #pragma unroll
-    for (int i = 0; i < 4; ++i) arow[i] = __shfl(alpha, (lane >> 4) * 4 + i, 64);
+    for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[nb][i] *= arow[i];
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const int col = nb * 16 + tr_col;
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = 32 * nb + tr_col;
+        const int p = col >> 3;
+        const uint8_t *pb = Vs + p * BK * 16 + ((col & 7) >> 2) * 8;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)&Vs[(ks2 * 32 + tr_row) * VP + col]);
+            (__attribute__((address_space(3))) s16x4 *)(pb + kslot(16 * kk + tr_key, p) * 16));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)&Vs[(ks2 * 32 + 16 + tr_row) * VP + col]);
-        const uint16_t w8[8] = {(uint16_t)lo[0], (uint16_t)lo[1], (uint16_t)lo[2], (uint16_t)lo[3],
-                                (uint16_t)hi[0], (uint16_t)hi[1], (uint16_t)hi[2], (uint16_t)hi[3]};
-        const bf16x8 vb = *reinterpret_cast<const bf16x8 *>(w8);
-        oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[ks2], vb, oacc[nb], 0, 0, 0);
+            (__attribute__((address_space(3))) s16x4 *)(pb + kslot(16 * kk + 8 + tr_key, p) * 16));
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], vb, oacc[nb], 0, 0, 0);
       }
-    }
-    if (tile + 1 < tile_end) {
-      __syncthreads();          // everyone is done with this tile's K and V
-      stash();                  // the next tile, fetched during this one
-      if (tile + 2 < tile_end) fetch(tile + 2);
-      __syncthreads();
     }
   }
 
-  float lrow[4], mrow[4];
+  // ---- normalise, or write the split partials
+  const float l_q = l_lane + __shfl_xor(l_lane, 32, 64);   // lanes q and q + 32 hold query q
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lrow[i] = __shfl(l_run, (lane >> 4) * 4 + i, 64);
-    mrow[i] = __shfl(m_run, (lane >> 4) * 4 + i, 64);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = qb * BQ + wave * 16 + (lane >> 4) * 4 + i;
+  for (int e = 0; e < 16; ++e) {
+    const int rq = 8 * (e >> 2) + 4 * hl + (e & 3);       // query of this O element
+    const float lr = __shfl(l_q, rq, 64);
+    const float mr = __shfl(m_ref, rq, 64);
+    const int row = qb * BQ + wave * 32 + rq;
     if (row >= GC) continue;
     const int h = g * a.G + row / a.C, ii = row % a.C;
     const int64_t r = static_cast<int64_t>(b) * a.C + ii;
     if (a.splits == 1) {
-      const float inv = 1.f / lrow[i];
-      uint16_t *orow = a.o + r * qcols + h * hd_stride;
+      const float inv = 1.f / lr;
+      uint16_t *orow = a.o + r * qcols + h * HD;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) orow[nb * 16 + (lane & 15)] = f32_to_bf16(oacc[nb][i] * inv);
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = 32 * nb + (lane & 31);
+        if (HDP == HD || col < HD) orow[col] = f32_to_bf16(oacc[nb][e] * inv);
+      }
     } else {
       const int64_t R = static_cast<int64_t>(a.B) * a.C;
-      float *prow = a.opart + ((split * R + r) * a.Hq + h) * hd_stride;
+      float *prow = a.opart + ((split * R + r) * a.Hq + h) * HD;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) prow[nb * 16 + (lane & 15)] = oacc[nb][i];
-      if ((lane & 15) == 0) a.ml[(split * R + r) * a.Hq + h] = make_float2(mrow[i], lrow[i]);
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = 32 * nb + (lane & 31);
+        if (HDP == HD || col < HD) prow[col] = oacc[nb][e];
+      }
+      if ((lane & 31) == 0) a.ml[(split * R + r) * a.Hq + h] = make_float2(mr, lr);
     }
   }
 }
@@ -438,9 +340,9 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float *__restri
 }
 
 void plan(const Shape &s, int &splits, int &tps) {
-  const int tiles = (s.P + s.C + BKV - 1) / BKV;
+  const int tiles = (s.P + s.C + BK - 1) / BK;
   const int base = ((s.G() * s.C + BQ - 1) / BQ) * s.Hkv * s.B;
-  int want = (512 + base - 1) / base;
+  int want = (256 + base - 1) / base;   // one block per CU fills the chip
   if (want < 1) want = 1;
   if (want > tiles) want = tiles;
   tps = (tiles + want - 1) / want;
@@ -477,9 +379,9 @@ hipError_t launch_attention_bf16(const uint16_t *q, const uint16_t *k, const uin
   a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(s.hd)));
   dim3 grid((s.G() * s.C + BQ - 1) / BQ, s.Hkv, s.B * a.splits);
   switch (s.hd) {
-    case 64: hipLaunchKernelGGL(attn_fwd_v2_kernel<64>, grid, dim3(256), 0, st, a); break;
-    case 128: hipLaunchKernelGGL(attn_fwd_v2_kernel<128>, grid, dim3(256), 0, st, a); break;
-    case 176: hipLaunchKernelGGL(attn_fwd_v2_kernel<176>, grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(512), 0, st, a); break;
+    case 128: hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(512), 0, st, a); break;
+    case 176: hipLaunchKernelGGL(attn_fwd_kernel<176>, grid, dim3(512), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
