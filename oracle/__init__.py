@@ -13,7 +13,9 @@ It follows the DiffusionGemma Technical Report as summarised on hyper.ai
   * decoder equation: L_t = Decoder(x_t, z_t, H) in R^{C x V};
   * three-line update: p0 = Softmax(L_t / tau_t), z = FFW(p0 E),
     x_{t-dt} ~ Step(x_t, p0);
-  * sampler paragraph: tau anneals linearly from 0.8 to 0.4.
+  * sampler paragraph: tau anneals linearly from 0.8 to 0.4; the
+    entropy-bounded acceptance, uniform re-noising and adaptive stopping of
+    the recommended sampler (entropy.py).
 
 Readings taken where the pages stop short (each documented where used):
 Step is the Euler step of the uniform-path CTMC,
@@ -39,10 +41,13 @@ from .decoder import embed, qkv_proj, attention, out_proj, lm_head
 from .sampling import bernoulli_uniforms, gumbel_noise, step_select
 from .corrupt import corrupt
 from .step import denoise_step, generate_canvas
+from .entropy import (row_entropy, accept_mask, renoise_tokens, entropy_step,
+                      generate_canvas_entropy)
 
 __all__ = [
     "philox4x32_10", "uniform01", "philox_scalar", "schedule_terms", "step_lambda",
     "temperature", "inv_temperature", "round_act", "round_bf16", "round_f32", "embed",
     "qkv_proj", "attention", "out_proj", "lm_head", "bernoulli_uniforms", "gumbel_noise",
-    "step_select", "corrupt", "denoise_step", "generate_canvas",
+    "step_select", "corrupt", "denoise_step", "generate_canvas", "row_entropy", "accept_mask",
+    "renoise_tokens", "entropy_step", "generate_canvas_entropy",
 ]

@@ -17,6 +17,7 @@ Counter map (ours; the pages are silent):
     stream 1, Step Bernoulli: (0, i, b, 1), word 0
     stream 2, corruption:    (i >> 1, 0, b, 2), words 2*(i&1) (keep draw)
                              and 2*(i&1)+1 (replacement token)
+    stream 3, entropy-step re-noise: (0, i, b, 3), word 0
 with i the canvas position and b the canvas index.
 """
 import numpy as np
