@@ -41,7 +41,8 @@ class dg_profile(ctypes.Structure):
 
 
 EXPORTS = ["dg_create", "dg_destroy", "dg_workspace_bytes", "dg_corrupt", "dg_corrupt_batch",
-           "dg_denoise_step", "dg_denoise_step_taps", "dg_generate_canvas", "dg_profile_enable",
+           "dg_denoise_step", "dg_denoise_step_taps", "dg_generate_canvas",
+           "dg_denoise_step_entropy", "dg_generate_canvas_entropy", "dg_profile_enable",
            "dg_profile_read", "dg_status_string", "dg_last_error"]
 
 _lib = None
@@ -72,6 +73,9 @@ def load_library():
     lib.dg_denoise_step_taps.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(f32), f32, u64, vp, vp,
                                          ctypes.POINTER(dg_taps), vp]
     lib.dg_generate_canvas.argtypes = [vp, vp, vp, i32, u64, vp, vp, vp]
+    lib.dg_denoise_step_entropy.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(f32), u64, f32, f32,
+                                            vp, vp, vp, vp, vp, vp, vp]
+    lib.dg_generate_canvas_entropy.argtypes = [vp, vp, vp, i32, u64, f32, f32, vp, vp, vp, vp]
     lib.dg_profile_enable.argtypes = [vp, ctypes.c_int]
     lib.dg_profile_read.argtypes = [vp, ctypes.POINTER(dg_profile)]
     lib.dg_status_string.argtypes = [ctypes.c_int]
@@ -196,6 +200,25 @@ def dg_denoise_step_taps(model, x_t, z_t, K_pre, V_pre, t, dt, seed, x_out, z_ou
 def dg_generate_canvas(model, K_pre, V_pre, steps, seed, x_out, z_out=None, stream=None):
     _check(load_library().dg_generate_canvas(model.handle, _ptr(K_pre), _ptr(V_pre), int(steps),
                                              int(seed), _ptr(x_out), _ptr(z_out), _stream(stream)))
+
+
+def dg_denoise_step_entropy(model, x_t, z_t, K_pre, V_pre, t, seed, eps_accept, eps_stop,
+                            det_prev, x_out, z_out, det_out, stop_out, entropy_out=None,
+                            stream=None):
+    _check(load_library().dg_denoise_step_entropy(model.handle, _ptr(x_t), _ptr(z_t), _ptr(K_pre),
+                                                  _ptr(V_pre), _floats(t), int(seed),
+                                                  float(eps_accept), float(eps_stop),
+                                                  _ptr(det_prev), _ptr(x_out), _ptr(z_out),
+                                                  _ptr(det_out), _ptr(entropy_out),
+                                                  _ptr(stop_out), _stream(stream)))
+
+
+def dg_generate_canvas_entropy(model, K_pre, V_pre, max_steps, seed, eps_accept, eps_stop, x_out,
+                               steps_out, z_out=None, stream=None):
+    _check(load_library().dg_generate_canvas_entropy(model.handle, _ptr(K_pre), _ptr(V_pre),
+                                                     int(max_steps), int(seed), float(eps_accept),
+                                                     float(eps_stop), _ptr(x_out), _ptr(z_out),
+                                                     _ptr(steps_out), _stream(stream)))
 
 
 def dg_profile_enable(model, stages=None):

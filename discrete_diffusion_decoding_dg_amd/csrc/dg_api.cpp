@@ -38,6 +38,7 @@ dg_status hip_fail(hipError_t e, const char *what) {
   } while (0)
 
 constexpr int kMaxSteps = 4096;
+constexpr int kPoll = 4;   // adaptive generation tests for early termination every kPoll steps
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -55,7 +56,7 @@ dg::Shape shape_of(const dg_config &c) {
 
 // Workspace layout, in carve order.
 struct Layout {
-  size_t h0, q, k, v, o, h1, attn, lm, prm, kappa, genx, genz, total;
+  size_t h0, q, k, v, o, h1, attn, lm, prm, kappa, genx, genz, ent, gendet, flags, total;
 };
 
 Layout layout_of(const dg_config &c) {
@@ -80,7 +81,11 @@ Layout layout_of(const dg_config &c) {
   L.kappa = align_up(static_cast<size_t>(s.B) * sizeof(float));
   L.genx = align_up(2 * R * sizeof(int32_t));
   L.genz = align_up(2 * R * s.d * es);
-  L.total = L.h0 + L.q + L.k + L.v + L.o + L.h1 + L.attn + L.lm + L.prm + L.kappa + L.genx + L.genz;
+  L.ent = align_up(3 * R * sizeof(int32_t));        // entropy step: H, draw, argmax per row
+  L.gendet = align_up(2 * R * sizeof(int32_t));     // generation: argmax predictions, ping-pong
+  L.flags = align_up(2 * static_cast<size_t>(s.B) * sizeof(int32_t));   // stopped, stop
+  L.total = L.h0 + L.q + L.k + L.v + L.o + L.h1 + L.attn + L.lm + L.prm + L.kappa + L.genx + L.genz +
+            L.ent + L.gendet + L.flags;
   return L;
 }
 
@@ -160,6 +165,10 @@ struct dg_model {
   float *kappa;
   int32_t *genx;
   char *genz;
+  dg::EntropyRows ent;      // per-row entropy-step results
+  int32_t *gendet;          // [2][R] argmax predictions during generation
+  int32_t *stopped, *stopbuf;   // [B] each
+  int32_t *host_stopped = nullptr;   // pinned [B], allocated on first use
   // profiling: event pairs recorded around stage launches while enabled
   int prof_mask = 0;
   struct Mark {
@@ -191,10 +200,14 @@ struct StageTimer {
 
 // prm: device step constants of every canvas; when n_inline > 0 the embedding
 // launch first stores them there from the host array `inline_prm`.
+// With `ent` the step is the entropy-bounded one: every row draws and the
+// merge writes per-row entropy, draw and argmax to *ent (the select kernel
+// then produces the tokens); rows of canvases marked in `frozen` keep z_t.
 dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void *Kp,
                    const void *Vp, dg::StepParams *prm, const dg::StepParams *inline_prm,
                    int n_inline, uint64_t seed, int32_t *x_out, void *z_out,
-                   const dg_taps *taps, float *lse, float *p0, hipStream_t st) {
+                   const dg_taps *taps, float *lse, float *p0, hipStream_t st,
+                   const dg::EntropyRows *ent = nullptr, const int32_t *frozen = nullptr) {
   const dg::Shape &s = m->s;
   const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
   void *h0 = taps && taps->h0 ? taps->h0 : m->h0;
@@ -237,13 +250,13 @@ dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void 
     {
       StageTimer tm(m, 4, st);
       DG_HIP(dg::launch_lmhead_bf16(static_cast<const u16 *>(h1), static_cast<const u16 *>(m->w.E),
-                                  x_t, prm, s, seed, m->lm, p0, st),
+                                  x_t, prm, s, seed, m->lm, p0, ent != nullptr, st),
            "LM head launch");
     }
     {
       StageTimer tm(m, 5, st);
       DG_HIP(dg::launch_combine(true, m->lm, dg::lmhead_splits(s), x_t, prm, s, seed, x_out, z_out,
-                              lse, best, st),
+                              lse, best, ent, frozen, z_t, st),
            "combine launch");
     }
   } else {
@@ -271,12 +284,13 @@ dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void 
     {
       StageTimer tm(m, 4, st);
       DG_HIP(dg::launch_lmhead_f32(static_cast<const float *>(h1), static_cast<const float *>(m->w.E),
-                                 prm, s, seed, m->lm, p0, st),
+                                 prm, s, seed, m->lm, p0, ent != nullptr, st),
            "LM head launch");
     }
     {
       StageTimer tm(m, 5, st);
-      DG_HIP(dg::launch_combine(false, m->lm, 1, x_t, prm, s, seed, x_out, z_out, lse, best, st),
+      DG_HIP(dg::launch_combine(false, m->lm, 1, x_t, prm, s, seed, x_out, z_out, lse, best, ent,
+                              frozen, z_t, st),
            "combine launch");
     }
   }
@@ -372,6 +386,17 @@ dg_status dg_create(const dg_config *cfg, const dg_weights *w, dg_model **out) {
   m->kappa = reinterpret_cast<float *>(p); p += L.kappa;
   m->genx = reinterpret_cast<int32_t *>(p); p += L.genx;
   m->genz = p; p += L.genz;
+  {
+    const size_t R = static_cast<size_t>(m->s.R());
+    m->ent.H = reinterpret_cast<float *>(p);
+    m->ent.y = reinterpret_cast<int32_t *>(p) + R;
+    m->ent.det = reinterpret_cast<int32_t *>(p) + 2 * R;
+    p += L.ent;
+  }
+  m->gendet = reinterpret_cast<int32_t *>(p); p += L.gendet;
+  m->stopped = reinterpret_cast<int32_t *>(p);
+  m->stopbuf = m->stopped + m->s.B;
+  p += L.flags;
   *out = m;
   return DG_OK;
 }
@@ -413,6 +438,7 @@ dg_status dg_destroy(dg_model *m) {
     (void)hipEventDestroy(mk.b);
   }
   hipError_t f = hipFree(m->ws);
+  if (m->host_stopped) (void)hipHostFree(m->host_stopped);
   delete m;
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
   if (f != hipSuccess) return hip_fail(f, "hipFree");
@@ -548,6 +574,125 @@ dg_status dg_generate_canvas(dg_model *m, const void *K_pre, const void *V_pre, 
                                nullptr, st))
       return e;
   }
+  return DG_OK;
+}
+
+
+dg_status dg_denoise_step_entropy(dg_model *m, const int32_t *x_t, const void *z_t,
+                                  const void *K_pre, const void *V_pre, const float *t,
+                                  uint64_t seed, float eps_accept, float eps_stop,
+                                  const int32_t *det_prev, int32_t *x_out, void *z_out,
+                                  int32_t *det_out, float *entropy_out, int32_t *stop_out,
+                                  void *stream) {
+  g_err.clear();
+  if (dg_status s = check_model(m)) return s;
+  const dg::Shape &s = m->s;
+  if (!x_t || !z_t || !x_out || !z_out || !det_out || !stop_out)
+    return fail(DG_ERR_INVALID_ARG, "x_t, z_t, x_out, z_out, det_out and stop_out must be non-NULL");
+  if (s.P > 0 && (!K_pre || !V_pre)) return fail(DG_ERR_INVALID_ARG, "K_pre and V_pre must be non-NULL when P > 0");
+  if (s.C > dg::kSelectMaxC)
+    return fail(DG_ERR_UNSUPPORTED, "the entropy-bounded step supports C <= %d (got %d)", dg::kSelectMaxC, s.C);
+  if (!std::isfinite(eps_accept) || !std::isfinite(eps_stop))
+    return fail(DG_ERR_INVALID_ARG, "eps_accept and eps_stop must be finite");
+  if (dg_status e = check_times(t, s.B, 1.0f)) return e;
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  const size_t es = bf16 ? 2 : 4;
+  const size_t nx = static_cast<size_t>(s.R()) * sizeof(int32_t);
+  const size_t nz = static_cast<size_t>(s.R()) * s.d * es;
+  if (overlap(x_out, nx, x_t, nx)) return fail(DG_ERR_INVALID_ARG, "x_out overlaps x_t");
+  if (overlap(z_out, nz, z_t, nz)) return fail(DG_ERR_INVALID_ARG, "z_out overlaps z_t");
+  if (det_prev && overlap(det_out, nx, det_prev, nx)) return fail(DG_ERR_INVALID_ARG, "det_out overlaps det_prev");
+  if (bf16 && (!aligned16(z_t) || !aligned16(z_out) || (K_pre && !aligned16(K_pre)) ||
+               (V_pre && !aligned16(V_pre))))
+    return fail(DG_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // only the temperature of the step constants is used here
+  std::vector<dg::StepParams> prm(s.B);
+  for (int b = 0; b < s.B; ++b) prm[b] = step_params(t[b], 1.0, m->cfg.schedule);
+  const int n_inline = s.B <= dg::kInlineParams ? s.B : 0;
+  if (!n_inline)
+    if (dg_status e = upload_params(m, m->prm, prm, st)) return e;
+  if (dg_status e = run_step(m, x_t, z_t, K_pre, V_pre, m->prm, prm.data(), n_inline, seed, x_out,
+                             z_out, nullptr, nullptr, nullptr, st, &m->ent, nullptr))
+    return e;
+  DG_HIP(dg::launch_entropy_select(m->ent, x_t, det_prev, s.B, s.C, s.V, eps_accept, eps_stop, seed,
+                                   0, x_out, det_out, entropy_out, stop_out, nullptr, nullptr, st),
+         "select launch");
+  return DG_OK;
+}
+
+dg_status dg_generate_canvas_entropy(dg_model *m, const void *K_pre, const void *V_pre,
+                                     int32_t max_steps, uint64_t seed, float eps_accept,
+                                     float eps_stop, int32_t *x_out, void *z_out,
+                                     int32_t *steps_out, void *stream) {
+  g_err.clear();
+  if (dg_status s = check_model(m)) return s;
+  const dg::Shape &s = m->s;
+  if (!x_out || !steps_out) return fail(DG_ERR_INVALID_ARG, "x_out and steps_out must be non-NULL");
+  if (s.P > 0 && (!K_pre || !V_pre)) return fail(DG_ERR_INVALID_ARG, "K_pre and V_pre must be non-NULL when P > 0");
+  if (max_steps < 1 || max_steps > kMaxSteps)
+    return fail(DG_ERR_INVALID_ARG, "max_steps must be in [1, %d] (got %d)", kMaxSteps, max_steps);
+  if (s.C > dg::kSelectMaxC)
+    return fail(DG_ERR_UNSUPPORTED, "the entropy-bounded step supports C <= %d (got %d)", dg::kSelectMaxC, s.C);
+  if (!std::isfinite(eps_accept) || !std::isfinite(eps_stop))
+    return fail(DG_ERR_INVALID_ARG, "eps_accept and eps_stop must be finite");
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  if (bf16 && ((K_pre && !aligned16(K_pre)) || (V_pre && !aligned16(V_pre)) ||
+               (z_out && !aligned16(z_out))))
+    return fail(DG_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+  if (!m->host_stopped) {
+    void *h = nullptr;
+    DG_HIP(hipHostMalloc(&h, static_cast<size_t>(s.B) * sizeof(int32_t), hipHostMallocDefault),
+           "hipHostMalloc");
+    m->host_stopped = static_cast<int32_t *>(h);
+  }
+  const size_t es = bf16 ? 2 : 4;
+  const size_t R = static_cast<size_t>(s.R());
+  const size_t nz = R * s.d * es;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  // temperatures of the whole grid t_k = 1 - k / max_steps, uploaded once
+  std::vector<dg::StepParams> prm(static_cast<size_t>(max_steps) * s.B);
+  for (int k = 0; k < max_steps; ++k) {
+    const float tk = static_cast<float>(1.0 - static_cast<double>(k) / max_steps);
+    const dg::StepParams p = step_params(tk, 1.0, m->cfg.schedule);
+    for (int b = 0; b < s.B; ++b) prm[static_cast<size_t>(k) * s.B + b] = p;
+  }
+  if (dg_status e = upload_params(m, m->prm, prm, st)) return e;
+
+  int32_t *xb[2] = {m->genx, m->genx + R};
+  char *zb[2] = {m->genz, m->genz + nz};
+  int32_t *db[2] = {m->gendet, m->gendet + R};
+  DG_HIP(dg::launch_fill_zero(m->kappa, align_up(s.B * sizeof(float)), st), "fill");
+  DG_HIP(dg::launch_fill_zero(xb[0], R * sizeof(int32_t), st), "fill");
+  DG_HIP(dg::launch_corrupt(xb[0], m->kappa, s.B, s.C, s.V, seed, xb[0], st), "corrupt launch");
+  DG_HIP(dg::launch_fill_zero(zb[0], nz, st), "fill");
+  DG_HIP(dg::launch_fill_zero(m->stopped, static_cast<size_t>(s.B) * sizeof(int32_t), st), "fill");
+  DG_HIP(dg::launch_fill_i32(steps_out, static_cast<size_t>(s.B), max_steps, st), "fill");
+  int cur = 0;
+  for (int k = 0; k < max_steps; ++k) {
+    const int nxt = cur ^ 1;
+    if (dg_status e = run_step(m, xb[cur], zb[cur], K_pre, V_pre, m->prm + static_cast<size_t>(k) * s.B,
+                               nullptr, 0, seed + static_cast<uint64_t>(k), xb[nxt], zb[nxt], nullptr,
+                               nullptr, nullptr, st, &m->ent, m->stopped))
+      return e;
+    DG_HIP(dg::launch_entropy_select(m->ent, xb[cur], k ? db[cur] : nullptr, s.B, s.C, s.V,
+                                     eps_accept, eps_stop, seed + static_cast<uint64_t>(k), k,
+                                     xb[nxt], db[nxt], nullptr, m->stopbuf, m->stopped, steps_out, st),
+           "select launch");
+    cur = nxt;
+    // every kPoll steps, end early once every canvas has stopped
+    if ((k + 1) % kPoll == 0 && k + 1 < max_steps) {
+      DG_HIP(hipMemcpyAsync(m->host_stopped, m->stopped, static_cast<size_t>(s.B) * sizeof(int32_t),
+                            hipMemcpyDeviceToHost, st), "stop flags copy");
+      DG_HIP(hipStreamSynchronize(st), "stop flags sync");
+      bool all = true;
+      for (int b = 0; b < s.B && all; ++b) all = m->host_stopped[b] != 0;
+      if (all) break;
+    }
+  }
+  DG_HIP(hipMemcpyAsync(x_out, xb[cur], R * sizeof(int32_t), hipMemcpyDeviceToDevice, st), "x copy");
+  if (z_out) DG_HIP(hipMemcpyAsync(z_out, zb[cur], nz, hipMemcpyDeviceToDevice, st), "z copy");
   return DG_OK;
 }
 

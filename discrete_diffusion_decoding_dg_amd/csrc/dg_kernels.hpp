@@ -25,9 +25,21 @@ struct Shape {
 // Partial results of the split-V LM head, one record per (split, row).
 struct RowPartial {
   float m;        // reference max of the scaled logits in log2 units
-  float l;        // sum of exp2(s*log2e - m) over the split
+  float l;        // sum of exp2(t - m) over the split, t = s*log2e
   float best;     // best Gumbel-perturbed logit (natural units), -inf if none
   int32_t arg;    // its vocab id (lowest on ties), -1 if none
+  // entropy statistics (entropy-bounded step only)
+  float s1;       // sum of exp2(t - m) (t - m) over the split
+  float dbest;    // largest t (log2 units), -inf if none
+  int32_t darg;   // its vocab id (lowest on ties), -1 if none
+  int32_t pad;
+};
+
+// Per-row results of the entropy-bounded step's merge, for the select kernel.
+struct EntropyRows {
+  float *H;        // [R] entropy of p0 in nats
+  int32_t *y;      // [R] Gumbel-max draw from p0
+  int32_t *det;    // [R] argmax of the scaled logits
 };
 
 // ---- k_elementwise.hip ----
@@ -46,6 +58,7 @@ hipError_t launch_p0_from_logits(float *p0, const float *lse, int R, int V, hipS
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
 // Copy small host arrays to device memory through kernel arguments.
 hipError_t launch_set_params(StepParams *dst, const StepParams *src, int n, hipStream_t st);
+hipError_t launch_fill_i32(int32_t *p, size_t n, int32_t v, hipStream_t st);
 hipError_t launch_set_floats(float *dst, const float *src, int n, hipStream_t st);
 
 // ---- k_gemm.hip (bf16 MFMA) ----
@@ -70,9 +83,11 @@ int lmhead_splits(const Shape &s);
 size_t lmhead_workspace_bytes(const Shape &s);
 // Fused LM head over V splits; writes RowPartial [splits, R] and z partials
 // [splits, R, d] fp32 into `work`, and raw scaled logits into p0 when non-null.
+// With `entropy` every row draws (no Bernoulli) and the entropy statistics
+// of RowPartial are filled in.
 hipError_t launch_lmhead_bf16(const uint16_t *h1, const uint16_t *E, const int32_t *x_t,
                               const StepParams *prm, const Shape &s, uint64_t seed, void *work,
-                              float *p0, hipStream_t st);
+                              float *p0, bool entropy, hipStream_t st);
 
 // ---- k_fp32.hip (fp32 VALU path, any shape) ----
 hipError_t launch_qkv_f32(const float *h0, const float *Wq, const float *Wk, const float *Wv,
@@ -83,14 +98,31 @@ hipError_t launch_oproj_f32(const float *o, const float *Wo, const float *h0, co
                             float *h1, hipStream_t st);
 size_t lmhead_f32_workspace_bytes(const Shape &s);
 hipError_t launch_lmhead_f32(const float *h1, const float *E, const StepParams *prm,
-                             const Shape &s, uint64_t seed, void *work, float *p0,
+                             const Shape &s, uint64_t seed, void *work, float *p0, bool entropy,
                              hipStream_t st);
 
 // ---- k_combine.hip ----
 // Merge the split partials of the LM head, draw the Step and finish z:
 // x_out, z_out (act), lse, best (each optional except x_out/z_out).
+// With `ent` (entropy-bounded step) the per-row entropy, draw and argmax go
+// to ent instead of a Step select into x_out; rows of canvases marked in
+// `frozen` (nullable) copy z_t to z_out instead.
 hipError_t launch_combine(bool bf16, const void *work, int splits, const int32_t *x_t,
                           const StepParams *prm, const Shape &s, uint64_t seed, int32_t *x_out,
-                          void *z_out, float *lse, int32_t *best, hipStream_t st);
+                          void *z_out, float *lse, int32_t *best, const EntropyRows *ent,
+                          const int32_t *frozen, const void *z_t, hipStream_t st);
+
+// ---- k_select.hip ----
+constexpr int kSelectMaxC = 1024;   // canvas positions the select kernel sorts in LDS
+// Entropy-bounded acceptance, uniform re-noise and the stop test, one block
+// per canvas. `det_prev` (nullable) holds the previous step's argmax
+// predictions; with `stopped` (nullable) a canvas already marked there keeps
+// x_t and det_prev, and a canvas that stops now is marked and records
+// step + 1 in steps_out (nullable).
+hipError_t launch_entropy_select(const EntropyRows &ent, const int32_t *x_t,
+                                 const int32_t *det_prev, int B, int C, int V, float eps_accept,
+                                 float eps_stop, uint64_t seed, int step, int32_t *x_out,
+                                 int32_t *det_out, float *entropy_out, int32_t *stop_out,
+                                 int32_t *stopped, int32_t *steps_out, hipStream_t st);
 
 }  // namespace dg

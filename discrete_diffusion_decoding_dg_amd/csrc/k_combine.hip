@@ -7,6 +7,12 @@
 // Gumbel argmax over the whole vocabulary (ties: lowest id, i.e. the lowest
 // split wins an exact tie between splits).
 //
+// Entropy-bounded step: every row keeps its Gumbel draw, and the merge also
+// yields the row's entropy H = ln 2 (log2 L - S1 / L), with L the merged sum
+// of exp2(t - M) and S1 the merged sum of exp2(t - M) (t - M) (t the scaled
+// logits in log2 units, M the merged reference), and the plain argmax; the
+// select kernel then decides which draws to keep.
+//
 // Grid: (row, strip of 1024 columns). The first wave of each block merges
 // the row's split statistics (one split per lane, wave-wide max / sum /
 // argmax); then every thread streams 4 consecutive columns of all splits.
@@ -27,10 +33,19 @@ __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restri
                                                       int32_t *__restrict__ x_out,
                                                       T *__restrict__ z_out,
                                                       float *__restrict__ lse,
-                                                      int32_t *__restrict__ best) {
+                                                      int32_t *__restrict__ best, EntropyRows ent,
+                                                      const int32_t *__restrict__ frozen,
+                                                      const T *__restrict__ z_t) {
   __shared__ float wsh[kMaxSplits];
   __shared__ float inv_l;
   const int r = blockIdx.x;
+  if (frozen && frozen[r / C]) {
+    // a stopped canvas keeps its self-conditioning signal
+    const int c0 = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
+    for (int c = c0; c < c0 + 4 && c < d; ++c)
+      z_out[static_cast<int64_t>(r) * d + c] = z_t[static_cast<int64_t>(r) * d + c];
+    return;
+  }
   if (threadIdx.x < 64) {
     const int s = threadIdx.x;
     RowPartial p;
@@ -38,6 +53,10 @@ __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restri
     p.l = 0.f;
     p.best = -INFINITY;
     p.arg = -1;
+    p.s1 = 0.f;
+    p.dbest = -INFINITY;
+    p.darg = -1;
+    p.pad = 0;
     if (s < splits) p = part[static_cast<int64_t>(s) * R + r];
     const float M = wave_max(p.m);
     const float w = (s < splits) ? exp2f(p.m - M) : 0.f;
@@ -53,7 +72,29 @@ __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restri
       if (ov > bv || (ov == bv && os < bs)) { bv = ov; bs = os; }
     }
     const int bi = __shfl(p.arg, bs < kMaxSplits ? bs : 0, 64);
-    if (s == 0) {
+    if (ent.H) {
+      // entropy and plain argmax of the row (exact ties: the lower split)
+      const float S1 = wave_sum((s < splits && p.l > 0.f) ? w * (p.s1 + (p.m - M) * p.l) : 0.f);
+      float dv = (s < splits && p.darg >= 0) ? p.dbest : -INFINITY;
+      int ds = (s < splits && p.darg >= 0) ? s : kMaxSplits;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(dv, o, 64);
+        const int os = __shfl_xor(ds, o, 64);
+        if (ov > dv || (ov == dv && os < ds)) { dv = ov; ds = os; }
+      }
+      const int di = __shfl(p.darg, ds < kMaxSplits ? ds : 0, 64);
+      if (s == 0) {
+        inv_l = 1.f / L;
+        if (blockIdx.y == 0) {
+          ent.H[r] = 0.6931471805599453f * (log2f(L) - S1 / L);
+          ent.y[r] = bs < kMaxSplits ? bi : -1;
+          ent.det[r] = ds < kMaxSplits ? di : -1;
+          if (lse) lse[r] = (M + log2f(L)) * 0.6931471805599453f;
+          if (best) best[r] = bs < kMaxSplits ? bi : -1;
+        }
+      }
+    } else if (s == 0) {
       inv_l = 1.f / L;
       if (blockIdx.y == 0) {
         const int b = r / C, i = r - b * C;
@@ -103,7 +144,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restri
 
 hipError_t launch_combine(bool bf16, const void *work, int splits, const int32_t *x_t,
                           const StepParams *prm, const Shape &s, uint64_t seed, int32_t *x_out,
-                          void *z_out, float *lse, int32_t *best, hipStream_t st) {
+                          void *z_out, float *lse, int32_t *best, const EntropyRows *ent,
+                          const int32_t *frozen, const void *z_t, hipStream_t st) {
   const int R = s.R();
   if (R == 0) return hipSuccess;
   if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
@@ -112,13 +154,16 @@ hipError_t launch_combine(bool bf16, const void *work, int splits, const int32_t
                                                        static_cast<size_t>(splits) * R * sizeof(RowPartial));
   const uint32_t k0 = static_cast<uint32_t>(seed), k1 = static_cast<uint32_t>(seed >> 32);
   const dim3 grid(R, (s.d + 1023) / 1024);
+  const EntropyRows er = ent ? *ent : EntropyRows{nullptr, nullptr, nullptr};
+  if (frozen && !z_t) return hipErrorInvalidValue;
   if (bf16)
     hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, st, part, zpart, splits,
                        x_t, prm, R, s.C, s.d, k0, k1, x_out, static_cast<uint16_t *>(z_out), lse,
-                       best);
+                       best, er, frozen, static_cast<const uint16_t *>(z_t));
   else
     hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, st, part, zpart, splits, x_t,
-                       prm, R, s.C, s.d, k0, k1, x_out, static_cast<float *>(z_out), lse, best);
+                       prm, R, s.C, s.d, k0, k1, x_out, static_cast<float *>(z_out), lse, best,
+                       er, frozen, static_cast<const float *>(z_t));
   return hipGetLastError();
 }
 

@@ -171,6 +171,20 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(uint32_t *__restrict__ p
     p[i] = 0u;
 }
 
+__global__ void __launch_bounds__(256) fill_i32_kernel(int32_t *__restrict__ p, size_t n, int32_t v) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t *p, size_t n, int32_t v, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st) {
   // bytes is a multiple of 4 for every caller (fp32 or bf16 pairs of even width)
   const size_t n = bytes / 4;

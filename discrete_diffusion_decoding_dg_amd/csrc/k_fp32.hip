@@ -135,17 +135,19 @@ __global__ void __launch_bounds__(256) lmhead_f32_kernel(const float *__restrict
                                                          int R, int C, int d, int V, uint32_t k0,
                                                          uint32_t k1, RowPartial *__restrict__ part,
                                                          float *__restrict__ zpart,
-                                                         float *__restrict__ p0) {
+                                                         float *__restrict__ p0, int ent) {
   __shared__ float pch[256];
   __shared__ float redv[256];
   __shared__ int redi[256];
+  __shared__ float reds[256];
   __shared__ float hrow[4096];
   const int r = blockIdx.x, t = threadIdx.x;
   const int b = r / C, i = r - b * C;
   const float inv_tau = prm[b].inv_tau;
   const u32x4 bw = philox4x32_10(0u, static_cast<uint32_t>(i), static_cast<uint32_t>(b),
                                  kStreamBernoulli, k0, k1);
-  const bool rs = u01(bw.x) < prm[b].lam;
+  // the entropy-bounded step draws for every row
+  const bool rs = ent ? true : u01(bw.x) < prm[b].lam;
   for (int c = t; c < d; c += 256) hrow[c] = h1[static_cast<int64_t>(r) * d + c];
   __syncthreads();
   float z[kZPerThread];
@@ -153,6 +155,8 @@ __global__ void __launch_bounds__(256) lmhead_f32_kernel(const float *__restrict
   for (int j = 0; j < kZPerThread; ++j) z[j] = 0.f;
   float m_run = -INFINITY, l_run = 0.f, bv = -INFINITY;
   int bi = -1;
+  float s1_run = 0.f, dv = -INFINITY;   // entropy statistics: sum p (t - m) and the plain argmax
+  int di = -1;
   for (int v0 = 0; v0 < V; v0 += 256) {
     const int v = v0 + t;
     float s2 = -INFINITY;
@@ -170,6 +174,7 @@ __global__ void __launch_bounds__(256) lmhead_f32_kernel(const float *__restrict
         if (pv > bv) { bv = pv; bi = v; }
       }
       s2 = s * kLog2e;
+      if (s2 > dv) { dv = s2; di = v; }
     }
     redv[t] = s2;
     __syncthreads();
@@ -183,11 +188,17 @@ __global__ void __launch_bounds__(256) lmhead_f32_kernel(const float *__restrict
     const float p = (v < V) ? exp2f(s2 - m_new) : 0.f;
     pch[t] = p;
     redv[t] = p;
+    reds[t] = (v < V) ? p * (s2 - m_new) : 0.f;
     __syncthreads();
     for (int s = 128; s > 0; s >>= 1) {
-      if (t < s) redv[t] += redv[t + s];
+      if (t < s) {
+        redv[t] += redv[t + s];
+        reds[t] += reds[t + s];
+      }
       __syncthreads();
     }
+    // re-reference the running sums to m_new, then add this chunk
+    s1_run = (l_run > 0.f) ? sc * (s1_run + (m_run - m_new) * l_run) + reds[0] : reds[0];
     l_run = l_run * sc + redv[0];
     m_run = m_new;
     const int nv = (V - v0 < 256) ? V - v0 : 256;
@@ -217,12 +228,34 @@ __global__ void __launch_bounds__(256) lmhead_f32_kernel(const float *__restrict
     }
     __syncthreads();
   }
+  const float gbest = redv[0];
+  const int garg = redi[0];
+  __syncthreads();
+  // block argmax of the plain scaled logits, lowest id on ties
+  redv[t] = dv;
+  redi[t] = di;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (t < s) {
+      const float ov = redv[t + s];
+      const int oi = redi[t + s];
+      if (ov > redv[t] || (ov == redv[t] && oi >= 0 && (redi[t] < 0 || oi < redi[t]))) {
+        redv[t] = ov;
+        redi[t] = oi;
+      }
+    }
+    __syncthreads();
+  }
   if (t == 0) {
     RowPartial p;
     p.m = m_run;
     p.l = l_run;
-    p.best = redv[0];
-    p.arg = redi[0];
+    p.best = gbest;
+    p.arg = garg;
+    p.s1 = s1_run;
+    p.dbest = redv[0];
+    p.darg = redi[0];
+    p.pad = 0;
     part[r] = p;
   }
 #pragma unroll
@@ -271,14 +304,14 @@ size_t lmhead_f32_workspace_bytes(const Shape &s) {
 }
 
 hipError_t launch_lmhead_f32(const float *h1, const float *E, const StepParams *prm,
-                             const Shape &s, uint64_t seed, void *work, float *p0,
+                             const Shape &s, uint64_t seed, void *work, float *p0, bool entropy,
                              hipStream_t st) {
   if (s.R() == 0) return hipSuccess;
   RowPartial *part = static_cast<RowPartial *>(work);
   float *zpart = reinterpret_cast<float *>(static_cast<char *>(work) + static_cast<size_t>(s.R()) * sizeof(RowPartial));
   hipLaunchKernelGGL(lmhead_f32_kernel, dim3(s.R()), dim3(256), 0, st, h1, E, prm, s.R(), s.C,
                      s.d, s.V, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32),
-                     part, zpart, p0);
+                     part, zpart, p0, entropy ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -139,11 +139,11 @@ __global__ void __launch_bounds__(256) gemm_tn_bf16_kernel(const uint16_t *__res
 // ---------------------------------------------------------------------------
 // Deep-pipelined variant for K % 64 == 0: NS stages of 64-wide A and B slabs
 // (8 KB each) are requested NS-1 slabs ahead with direct global->LDS loads,
-// so about 80 KB per block is in flight -- what it takes to cover the memory
-// latency at the rate the matrix cores consume slabs. Rows of a slab are 128
+// so about 128 KB per block is in flight: with few rows the tile is small and
+// the memory latency, not the matrix cores, sets the pace. Rows of a slab are 128
 // bytes; the 16-byte piece p of row r sits at p ^ ((r ^ (r >> 3)) & 7), which
 // keeps the 32-row operand reads free of bank conflicts (32 or 64 banks).
-constexpr int NS = 6;
+constexpr int NS = 9;
 constexpr int SLAB = 64 * 64;            // elements per operand slab
 
 __device__ __forceinline__ int gswz(int r, int p) { return p ^ ((r ^ (r >> 3)) & 7); }
@@ -171,20 +171,21 @@ __device__ __forceinline__ void dma16(const void *base, uint32_t voff, const uin
 
 template <int N>
 __device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
   asm volatile("" ::: "memory");
 }
+// wait until at most n of this wave's vector-memory operations are outstanding
+template <int N = 63>
 __device__ __forceinline__ void vm_wait_le(int n) {
-  switch (n) {
-    case 0: vm_wait<0>(); break;
-    case 4: vm_wait<4>(); break;
-    case 8: vm_wait<8>(); break;
-    case 2: vm_wait<2>(); break;
-    case 6: vm_wait<6>(); break;
-    case 10: vm_wait<10>(); break;
-    case 12: vm_wait<12>(); break;
-    case 16: vm_wait<16>(); break;
-    default: vm_wait<0>(); break;
+  if constexpr (N > 0) {
+    if (n >= N) {
+      vm_wait<N>();
+      return;
+    }
+    vm_wait_le<N - 1>(n);
+  } else {
+    vm_wait<0>();
   }
 }
 
@@ -224,7 +225,7 @@ __global__ void __launch_bounds__(512) gemm_tn_bf16_dma_kernel(const uint16_t *_
   };
   for (int it = 0; it < NS - 1 && it < nk; ++it) issue(it);
 
-  f32x16 acc = {};
+  f32x16 acc = {}, acc1 = {};
   const int ar = wm * 32 + (lane & 31), br = wn * 32 + (lane & 31);
   for (int it = 0; it < nk; ++it) {
     int younger = nk - 1 - it;                      // slabs issued after this one
@@ -234,14 +235,17 @@ __global__ void __launch_bounds__(512) gemm_tn_bf16_dma_kernel(const uint16_t *_
     if (it + NS - 1 < nk) issue(it + NS - 1);       // refill the slab computed last iteration
     const uint16_t *as = As + (it % NS) * SLAB;
     const uint16_t *bs = Bs + (it % NS) * SLAB;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int p = 2 * (2 * wk + kk) + (lane >> 5);
-      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(as + ar * 64 + gswz(ar, p) * 8);
-      const bf16x8 b = *reinterpret_cast<const bf16x8 *>(bs + br * 64 + gswz(br, p) * 8);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    {
+      const int p0 = 2 * (2 * wk) + (lane >> 5), p1 = p0 + 2;
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(as + ar * 64 + gswz(ar, p0) * 8);
+      const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(bs + br * 64 + gswz(br, p0) * 8);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(as + ar * 64 + gswz(ar, p1) * 8);
+      const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(bs + br * 64 + gswz(br, p1) * 8);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc, 0, 0, 0);     // two independent chains
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc1, 0, 0, 0);
     }
   }
+  acc += acc1;
 
   // k-halves meet in LDS (the stage buffers are free once everyone is here)
   __syncthreads();
@@ -267,7 +271,145 @@ __global__ void __launch_bounds__(512) gemm_tn_bf16_dma_kernel(const uint16_t *_
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile variant for many rows (batched canvases): 256 x 256 output tile
+// per block, 8 waves as 2 x 4, each wave 128 x 64 (eight independent 32x32
+// accumulators), K in 32-wide slabs (16 KB per operand) streamed by direct
+// global->LDS loads through NS_BIG stages. A slab row is 64 bytes; its
+// 16-byte piece p sits at p ^ bswz(r), which keeps the 32-row operand reads
+// free of bank conflicts (32 or 64 banks).
+namespace big {
+constexpr int BMB = 256, BNB = 256, BKB = 32, NS_BIG = 4;
+constexpr int kGroup = 4;        // row tiles per group of the XCD-aware order
+constexpr int SLB = BMB * BKB;   // elements per operand slab
+
+__device__ __forceinline__ int bswz(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); }
+
+// 16 bytes per lane from a per-lane 64-bit address into lds + 16 * lane.
+__device__ __forceinline__ void dma16_va(const void *src, const uint16_t *lds) {
+  const uint32_t m0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint16_t *)lds))));
+  const uint64_t addr = reinterpret_cast<uint64_t>(src);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(addr)
+      : "memory");
+}
+
+template <class Epi>
+__global__ void __launch_bounds__(512) gemm_big_kernel(const uint16_t *__restrict__ A, int M, int N,
+                                                       int K, Epi epi) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[NS_BIG * SLB];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[NS_BIG * SLB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  // XCD-aware tile order: the hardware deals blocks to the 8 XCDs in turn,
+  // so block b runs on XCD b % 8. Give XCD x a contiguous run of tiles in a
+  // grouped order (kGroup row tiles, column tiles slowest) so that the
+  // blocks resident on one XCD share A and B tiles through its L2.
+  const int gm = gridDim.y, gn = gridDim.x, T = gm * gn;
+  int tm = blockIdx.y, tn = blockIdx.x;
+  if ((T & 7) == 0 && gm % kGroup == 0) {
+    const int b = blockIdx.y * gn + blockIdx.x;
+    const int idx = (b & 7) * (T >> 3) + (b >> 3);
+    const int grp = idx / (kGroup * gn), within = idx - grp * (kGroup * gn);
+    tm = grp * kGroup + within % kGroup;
+    tn = within / kGroup;
+  }
+  const int m0 = tm * BMB, n0 = tn * BNB;
+  const int nk = K / BKB;
+
+  // loads: a slab is 16 instructions per operand, each 16 rows x 64 bytes;
+  // wave w issues instructions 2 w and 2 w + 1 of both. Lane i fills row
+  // 16 u + i / 4, physical piece i % 4 (logical piece (i % 4) ^ bswz(row)).
+  // Rows past M (N) re-read the last valid row; their results are dropped.
+  const uint16_t *bbase = epi.brow(n0, K);   // the tile's rows come from one matrix
+  const uint16_t *asrc[2], *bsrc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 16 * (2 * wave + j) + (lane >> 2);
+    const int lp = (lane & 3) ^ bswz(r);
+    const int am = (m0 + r < M) ? m0 + r : M - 1;
+    const int bn = (n0 + r < N) ? r : N - 1 - n0;
+    asrc[j] = A + static_cast<int64_t>(am) * K + lp * 8;
+    bsrc[j] = bbase + static_cast<int64_t>(bn) * K + lp * 8;
+  }
+  auto issue = [&](int it) {
+    const int buf = it % NS_BIG, k0 = it * BKB;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      dma16_va(asrc[j] + k0, As + buf * SLB + (2 * wave + j) * 16 * BKB);
+      dma16_va(bsrc[j] + k0, Bs + buf * SLB + (2 * wave + j) * 16 * BKB);
+    }
+  };
+  for (int it = 0; it < NS_BIG - 1 && it < nk; ++it) issue(it);
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    acc[mi][0] = f32x16{};
+    acc[mi][1] = f32x16{};
+  }
+  for (int it = 0; it < nk; ++it) {
+    int younger = nk - 1 - it;                      // slabs issued after this one
+    if (younger > NS_BIG - 2) younger = NS_BIG - 2;
+    vm_wait_le(4 * younger);
+    __syncthreads();                                // every wave's part of slab `it` landed
+    if (it + NS_BIG - 1 < nk) issue(it + NS_BIG - 1);   // refill the slab computed last iteration
+    const uint16_t *as = As + (it % NS_BIG) * SLB;
+    const uint16_t *bs = Bs + (it % NS_BIG) * SLB;
+#pragma unroll
+    for (int ks = 0; ks < BKB / 16; ++ks) {
+      const int p = 2 * ks + (lane >> 5);
+      bf16x8 a[4], b[2];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const int r = wm * 128 + mi * 32 + (lane & 31);
+        a[mi] = *reinterpret_cast<const bf16x8 *>(as + r * BKB + ((p ^ bswz(r)) << 3));
+      }
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int r = wn * 64 + ni * 32 + (lane & 31);
+        b[ni] = *reinterpret_cast<const bf16x8 *>(bs + r * BKB + ((p ^ bswz(r)) << 3));
+      }
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    }
+  }
+
+  // C layout of the 32x32 MFMA: lane holds column lane % 32 and rows
+  // 8 j + 4 (lane / 32) + i in register 4 j + i
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) {
+    const int n = n0 + wn * 64 + ni * 32 + (lane & 31);
+    if (n >= N) continue;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + wm * 128 + mi * 32 + 8 * j + 4 * (lane >> 5) + i;
+          if (m < M) epi.store(m, n, acc[mi][ni][4 * j + i]);
+        }
+  }
+}
+}  // namespace big
+
 }  // namespace
+
+// below this many rows the 256-row tiles would leave most of the chip idle
+constexpr int kBigRows = 2048;
 
 hipError_t launch_qkv_bf16(const uint16_t *h0, const uint16_t *Wq, const uint16_t *Wk,
                            const uint16_t *Wv, const Shape &s, uint16_t *q, uint16_t *k,
@@ -276,7 +418,11 @@ hipError_t launch_qkv_bf16(const uint16_t *h0, const uint16_t *Wq, const uint16_
   const int M = s.R(), N = s.Hq * s.hd + 2 * s.Hkv * s.hd;
   if (M == 0) return hipSuccess;
   dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
-  if (s.d % 64 == 0 && (s.Hq * s.hd) % 64 == 0 && (s.Hkv * s.hd) % 64 == 0)
+  if (M >= kBigRows && s.d % big::BKB == 0 && (s.Hq * s.hd) % big::BNB == 0 &&
+      (s.Hkv * s.hd) % big::BNB == 0)
+    hipLaunchKernelGGL(big::gemm_big_kernel<QkvEpi>, dim3(N / big::BNB, (M + big::BMB - 1) / big::BMB),
+                       dim3(512), 0, st, h0, M, N, s.d, epi);
+  else if (s.d % 64 == 0 && (s.Hq * s.hd) % 64 == 0 && (s.Hkv * s.hd) % 64 == 0)
     hipLaunchKernelGGL(gemm_tn_bf16_dma_kernel<QkvEpi>, grid, dim3(512), 0, st, h0, M, N, s.d, epi);
   else
     hipLaunchKernelGGL(gemm_tn_bf16_kernel<QkvEpi>, grid, dim3(256), 0, st, h0, M, N, s.d, epi);
@@ -289,7 +435,10 @@ hipError_t launch_oproj_bf16(const uint16_t *o, const uint16_t *Wo, const uint16
   const int M = s.R(), N = s.d, K = s.Hq * s.hd;
   if (M == 0) return hipSuccess;
   dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
-  if (K % 64 == 0)
+  if (M >= kBigRows && K % big::BKB == 0 && N % big::BNB == 0)
+    hipLaunchKernelGGL(big::gemm_big_kernel<ResidualEpi>, dim3(N / big::BNB, (M + big::BMB - 1) / big::BMB),
+                       dim3(512), 0, st, o, M, N, K, epi);
+  else if (K % 64 == 0)
     hipLaunchKernelGGL(gemm_tn_bf16_dma_kernel<ResidualEpi>, grid, dim3(512), 0, st, o, M, N, K, epi);
   else
     hipLaunchKernelGGL(gemm_tn_bf16_kernel<ResidualEpi>, grid, dim3(256), 0, st, o, M, N, K, epi);

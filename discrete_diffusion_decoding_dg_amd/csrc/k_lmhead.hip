@@ -153,7 +153,8 @@ __device__ __forceinline__ uint32_t sel4(uint32_t w0, uint32_t w1, uint32_t w2, 
   return (k & 2) ? ((k & 1) ? w3 : w2) : ((k & 1) ? w1 : w0);
 }
 
-template <int MT, int DW, int NBUF>
+// ENT: entropy-bounded step (every row draws; entropy statistics kept).
+template <int MT, int DW, int NBUF, bool ENT>
 __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
   static_assert(MT == 16 || MT == 32, "row block");
   static_assert(DW % 32 == 0, "slice width");
@@ -228,12 +229,19 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
   const float inv_tau = rvalid ? a.prm[gb].inv_tau : 0.f;
   bool resample = false;
   if (rvalid) {
-    const u32x4 w = philox4x32_10(0u, static_cast<uint32_t>(gi), static_cast<uint32_t>(gb),
-                                  kStreamBernoulli, a.k0, a.k1);
-    resample = u01(w.x) < a.prm[gb].lam;
+    if constexpr (ENT) {
+      resample = true;
+    } else {
+      const u32x4 w = philox4x32_10(0u, static_cast<uint32_t>(gi), static_cast<uint32_t>(gb),
+                                    kStreamBernoulli, a.k0, a.k1);
+      resample = u01(w.x) < a.prm[gb].lam;
+    }
   }
   float m_ref = -INFINITY, l_lane = 0.f, best_v = -INFINITY;
   int best_i = -1;
+  // entropy statistics: sum of p (t - m_ref) and the plain argmax
+  float s1_lane = 0.f, dbest_v = -INFINITY;
+  int dbest_i = -1;
   uint32_t gw0 = 0, gw1 = 0, gw2 = 0, gw3 = 0;   // Philox words of the current group
   auto gumbel_block = [&](int tile) {
     const u32x4 w = philox4x32_10(static_cast<uint32_t>(16 * (tile >> 2) + j), static_cast<uint32_t>(gi),
@@ -325,6 +333,12 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
         }
       }
       const float t2 = s * kLog2e;
+      if constexpr (ENT) {
+        if (rvalid && t2 > dbest_v) {   // strict: the earlier (lower) id keeps a tie
+          dbest_v = t2;
+          dbest_i = v;
+        }
+      }
       float sc = 1.f;
       if (__builtin_amdgcn_ballot_w64(t2 > m_ref + kRescaleSlack)) {
         float mx = t2;
@@ -332,6 +346,9 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
         for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
         if (mx > m_ref + kRescaleSlack) {
           sc = __builtin_amdgcn_exp2f(m_ref - mx);   // 0 on the first tile
+          // re-reference sum p (t - m): every p scales by sc and every
+          // (t - m) grows by m_old - m_new
+          if constexpr (ENT) s1_lane = (l_lane > 0.f) ? sc * (s1_lane + (m_ref - mx) * l_lane) : 0.f;
           m_ref = mx;
         }
         if (__builtin_amdgcn_ballot_w64(sc != 1.f) && lane == 0) last_resc = tile;
@@ -340,6 +357,7 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
       // bf16 probability times an embedding row can contribute to z
       const float p = __builtin_amdgcn_exp2f(t2 - m_ref);
       l_lane = l_lane * sc + p;
+      if constexpr (ENT) s1_lane += p * (t2 - m_ref);
       *reinterpret_cast<uint16_t *>(Pb + poff<MT>(er, j)) = f32_to_bf16(p);
       if (j == 0) scl[er] = sc;
     }
@@ -423,8 +441,8 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
 
   // ---- write the split partials
   if (epi) {
-    float l = l_lane, bv = best_v;
-    int bi = best_i;
+    float l = l_lane, bv = best_v, s1 = s1_lane, dv = dbest_v;
+    int bi = best_i, di = dbest_i;
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) {
       l += __shfl_xor(l, o, 64);
@@ -434,6 +452,15 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
         bv = ov;
         bi = oi;
       }
+      if constexpr (ENT) {
+        s1 += __shfl_xor(s1, o, 64);
+        const float odv = __shfl_xor(dv, o, 64);
+        const int odi = __shfl_xor(di, o, 64);
+        if (odi >= 0 && (di < 0 || odv > dv || (odv == dv && odi < di))) {
+          dv = odv;
+          di = odi;
+        }
+      }
     }
     if (rvalid && j == 0) {
       RowPartial p;
@@ -441,6 +468,10 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
       p.l = l;
       p.best = bv;
       p.arg = bi;
+      p.s1 = ENT ? s1 : 0.f;
+      p.dbest = ENT ? dv : -INFINITY;
+      p.darg = ENT ? di : -1;
+      p.pad = 0;
       a.part[static_cast<int64_t>(split) * a.R + grow] = p;
     }
   }
@@ -519,7 +550,7 @@ size_t lmhead_workspace_bytes(const Shape &s) {
 
 hipError_t launch_lmhead_bf16(const uint16_t *h1, const uint16_t *E, const int32_t *x_t,
                               const StepParams *prm, const Shape &s, uint64_t seed, void *work,
-                              float *p0, hipStream_t st) {
+                              float *p0, bool entropy, hipStream_t st) {
   Plan p;
   if (!plan(s, p)) return hipErrorInvalidValue;
   if (s.R() == 0) return hipSuccess;
@@ -533,10 +564,13 @@ hipError_t launch_lmhead_bf16(const uint16_t *h1, const uint16_t *E, const int32
                                       static_cast<size_t>(p.splits) * s.R() * sizeof(RowPartial));
   const int rblocks = (s.R() + p.MT - 1) / p.MT;
   const dim3 grid(rblocks * p.splits);
-#define DG_LM(MT_, DW_, NB_)                                                              \
-  if (p.MT == MT_ && p.DW == DW_ && p.NBUF == NB_) {                                      \
-    hipLaunchKernelGGL((lmhead_kernel<MT_, DW_, NB_>), grid, dim3(512), 0, st, a, rblocks); \
-    return hipGetLastError();                                                             \
+#define DG_LM(MT_, DW_, NB_)                                                                     \
+  if (p.MT == MT_ && p.DW == DW_ && p.NBUF == NB_) {                                             \
+    if (entropy)                                                                                 \
+      hipLaunchKernelGGL((lmhead_kernel<MT_, DW_, NB_, true>), grid, dim3(512), 0, st, a, rblocks); \
+    else                                                                                         \
+      hipLaunchKernelGGL((lmhead_kernel<MT_, DW_, NB_, false>), grid, dim3(512), 0, st, a, rblocks); \
+    return hipGetLastError();                                                                    \
   }
   DG_LM(32, 32, 2) DG_LM(32, 64, 2) DG_LM(32, 128, 2) DG_LM(32, 256, 2) DG_LM(16, 352, 1)
 #undef DG_LM

@@ -1,0 +1,126 @@
+// Entropy-bounded acceptance, uniform re-noise and the adaptive stop test.
+//
+// DiffusionGemma Technical Report (hyper.ai summary), Method, sampler
+// paragraph (the recommended sampler): canvas positions are accepted in order
+// of increasing entropy while the summed entropy of the accepted set (read as
+// the bound on their mutual information) stays below eps_accept, and at least
+// the lowest-entropy position; every other position is re-noised with a
+// uniformly random token; a canvas stops once its mean entropy is below
+// eps_stop and its argmax predictions repeat those of the previous step.
+//
+// One block per canvas, one thread per position (padded to a power of two):
+// a bitonic sort of (entropy, position) in LDS, an inclusive scan of the
+// sorted entropies, then every thread settles the position of its rank.
+#include "dg_device.hpp"
+#include "dg_kernels.hpp"
+
+namespace dg {
+namespace {
+
+constexpr uint32_t kStreamRenoise = 3;
+
+__device__ __forceinline__ bool key_less(float ha, int pa, float hb, int pb) {
+  return ha < hb || (ha == hb && pa < pb);
+}
+
+__global__ void __launch_bounds__(1024) entropy_select_kernel(
+    EntropyRows ent, const int32_t *__restrict__ x_t, const int32_t *__restrict__ det_prev, int C,
+    int V, float eps_accept, float eps_stop, uint32_t k0, uint32_t k1, int step,
+    int32_t *__restrict__ x_out, int32_t *__restrict__ det_out, float *__restrict__ entropy_out,
+    int32_t *__restrict__ stop_out, int32_t *__restrict__ stopped, int32_t *__restrict__ steps_out) {
+  __shared__ float key[kSelectMaxC];
+  __shared__ int pos[kSelectMaxC];
+  __shared__ float scan[kSelectMaxC];
+  const int b = blockIdx.x, t = threadIdx.x, n = blockDim.x;   // n: a power of two >= C
+  const int64_t base = static_cast<int64_t>(b) * C;
+  if (stopped && stopped[b]) {
+    // a stopped canvas keeps its tokens and predictions
+    for (int i = t; i < C; i += n) {
+      x_out[base + i] = x_t[base + i];
+      det_out[base + i] = det_prev ? det_prev[base + i] : ent.det[base + i];
+      if (entropy_out) entropy_out[base + i] = ent.H[base + i];
+    }
+    if (t == 0) stop_out[b] = 1;
+    return;
+  }
+  const bool in = t < C;
+  key[t] = in ? ent.H[base + t] : INFINITY;
+  pos[t] = in ? t : 0x7fffffff;
+  if (in) {
+    det_out[base + t] = ent.det[base + t];
+    if (entropy_out) entropy_out[base + t] = ent.H[base + t];
+  }
+  __syncthreads();
+  // bitonic sort, ascending by (entropy, position)
+  for (int k = 2; k <= n; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int p = t ^ j;
+      if (p > t) {
+        const bool up = (t & k) == 0;
+        const bool swap = up ? key_less(key[p], pos[p], key[t], pos[t])
+                             : key_less(key[t], pos[t], key[p], pos[p]);
+        if (swap) {
+          const float kt = key[t];
+          key[t] = key[p];
+          key[p] = kt;
+          const int pt = pos[t];
+          pos[t] = pos[p];
+          pos[p] = pt;
+        }
+      }
+      __syncthreads();
+    }
+  // inclusive scan of the sorted entropies (padding sorts last)
+  scan[t] = in ? key[t] : 0.f;
+  __syncthreads();
+  for (int off = 1; off < n; off <<= 1) {
+    const float add = (t >= off) ? scan[t - off] : 0.f;
+    __syncthreads();
+    scan[t] += add;
+    __syncthreads();
+  }
+  if (in) {
+    const int i = pos[t];
+    const bool accept = (t == 0) || (scan[t] < eps_accept);
+    int32_t tok;
+    if (accept) {
+      tok = ent.y[base + i];
+    } else {
+      const u32x4 w = philox4x32_10(0u, static_cast<uint32_t>(i), static_cast<uint32_t>(b),
+                                    kStreamRenoise, k0, k1);
+      tok = static_cast<int32_t>((static_cast<uint64_t>(w.x) * static_cast<uint32_t>(V)) >> 32);
+    }
+    x_out[base + i] = tok;
+  }
+  const bool same = !in || !det_prev || ent.det[base + t] == det_prev[base + t];
+  const int all_same = __syncthreads_and(same ? 1 : 0);
+  if (t == 0) {
+    const float mean = scan[C - 1] / static_cast<float>(C);
+    const int stop = (det_prev && all_same && mean < eps_stop) ? 1 : 0;
+    stop_out[b] = stop;
+    if (stop && stopped) {
+      stopped[b] = 1;
+      if (steps_out) steps_out[b] = step + 1;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_entropy_select(const EntropyRows &ent, const int32_t *x_t,
+                                 const int32_t *det_prev, int B, int C, int V, float eps_accept,
+                                 float eps_stop, uint64_t seed, int step, int32_t *x_out,
+                                 int32_t *det_out, float *entropy_out, int32_t *stop_out,
+                                 int32_t *stopped, int32_t *steps_out, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  if (C < 1 || C > kSelectMaxC) return hipErrorInvalidValue;
+  int n = 64;
+  while (n < C) n <<= 1;
+  hipLaunchKernelGGL(entropy_select_kernel, dim3(B), dim3(n), 0, st, ent, x_t, det_prev, C, V,
+                     eps_accept, eps_stop, static_cast<uint32_t>(seed),
+                     static_cast<uint32_t>(seed >> 32), step, x_out, det_out, entropy_out,
+                     stop_out, stopped, steps_out);
+  return hipGetLastError();
+}
+
+}  // namespace dg

@@ -163,6 +163,41 @@ dg_status dg_denoise_step_taps(dg_model *m, const int32_t *x_t, const void *z_t,
 dg_status dg_generate_canvas(dg_model *m, const void *K_pre, const void *V_pre, int32_t steps,
                              uint64_t seed, int32_t *x_out, void *z_out, void *stream);
 
+/* Entropy-bounded step, the recommended sampler (TR summary, Method, sampler
+ * paragraph; Experiments: at most 48 steps, about 12 with adaptive stopping).
+ * Same decoder, temperature and z as dg_denoise_step at time t; then, per
+ * canvas (readings of the pages, which give no formula):
+ *   H_i = entropy of p0_i in nats; positions taken in increasing H (ties by
+ *   position) are accepted while the running sum of H stays < eps_accept, and
+ *   at least the first; an accepted position takes the Gumbel-max draw of
+ *   p0 (the Step path's noise); every other position is re-noised with
+ *   floor(w V / 2^32), w = word 0 of Philox block (0, i, b, 3);
+ *   det_out = argmax_v of the scaled logits (lowest id on ties);
+ *   stop_out[b] = 1 iff det_prev is given, the mean of H over the canvas is
+ *   < eps_stop and det_out equals det_prev at every position.
+ *   det_prev [B,C] int32 may be NULL (first step: never stops);
+ *   entropy_out [B,C] f32 may be NULL. C <= 1024 (DG_ERR_UNSUPPORTED else).
+ *   x_out / z_out / det_out must not overlap x_t / z_t / det_prev. */
+dg_status dg_denoise_step_entropy(dg_model *m, const int32_t *x_t, const void *z_t,
+                                  const void *K_pre, const void *V_pre, const float *t,
+                                  uint64_t seed, float eps_accept, float eps_stop,
+                                  const int32_t *det_prev, int32_t *x_out, void *z_out,
+                                  int32_t *det_out, float *entropy_out, int32_t *stop_out,
+                                  void *stream);
+
+/* Generate B canvases with the entropy-bounded step and adaptive stopping:
+ * x_init and z = 0 as dg_generate_canvas; step k (t_k = 1 - k/max_steps,
+ * seed + k) runs dg_denoise_step_entropy with the previous step's argmax
+ * (none at k = 0); a canvas that stops keeps its tokens and z from then on
+ * and steps_out[b] (device int32 [B]) receives the number of steps it took
+ * (max_steps if it never stopped). Every 4 steps the call synchronises the
+ * stream to end early once every canvas has stopped. x_out [B,C] int32 and
+ * z_out [B,C,d] act (may be NULL) receive the final canvases. */
+dg_status dg_generate_canvas_entropy(dg_model *m, const void *K_pre, const void *V_pre,
+                                     int32_t max_steps, uint64_t seed, float eps_accept,
+                                     float eps_stop, int32_t *x_out, void *z_out,
+                                     int32_t *steps_out, void *stream);
+
 /* Per-stage GPU time of the calls made while profiling is on, measured with a
  * HIP event pair recorded on the call's stream around each stage's launches.
  * Stages: 0 embed, 1 q/k/v projection, 2 attention (+ split merge),

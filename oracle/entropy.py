@@ -143,5 +143,6 @@ def generate_canvas_entropy(cfg, w, K_pre, V_pre, max_steps, seed, eps_accept, e
         stopped[newly] = True
         steps[newly] = k + 1
         records.append(dict(k=k, active=act, **{n: r[n] for n in
-                                                ["H", "det", "det_gap", "y", "gap", "top1", "accept", "stop"]}))
+                                                ["H", "det", "det_gap", "det_top", "y", "gap", "top1",
+                                                 "accept", "stop", "x_out"]}))
     return {"x": x, "z": z, "steps": steps, "records": records}
