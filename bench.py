@@ -200,6 +200,43 @@ def main():
     torch.cuda.synchronize()
     gen_ms = g0.elapsed_time(g1)
 
+    # the entropy-bounded step (the pages' recommended sampler) on the same
+    # workload: per-step time, and adaptive generation with at most 48 steps
+    # (thresholds in nats; with random weights the entropies sit near ln V, so
+    # the canvas accepts a couple of tokens per step and does not stop early)
+    import math
+    eps_a, eps_s = 2.0 * math.log(cfg.V), 1.0
+    det = [torch.empty_like(x), torch.empty_like(x)]
+    stop = torch.empty((cfg.B,), dtype=torch.int32, device="cuda")
+
+    def ent_step(k):
+        a, b = k & 1, (k & 1) ^ 1
+        dg.dg_denoise_step_entropy(model, xs[a], zs[a], Kp, Vp, tvec(k), 2000 + k, eps_a, eps_s,
+                                   det[a] if k else None, xs[b], zs[b], det[b], stop)
+
+    for k in range(args.warmup):
+        ent_step(k)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(args.steps):
+        ent_step(args.warmup + k)
+    e1.record()
+    torch.cuda.synchronize()
+    ent_ms = e0.elapsed_time(e1) / args.steps
+    steps_out = torch.empty((cfg.B,), dtype=torch.int32, device="cuda")
+    dg.dg_generate_canvas_entropy(model, Kp, Vp, 48, 11, eps_a, eps_s, xo, steps_out)
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    dg.dg_generate_canvas_entropy(model, Kp, Vp, 48, 11, eps_a, eps_s, xo, steps_out)
+    a1.record()
+    torch.cuda.synchronize()
+    entropy = {"ms_per_step": ent_ms, "steps_per_s": 1000.0 / ent_ms,
+               "eps_accept_nats": eps_a, "eps_stop_nats": eps_s,
+               "generate_max48_ms": a0.elapsed_time(a1),
+               "generate_steps_taken": steps_out.cpu().tolist()[:8]}
+
     fl = cfg.flops_per_step()
     lm_ms, lm_n = prof["lmhead"]
     lm_avg_ms = lm_ms / max(1, lm_n)
@@ -235,6 +272,7 @@ def main():
                      "traffic": traffic, "avg_ms": lm_avg_ms,
                      "algorithmic_flop_per_launch": fl["lm"]},
         "kernels": kernels,
+        "entropy_step": entropy,
     }
     if not args.no_corrupt:
         result["corrupt"] = corrupt_bandwidth()
