@@ -69,14 +69,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
   asm volatile("" ::: "memory");
 }
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_le_rt(int n) {
-  if constexpr (N > 0) {
-    if (n >= N) {
-      wait_vmcnt<N>();
+// wait until at most k * STEP vector-memory operations are outstanding, for a
+// runtime k in [0, K]: K + 1 compile-time cases
+template <int STEP, int K>
+__device__ __forceinline__ void wait_vmcnt_steps(int k) {
+  if constexpr (K > 0) {
+    if (k >= K) {
+      wait_vmcnt<K * STEP>();
       return;
     }
-    wait_vmcnt_le_rt<N - 1>(n);
+    wait_vmcnt_steps<STEP, K - 1>(k);
   } else {
     wait_vmcnt<0>();
   }
@@ -157,7 +159,7 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(AttnArgs a) {
 
   // direct loads of one tile: load u in [0, NDMA) fills piece u % NPR of K
   // (u < NPR) or of V; wave w issues loads w, w + 8, ...
-  const int my_loads = (NDMA - wave + NWA - 1) / NWA;
+  constexpr int MINL = NDMA / NWA;               // loads per wave and tile, at least
   auto issue_tile = [&](int tile) {
     uint8_t *st = stage_mem + (tile % NS) * 2 * TILE_B;
 #pragma unroll
@@ -176,6 +178,11 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(AttnArgs a) {
       }
     }
   };
+  // the Q loads must have landed before the first direct load is issued: the
+  // compiler does not see the inline-asm loads, and with Q still pending it
+  // would wait for every outstanding load (vmcnt 0) before the first score
+  // MFMA of each tile, which would drain the pipeline every tile
+  wait_vmcnt<0>();
   for (int t = tile0; t < tile_end && t < tile0 + NS - 1; ++t) issue_tile(t);
 
   f32x16 oacc[NB];
@@ -188,11 +195,12 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(AttnArgs a) {
 
   for (int tile = tile0; tile < tile_end; ++tile) {
     // this wave's loads of `tile` have landed once at most those of the
-    // tiles issued after it are outstanding; the barrier makes every wave's
-    // loads visible and frees the stage read during the previous tile
+    // tiles issued after it are outstanding (MINL or MINL + 1 per tile and
+    // wave; MINL is the safe bound); the barrier makes every wave's loads
+    // visible and frees the stage read during the previous tile
     int after = tile_end - 1 - tile;
     if (after > NS - 2) after = NS - 2;
-    wait_vmcnt_le_rt<63>(after * my_loads);
+    wait_vmcnt_steps<MINL, NS - 2>(after);
     __syncthreads();
     if (tile + NS - 1 < tile_end) issue_tile(tile + NS - 1);
     const uint8_t *Ks = stage_mem + (tile % NS) * 2 * TILE_B;

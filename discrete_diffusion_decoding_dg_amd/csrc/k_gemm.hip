@@ -175,15 +175,16 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
   asm volatile("" ::: "memory");
 }
-// wait until at most n of this wave's vector-memory operations are outstanding
-template <int N = 63>
-__device__ __forceinline__ void vm_wait_le(int n) {
-  if constexpr (N > 0) {
-    if (n >= N) {
-      vm_wait<N>();
+// wait until at most k * STEP of this wave's vector-memory operations are
+// outstanding, for a runtime k in [0, K]: K + 1 compile-time cases
+template <int STEP, int K>
+__device__ __forceinline__ void vm_wait_steps(int k) {
+  if constexpr (K > 0) {
+    if (k >= K) {
+      vm_wait<K * STEP>();
       return;
     }
-    vm_wait_le<N - 1>(n);
+    vm_wait_steps<STEP, K - 1>(k);
   } else {
     vm_wait<0>();
   }
@@ -230,7 +231,7 @@ __global__ void __launch_bounds__(512) gemm_tn_bf16_dma_kernel(const uint16_t *_
   for (int it = 0; it < nk; ++it) {
     int younger = nk - 1 - it;                      // slabs issued after this one
     if (younger > NS - 2) younger = NS - 2;
-    vm_wait_le(2 * younger);
+    vm_wait_steps<2, NS - 2>(younger);
     __syncthreads();                                // every wave's part of slab `it` landed
     if (it + NS - 1 < nk) issue(it + NS - 1);       // refill the slab computed last iteration
     const uint16_t *as = As + (it % NS) * SLAB;
@@ -360,7 +361,7 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(const uint16_t *__restric
   for (int it = 0; it < nk; ++it) {
     int younger = nk - 1 - it;                      // slabs issued after this one
     if (younger > NS_BIG - 2) younger = NS_BIG - 2;
-    vm_wait_le(4 * younger);
+    vm_wait_steps<4, NS_BIG - 2>(younger);
     __syncthreads();                                // every wave's part of slab `it` landed
     if (it + NS_BIG - 1 < nk) issue(it + NS_BIG - 1);   // refill the slab computed last iteration
     const uint16_t *as = As + (it % NS_BIG) * SLB;
