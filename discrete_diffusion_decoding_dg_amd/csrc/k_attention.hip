@@ -107,6 +107,29 @@ __device__ __forceinline__ void lds_dma16_va(const void *src, void *lds) {
       : "memory");
 }
 
+// The same load with a wave-uniform 64-bit base (scalar registers) and a
+// 32-bit per-lane byte offset: cheaper to form than a per-lane address.
+__device__ __forceinline__ void lds_dma16_sa(const void *base, uint32_t voff, void *lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds)));
+  // readfirstlane returns a signed int: go through uint32_t so that the low
+  // half is zero-extended
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+  const uint64_t sb = (static_cast<uint64_t>(hi) << 32) | lo;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(voff), "s"(sb)
+      : "memory");
+}
+
 template <int HD>
 __global__ void __launch_bounds__(512) attn_fwd_kernel(AttnArgs a) {
   using G_ = Geo<HD>;
@@ -160,8 +183,30 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(AttnArgs a) {
   // direct loads of one tile: load u in [0, NDMA) fills piece u % NPR of K
   // (u < NPR) or of V; wave w issues loads w, w + 8, ...
   constexpr int MINL = NDMA / NWA;               // loads per wave and tile, at least
+  // byte offset of this lane's key row inside a tile, for each piece phase
+  uint32_t koff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) koff[q] = static_cast<uint32_t>((lane ^ (4 * q)) * HD * 2);
   auto issue_tile = [&](int tile) {
     uint8_t *st = stage_mem + (tile % NS) * 2 * TILE_B;
+    const int j0 = tile * BK;
+    if (j0 + BK <= a.P || (j0 >= a.P && j0 + BK <= Lk)) {
+      // the whole tile lies in the prefix or in the canvas: one uniform base
+      const bool pre = j0 + BK <= a.P;
+      const uint16_t *kb = pre ? a.Kp + kvp_base + static_cast<int64_t>(j0) * HD
+                               : a.k + kvc_base + static_cast<int64_t>(j0 - a.P) * HD;
+      const uint16_t *vb = pre ? a.Vp + kvp_base + static_cast<int64_t>(j0) * HD
+                               : a.v + kvc_base + static_cast<int64_t>(j0 - a.P) * HD;
+#pragma unroll
+      for (int n = 0; n < MAXL; ++n) {
+        const int u = wave + n * NWA;
+        if (u < NDMA) {
+          const int tensor = u >= NPR, p = tensor ? u - NPR : u;
+          lds_dma16_sa((tensor ? vb : kb) + p * 8, koff[p & 3], st + tensor * TILE_B + p * BK * 16);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int n = 0; n < MAXL; ++n) {
       const int u = wave + n * NWA;
@@ -225,21 +270,31 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(AttnArgs a) {
         sacc[mb][ks % SCH] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], sacc[mb][ks % SCH], 0, 0, 0);
       }
     }
-    // element e = 4 jj + i of block mb: key 32 mb + 8 jj + 4 hl + i of this tile
+    // element e = 4 jj + i of block mb: key 32 mb + 8 jj + 4 hl + i of this
+    // tile. Raw scores here; the scale folds into the exponent below
+    // (scale_log2 > 0, so the max commutes with it).
     float sv[2][16];
-    float tmax = -INFINITY;
+    float rmax = -INFINITY;
     const int kv0 = tile * BK;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int key = kv0 + mb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
-        const float sum = (SCH == 2) ? sacc[mb][0][e] + sacc[mb][1][e] : sacc[mb][0][e];
-        const float v = (key < Lk) ? sum * a.scale_log2 : -INFINITY;
-        sv[mb][e] = v;
-        tmax = fmaxf(tmax, v);
+        sv[mb][e] = (SCH == 2) ? sacc[mb][0][e] + sacc[mb][1][e] : sacc[mb][0][e];
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));   // both halves of the query
+    if (kv0 + BK > Lk) {   // the last, partial tile: keys past the end drop out
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (kv0 + mb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3) >= Lk) sv[mb][e] = -INFINITY;
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) rmax = fmaxf(rmax, sv[mb][e]);
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));   // both halves of the query
+    const float tmax = rmax * a.scale_log2;
     if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kSlack)) {
       float alpha = 1.f;
       if (tmax > m_ref + kSlack) {
@@ -266,7 +321,7 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(AttnArgs a) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(sv[mb][e] - m_ref);
+        const float p = __builtin_amdgcn_exp2f(fmaf(sv[mb][e], a.scale_log2, -m_ref));
         psum += p;
         pa[2 * mb + (e >> 3)][e & 7] = static_cast<__bf16>(p);
       }
