@@ -21,7 +21,8 @@ Readings taken where the pages stop short (each documented where used):
 Step is the Euler step of the uniform-path CTMC,
 (1 - lambda) delta(y, x_t) + lambda p0(y) with
 lambda = clamp(dt * (-dkappa/dt) / (1 - kappa), 0, 1); FFW is the identity
-(z = p0 E); the decoder is one residual attention block with a tied head.
+(z = p0 E) unless a gated feed-forward block is given (ffw.py); the decoder
+is one residual attention block with a tied head.
 
 Floating point: reductions in float64; tensors are rounded to the
 activation dtype (bf16 round-to-nearest-even or fp32) at the same tensor
@@ -40,7 +41,8 @@ from .rounding import round_act, round_bf16, round_f32
 from .decoder import embed, qkv_proj, attention, out_proj, lm_head
 from .sampling import bernoulli_uniforms, gumbel_noise, step_select
 from .corrupt import corrupt
-from .step import denoise_step, generate_canvas
+from .step import denoise_step, generate_canvas, self_condition
+from .ffw import gelu_tanh, ffw, ffw_hidden
 from .entropy import (row_entropy, accept_mask, renoise_tokens, entropy_step,
                       generate_canvas_entropy)
 
@@ -49,5 +51,6 @@ __all__ = [
     "temperature", "inv_temperature", "round_act", "round_bf16", "round_f32", "embed",
     "qkv_proj", "attention", "out_proj", "lm_head", "bernoulli_uniforms", "gumbel_noise",
     "step_select", "corrupt", "denoise_step", "generate_canvas", "row_entropy", "accept_mask",
-    "renoise_tokens", "entropy_step", "generate_canvas_entropy",
+    "renoise_tokens", "entropy_step", "generate_canvas_entropy", "self_condition", "gelu_tanh",
+    "ffw", "ffw_hidden",
 ]

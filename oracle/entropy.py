@@ -5,7 +5,8 @@ the entropy of their predicted distribution, from low to high, and accepts
 tokens in that order while a bound on their mutual information stays strictly
 below an error tolerance; every other position is re-noised with a uniformly
 random token. Probabilities are sharpened by the annealed temperature
-(tau 0.8 -> 0.4, the same schedule as the Step path). Adaptive stopping ends
+(tau 0.8 -> 0.4, the same schedule as the Step path); z is the same
+self-conditioning signal as on the Step path (step.self_condition). Adaptive stopping ends
 the loop once the mean predicted entropy over the canvas is below a threshold
 and the deterministic predictions of two consecutive steps are identical.
 Experiments: at most 48 steps, about 12 on average; acceptance and stopping
@@ -35,6 +36,7 @@ from .decoder import embed, qkv_proj, attention, out_proj, lm_head
 from .sampling import gumbel_noise
 from .philox import philox4x32_10, mulhi_token
 from .corrupt import corrupt
+from .step import self_condition
 
 
 def row_entropy(s):
@@ -110,7 +112,8 @@ def entropy_step(cfg, w, x_t, z_t, K_pre, V_pre, t, seed, eps_accept, eps_stop, 
         stop = (H.mean(axis=1) < eps_stop) & np.all(det == np.asarray(det_prev), axis=1)
     out = dict(h0=h0, q=q, k=k, v=v, o=o, h1=h1, inv_tau=inv_tau, **head)
     out.update(H=H, det=det.astype(np.int32), det_gap=det_gap, det_top=det_top, y=y.astype(np.int32),
-               top1=top1, gap=gap, accept=acc, renoise=rn, x_out=x_out, stop=stop, z_out=head["z"])
+               top1=top1, gap=gap, accept=acc, renoise=rn, x_out=x_out, stop=stop, p0E=head["z"],
+               z_out=self_condition(w, head["z"], act))
     return out
 
 

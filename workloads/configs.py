@@ -31,6 +31,8 @@ class Config:
     zero_z_half: bool = False     # z_t = 0 for a seeded random half of the canvases
     seed: int = 0
     note: str = ""
+    ffw_hidden: int = 0           # width F of the gated self-conditioning block (0: identity)
+    ffw_gain: float = 1.0         # W_gate, W_up ~ N(0, (gain / sqrt(d))^2); W_down ~ N(0, 1 / F)
 
     @property
     def R(self):
@@ -51,7 +53,9 @@ class Config:
         attn = 4 * self.B * self.C * (self.P + self.C) * Hq * hd
         oproj = 2 * R * Hq * hd * d
         lm = 4 * R * self.V * d
-        return dict(qkv=qkv, attn=attn, oproj=oproj, lm=lm, total=qkv + attn + oproj + lm)
+        ffw = 6 * R * d * self.ffw_hidden
+        return dict(qkv=qkv, attn=attn, oproj=oproj, lm=lm, ffw=ffw,
+                    total=qkv + attn + oproj + lm + ffw)
 
 
 CONFIGS = {

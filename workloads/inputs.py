@@ -7,7 +7,9 @@ both sides then consume the same bits.
 """
 import numpy as np
 
-STREAMS = ["E", "Wq", "Wk", "Wv", "Wo", "K_pre", "V_pre", "x", "t", "z_mask", "z"]
+# New streams go at the end: child i of the spawn does not depend on the count.
+STREAMS = ["E", "Wq", "Wk", "Wv", "Wo", "K_pre", "V_pre", "x", "t", "z_mask", "z",
+           "W_gate", "W_up", "W_down"]
 
 
 def bf16_bits_from_f32(a):
@@ -42,9 +44,11 @@ def make_inputs(cfg, which=None):
 
     Layouts (row-major): E [V, d]; Wq [Hq*hd, d]; Wk, Wv [Hkv*hd, d];
     Wo [d, Hq*hd]; K_pre, V_pre [B, Hkv, P, hd]; x [B, C] int32;
-    z [B, C, d]; t [B] float32 (per-canvas t when the config asks for it).
+    z [B, C, d]; t [B] float32 (per-canvas t when the config asks for it);
+    with a self-conditioning block of width F: W_gate, W_up [F, d], W_down [d, F].
     """
-    names = which or ["E", "Wq", "Wk", "Wv", "Wo", "K_pre", "V_pre", "x", "t", "z"]
+    names = which or (["E", "Wq", "Wk", "Wv", "Wo", "K_pre", "V_pre", "x", "t", "z"] +
+                      (["W_gate", "W_up", "W_down"] if cfg.ffw_hidden else []))
     out = Inputs()
     hq, hkv, hd = cfg.n_q_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim, cfg.head_dim
     shapes = {
@@ -56,6 +60,11 @@ def make_inputs(cfg, which=None):
         "K_pre": ((cfg.B, cfg.n_kv_heads, cfg.P, hd), cfg.kv_std),
         "V_pre": ((cfg.B, cfg.n_kv_heads, cfg.P, hd), cfg.kv_std),
     }
+    if cfg.ffw_hidden:
+        F = cfg.ffw_hidden
+        shapes["W_gate"] = ((F, cfg.d), cfg.ffw_gain / np.sqrt(cfg.d))
+        shapes["W_up"] = ((F, cfg.d), cfg.ffw_gain / np.sqrt(cfg.d))
+        shapes["W_down"] = ((cfg.d, F), 1.0 / np.sqrt(F))
     for n in names:
         if n in shapes:
             shape, std = shapes[n]
