@@ -409,6 +409,8 @@ void plan(const Shape &s, int &splits, int &tps) {
   if (want < 1) want = 1;
   if (want > tiles) want = tiles;
   tps = (tiles + want - 1) / want;
+  // a one-tile split costs more in partials (and their merge) than it gains
+  if (tps < 2) tps = 2;
   splits = (tiles + tps - 1) / tps;
 }
 
