@@ -110,6 +110,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-corrupt", action="store_true")
+    ap.add_argument("--no-ffw", action="store_true", help="skip the feed-forward block timings")
     ap.add_argument("--copy-mib", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device to device three times (a plain copy kernel "
                          "of known size, to scale HBM byte counters)")
@@ -237,6 +238,45 @@ def main():
                "generate_max48_ms": a0.elapsed_time(a1),
                "generate_steps_taken": steps_out.cpu().tolist()[:8]}
 
+    # the step with the gated self-conditioning block z = FFW(p0 E) attached,
+    # at hidden widths d and 4 d (not part of `value`, whose workload keeps
+    # the identity block)
+    ffw_res = None
+    if not args.no_ffw:
+        ffw_res = {}
+        nsteps = min(args.steps, 100)
+        for F in (cfg.d, 4 * cfg.d):
+            cf = cfg.with_(ffw_hidden=F)
+            fw = {n: to_dev(make_inputs(cf, [n]), n, cf) for n in ["W_gate", "W_up", "W_down"]}
+            dg.dg_set_ffw(model, fw["W_gate"], fw["W_up"], fw["W_down"])
+            for k in range(args.warmup):
+                step(k)
+            torch.cuda.synchronize()
+            f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            f0.record()
+            for k in range(nsteps):
+                step(args.warmup + k)
+            f1.record()
+            torch.cuda.synchronize()
+            dg.dg_profile_read(model)
+            dg.dg_profile_enable(model, ["ffw"])
+            for k in range(nsteps):
+                step(k)
+            torch.cuda.synchronize()
+            dg.dg_profile_enable(model, [])
+            b_ms, b_n = dg.dg_profile_read(model)["ffw"]
+            blk_ms = b_ms / max(1, b_n)
+            flop = 6.0 * cfg.R * cfg.d * F
+            wbytes = 3.0 * F * cfg.d * 2
+            ffw_res[f"hidden_{F}"] = {
+                "ms_per_step": f0.elapsed_time(f1) / nsteps,
+                "block_ms": blk_ms,
+                "block_tflops": flop / (blk_ms * 1e-3) / 1e12,
+                "block_weight_gbs": wbytes / (blk_ms * 1e-3) / 1e9,
+                "block_gflop": flop / 1e9, "block_weight_mb": wbytes / 1e6}
+            dg.dg_set_ffw(model)
+            del fw
+
     fl = cfg.flops_per_step()
     lm_ms, lm_n = prof["lmhead"]
     lm_avg_ms = lm_ms / max(1, lm_n)
@@ -274,6 +314,8 @@ def main():
         "kernels": kernels,
         "entropy_step": entropy,
     }
+    if ffw_res is not None:
+        result["ffw_block"] = ffw_res
     if not args.no_corrupt:
         result["corrupt"] = corrupt_bandwidth()
     model.close()

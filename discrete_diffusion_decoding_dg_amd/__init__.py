@@ -7,13 +7,13 @@ libdg.so. Importing the binding fails loudly when the library is not built.
 from ._lib import (DG_DTYPE_BF16, DG_DTYPE_F32, DG_SCHEDULE_COSINE, DG_SCHEDULE_LINEAR,
                    DgError, Model, dg_corrupt, dg_corrupt_batch, dg_create, dg_denoise_step,
                    dg_denoise_step_taps, dg_denoise_step_entropy, dg_destroy, dg_generate_canvas,
-                   dg_generate_canvas_entropy, dg_last_error,
+                   dg_generate_canvas_entropy, dg_last_error, dg_set_ffw, dg_ffw,
                    dg_profile_enable, dg_profile_read,
                    dg_status_string, dg_workspace_bytes, library_path, load_library)
 
 __all__ = ["DG_DTYPE_BF16", "DG_DTYPE_F32", "DG_SCHEDULE_COSINE", "DG_SCHEDULE_LINEAR", "DgError",
            "Model", "dg_corrupt", "dg_corrupt_batch", "dg_create", "dg_denoise_step",
            "dg_denoise_step_taps", "dg_denoise_step_entropy", "dg_destroy", "dg_generate_canvas",
-           "dg_generate_canvas_entropy", "dg_last_error",
+           "dg_generate_canvas_entropy", "dg_last_error", "dg_set_ffw", "dg_ffw",
            "dg_profile_enable", "dg_profile_read",
            "dg_status_string", "dg_workspace_bytes", "library_path", "load_library"]

@@ -29,11 +29,12 @@ class dg_weights(ctypes.Structure):
 class dg_taps(ctypes.Structure):
     _fields_ = [("h0", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
                 ("v", ctypes.c_void_p), ("o", ctypes.c_void_p), ("h1", ctypes.c_void_p),
-                ("lse", ctypes.c_void_p), ("p0", ctypes.c_void_p), ("best", ctypes.c_void_p)]
+                ("lse", ctypes.c_void_p), ("p0", ctypes.c_void_p), ("best", ctypes.c_void_p),
+                ("p0E", ctypes.c_void_p)]
 
 
-NUM_STAGES = 7
-STAGES = ["embed", "qkv", "attention", "oproj", "lmhead", "combine", "corrupt"]
+NUM_STAGES = 8
+STAGES = ["embed", "qkv", "attention", "oproj", "lmhead", "combine", "corrupt", "ffw"]
 
 
 class dg_profile(ctypes.Structure):
@@ -42,7 +43,8 @@ class dg_profile(ctypes.Structure):
 
 EXPORTS = ["dg_create", "dg_destroy", "dg_workspace_bytes", "dg_corrupt", "dg_corrupt_batch",
            "dg_denoise_step", "dg_denoise_step_taps", "dg_generate_canvas",
-           "dg_denoise_step_entropy", "dg_generate_canvas_entropy", "dg_profile_enable",
+           "dg_denoise_step_entropy", "dg_generate_canvas_entropy", "dg_set_ffw", "dg_ffw",
+           "dg_profile_enable",
            "dg_profile_read", "dg_status_string", "dg_last_error"]
 
 _lib = None
@@ -76,6 +78,8 @@ def load_library():
     lib.dg_denoise_step_entropy.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(f32), u64, f32, f32,
                                             vp, vp, vp, vp, vp, vp, vp]
     lib.dg_generate_canvas_entropy.argtypes = [vp, vp, vp, i32, u64, f32, f32, vp, vp, vp, vp]
+    lib.dg_set_ffw.argtypes = [vp, i32, vp, vp, vp]
+    lib.dg_ffw.argtypes = [vp, vp, vp, vp]
     lib.dg_profile_enable.argtypes = [vp, ctypes.c_int]
     lib.dg_profile_read.argtypes = [vp, ctypes.POINTER(dg_profile)]
     lib.dg_status_string.argtypes = [ctypes.c_int]
@@ -186,7 +190,7 @@ def dg_denoise_step(model, x_t, z_t, K_pre, V_pre, t, dt, seed, x_out, z_out, ls
 
 def dg_denoise_step_taps(model, x_t, z_t, K_pre, V_pre, t, dt, seed, x_out, z_out, taps=None,
                          stream=None):
-    """`taps` maps any of h0, q, k, v, o, h1, lse, p0, best to output tensors."""
+    """`taps` maps any of h0, q, k, v, o, h1, lse, p0, best, p0E to output tensors."""
     tp = None
     if taps:
         tp = dg_taps(**{k: (v.data_ptr() if v is not None else None) for k, v in taps.items()})
@@ -219,6 +223,22 @@ def dg_generate_canvas_entropy(model, K_pre, V_pre, max_steps, seed, eps_accept,
                                                      int(max_steps), int(seed), float(eps_accept),
                                                      float(eps_stop), _ptr(x_out), _ptr(z_out),
                                                      _ptr(steps_out), _stream(stream)))
+
+
+def dg_set_ffw(model, W_gate=None, W_up=None, W_down=None):
+    """Attach the gated feed-forward block (W_gate, W_up [F, d], W_down [d, F]);
+    no tensors detach it. The model keeps references to the tensors."""
+    if W_gate is None:
+        _check(load_library().dg_set_ffw(model.handle, 0, None, None, None))
+        model._ffw = None
+        return
+    _check(load_library().dg_set_ffw(model.handle, int(W_gate.shape[0]), _ptr(W_gate), _ptr(W_up),
+                                     _ptr(W_down)))
+    model._ffw = (W_gate, W_up, W_down)
+
+
+def dg_ffw(model, u, z_out, stream=None):
+    _check(load_library().dg_ffw(model.handle, _ptr(u), _ptr(z_out), _stream(stream)))
 
 
 def dg_profile_enable(model, stages=None):

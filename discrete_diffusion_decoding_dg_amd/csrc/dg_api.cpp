@@ -169,6 +169,11 @@ struct dg_model {
   int32_t *gendet;          // [2][R] argmax predictions during generation
   int32_t *stopped, *stopbuf;   // [B] each
   int32_t *host_stopped = nullptr;   // pinned [B], allocated on first use
+  // gated self-conditioning block (dg_set_ffw); ffw_F == 0 is the identity
+  int ffw_F = 0;
+  const void *ffw_wg = nullptr, *ffw_wu = nullptr, *ffw_wd = nullptr;
+  char *ffw_mem = nullptr;   // owned: packed gate/up rows (bf16), u [R, d], hid [R, F]
+  void *ffw_gu = nullptr, *ffw_u = nullptr, *ffw_hid = nullptr;
   // profiling: event pairs recorded around stage launches while enabled
   int prof_mask = 0;
   struct Mark {
@@ -198,6 +203,35 @@ struct StageTimer {
   }
 };
 
+// z = FFW(u) through the attached block; rows of canvases marked in `frozen`
+// (nullable) take z_t instead.
+dg_status run_ffw(dg_model *m, const void *u, void *z, const int32_t *frozen, const void *z_t,
+                  hipStream_t st) {
+  const dg::Shape &s = m->s;
+  const int F = m->ffw_F;
+  StageTimer tm(m, 7, st);
+  if (m->cfg.dtype == DG_DTYPE_BF16) {
+    using u16 = uint16_t;
+    DG_HIP(dg::launch_ffw_gate_up_bf16(static_cast<const u16 *>(u), static_cast<const u16 *>(m->ffw_gu),
+                                       s.R(), s.d, F, static_cast<u16 *>(m->ffw_hid), st),
+           "feed-forward gate/up launch");
+    DG_HIP(dg::launch_ffw_down_bf16(static_cast<const u16 *>(m->ffw_hid),
+                                    static_cast<const u16 *>(m->ffw_wd), s.R(), s.d, F, s.C, frozen,
+                                    static_cast<const u16 *>(z_t), static_cast<u16 *>(z), st),
+           "feed-forward down launch");
+  } else {
+    DG_HIP(dg::launch_ffw_gate_up_f32(static_cast<const float *>(u), static_cast<const float *>(m->ffw_wg),
+                                      static_cast<const float *>(m->ffw_wu), s.R(), s.d, F,
+                                      static_cast<float *>(m->ffw_hid), st),
+           "feed-forward gate/up launch");
+    DG_HIP(dg::launch_ffw_down_f32(static_cast<const float *>(m->ffw_hid),
+                                   static_cast<const float *>(m->ffw_wd), s.R(), s.d, F, s.C, frozen,
+                                   static_cast<const float *>(z_t), static_cast<float *>(z), st),
+           "feed-forward down launch");
+  }
+  return DG_OK;
+}
+
 // prm: device step constants of every canvas; when n_inline > 0 the embedding
 // launch first stores them there from the host array `inline_prm`.
 // With `ent` the step is the entropy-bounded one: every row draws and the
@@ -217,6 +251,14 @@ dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void 
   void *o = taps && taps->o ? taps->o : m->o;
   void *h1 = taps && taps->h1 ? taps->h1 : m->h1;
   int32_t *best = taps ? taps->best : nullptr;
+  // with a feed-forward block the merge writes its input p0 E, and the block
+  // takes care of frozen canvases
+  void *zc = z_out;
+  const int32_t *frozen_c = frozen;
+  if (m->ffw_F) {
+    zc = taps && taps->p0E ? taps->p0E : m->ffw_u;
+    frozen_c = nullptr;
+  }
   {
     StageTimer tm(m, 0, st);
     DG_HIP(dg::launch_embed(bf16, m->w.E, x_t, z_t, s.R(), s.d, s.V, h0, prm, inline_prm, n_inline,
@@ -255,8 +297,8 @@ dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void 
     }
     {
       StageTimer tm(m, 5, st);
-      DG_HIP(dg::launch_combine(true, m->lm, dg::lmhead_splits(s), x_t, prm, s, seed, x_out, z_out,
-                              lse, best, ent, frozen, z_t, st),
+      DG_HIP(dg::launch_combine(true, m->lm, dg::lmhead_splits(s), x_t, prm, s, seed, x_out, zc,
+                              lse, best, ent, frozen_c, z_t, st),
            "combine launch");
     }
   } else {
@@ -289,11 +331,13 @@ dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void 
     }
     {
       StageTimer tm(m, 5, st);
-      DG_HIP(dg::launch_combine(false, m->lm, 1, x_t, prm, s, seed, x_out, z_out, lse, best, ent,
-                              frozen, z_t, st),
+      DG_HIP(dg::launch_combine(false, m->lm, 1, x_t, prm, s, seed, x_out, zc, lse, best, ent,
+                              frozen_c, z_t, st),
            "combine launch");
     }
   }
+  if (m->ffw_F)
+    if (dg_status e = run_ffw(m, zc, z_out, frozen, z_t, st)) return e;
   if (p0) {
     if (!lse) return fail(DG_ERR_INVALID_ARG, "internal: p0 requires lse");
     DG_HIP(dg::launch_p0_from_logits(p0, lse, s.R(), s.V, st), "p0 launch");
@@ -438,6 +482,7 @@ dg_status dg_destroy(dg_model *m) {
     (void)hipEventDestroy(mk.b);
   }
   hipError_t f = hipFree(m->ws);
+  if (m->ffw_mem) (void)hipFree(m->ffw_mem);
   if (m->host_stopped) (void)hipHostFree(m->host_stopped);
   delete m;
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
@@ -501,7 +546,7 @@ dg_status dg_denoise_step_taps(dg_model *m, const int32_t *x_t, const void *z_t,
   if (taps && taps->p0 && !taps->lse)
     return fail(DG_ERR_INVALID_ARG, "taps->p0 requires taps->lse");
   if (taps && bf16) {
-    const void *tp[6] = {taps->h0, taps->q, taps->k, taps->v, taps->o, taps->h1};
+    const void *tp[7] = {taps->h0, taps->q, taps->k, taps->v, taps->o, taps->h1, taps->p0E};
     for (const void *p : tp)
       if (p && !aligned16(p)) return fail(DG_ERR_INVALID_ARG, "bf16 taps must be 16-byte aligned");
   }
@@ -514,6 +559,78 @@ dg_status dg_denoise_step_taps(dg_model *m, const int32_t *x_t, const void *z_t,
     if (dg_status e = upload_params(m, m->prm, prm, st)) return e;
   return run_step(m, x_t, z_t, K_pre, V_pre, m->prm, prm.data(), n_inline, seed, x_out, z_out,
                   taps, taps ? taps->lse : nullptr, taps ? taps->p0 : nullptr, st);
+}
+
+dg_status dg_set_ffw(dg_model *m, int32_t hidden, const void *W_gate, const void *W_up,
+                     const void *W_down) {
+  g_err.clear();
+  if (dg_status s = check_model(m)) return s;
+  const dg::Shape &s = m->s;
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  if (hidden < 0) return fail(DG_ERR_INVALID_ARG, "hidden must be >= 0 (got %d)", hidden);
+  if (hidden > 0) {
+    if (!W_gate || !W_up || !W_down) return fail(DG_ERR_INVALID_ARG, "a feed-forward weight pointer is NULL");
+    if (!aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down))
+      return fail(DG_ERR_INVALID_ARG, "feed-forward weight pointers must be 16-byte aligned");
+    if (static_cast<int64_t>(s.R()) * hidden >= (int64_t(1) << 31) ||
+        static_cast<int64_t>(hidden) * s.d >= (int64_t(1) << 31))
+      return fail(DG_ERR_INVALID_ARG, "B*C*hidden and hidden*d must be < 2^31");
+    if (bf16 && (hidden % 64 != 0 || s.d % 64 != 0))
+      return fail(DG_ERR_UNSUPPORTED, "the bf16 feed-forward kernels need hidden %% 64 == 0 (got %d)", hidden);
+  }
+  // queued steps may still read the old block
+  DG_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize");
+  if (m->ffw_mem) {
+    DG_HIP(hipFree(m->ffw_mem), "hipFree");
+    m->ffw_mem = nullptr;
+  }
+  m->ffw_F = 0;
+  m->ffw_wg = m->ffw_wu = m->ffw_wd = nullptr;
+  m->ffw_gu = m->ffw_u = m->ffw_hid = nullptr;
+  if (hidden == 0) return DG_OK;
+
+  const size_t es = bf16 ? 2 : 4;
+  const size_t R = static_cast<size_t>(s.R()), F = static_cast<size_t>(hidden), d = static_cast<size_t>(s.d);
+  const size_t n_gu = bf16 ? align_up(2 * F * d * es) : 0;
+  const size_t n_u = align_up(R * d * es), n_hid = align_up(R * F * es);
+  char *mem = nullptr;
+  hipError_t e = hipMalloc(&mem, n_gu + n_u + n_hid);
+  if (e != hipSuccess)
+    return fail(DG_ERR_OOM, "feed-forward buffers of %zu bytes: %s", n_gu + n_u + n_hid, hipGetErrorString(e));
+  if (bf16) {
+    // gate/up rows interleaved in groups of 32: rows 64 j + [0, 32) are gate
+    // rows 32 j + [0, 32), rows 64 j + 32 + [0, 32) the up rows of the same units
+    const size_t grp = 32 * d * es;
+    e = hipMemcpy2D(mem, 2 * grp, W_gate, grp, grp, F / 32, hipMemcpyDeviceToDevice);
+    if (e == hipSuccess) e = hipMemcpy2D(mem + grp, 2 * grp, W_up, grp, grp, F / 32, hipMemcpyDeviceToDevice);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      (void)hipFree(mem);
+      return hip_fail(e, "feed-forward weight packing");
+    }
+  }
+  m->ffw_mem = mem;
+  m->ffw_F = hidden;
+  m->ffw_wg = W_gate;
+  m->ffw_wu = W_up;
+  m->ffw_wd = W_down;
+  m->ffw_gu = bf16 ? mem : nullptr;
+  m->ffw_u = mem + n_gu;
+  m->ffw_hid = mem + n_gu + n_u;
+  return DG_OK;
+}
+
+dg_status dg_ffw(dg_model *m, const void *u, void *z_out, void *stream) {
+  g_err.clear();
+  if (dg_status s = check_model(m)) return s;
+  if (!m->ffw_F) return fail(DG_ERR_INVALID_ARG, "no feed-forward block is attached (dg_set_ffw)");
+  if (!u || !z_out) return fail(DG_ERR_INVALID_ARG, "u and z_out must be non-NULL");
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  const size_t nz = static_cast<size_t>(m->s.R()) * m->s.d * (bf16 ? 2 : 4);
+  if (overlap(u, nz, z_out, nz)) return fail(DG_ERR_INVALID_ARG, "z_out overlaps u");
+  if (bf16 && (!aligned16(u) || !aligned16(z_out)))
+    return fail(DG_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+  return run_ffw(m, u, z_out, nullptr, nullptr, static_cast<hipStream_t>(stream));
 }
 
 dg_status dg_denoise_step(dg_model *m, const int32_t *x_t, const void *z_t, const void *K_pre,

@@ -94,6 +94,13 @@ __device__ __forceinline__ uint32_t gumbel_block_of(int v) {
 }
 __device__ __forceinline__ int gumbel_word_of(int v) { return (v >> 4) & 3; }
 
+// GELU in its tanh form, a/2 (1 + tanh(sqrt(2/pi) (a + 0.044715 a^3))), the
+// activation of the gated self-conditioning block.
+__device__ __forceinline__ float gelu_tanh(float a) {
+  constexpr float kC = 0.7978845608028654f;   // sqrt(2 / pi)
+  return 0.5f * a * (1.f + tanhf(kC * fmaf(0.044715f * a, a * a, a)));
+}
+
 // ------------------------------------------------------ small reductions ---
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -70,6 +70,19 @@ hipError_t launch_qkv_bf16(const uint16_t *h0, const uint16_t *Wq, const uint16_
 hipError_t launch_oproj_bf16(const uint16_t *o, const uint16_t *Wo, const uint16_t *h0,
                              const Shape &s, uint16_t *h1, hipStream_t st);
 
+// ---- gated self-conditioning block z = FFW(u) (k_gemm.hip bf16 MFMA) ----
+// hid [M, F] = round(gelu(u Wg^T) * (u Wu^T)) from the packed gate/up matrix
+// Wgu [2F, d] (rows 64 j + [0, 32): gate rows 32 j + [0, 32); rows
+// 64 j + 32 + [0, 32): the up rows of the same units). Needs d % 64 == 0 and
+// F % 32 == 0 (hipErrorInvalidValue otherwise).
+hipError_t launch_ffw_gate_up_bf16(const uint16_t *u, const uint16_t *Wgu, int M, int d, int F,
+                                   uint16_t *hid, hipStream_t st);
+// z [M, d] = hid Wd^T, Wd [d, F]; rows m of canvases m / C marked in `frozen`
+// (nullable) copy z_t. Needs F % 64 == 0 and d % 64 == 0.
+hipError_t launch_ffw_down_bf16(const uint16_t *hid, const uint16_t *Wd, int M, int d, int F, int C,
+                                const int32_t *frozen, const uint16_t *z_t, uint16_t *z,
+                                hipStream_t st);
+
 // ---- k_attention.hip (bf16 MFMA) ----
 int attention_splits(const Shape &s);
 size_t attention_workspace_bytes(const Shape &s);
@@ -97,6 +110,10 @@ hipError_t launch_attention_f32(const float *q, const float *k, const float *v, 
 hipError_t launch_oproj_f32(const float *o, const float *Wo, const float *h0, const Shape &s,
                             float *h1, hipStream_t st);
 size_t lmhead_f32_workspace_bytes(const Shape &s);
+hipError_t launch_ffw_gate_up_f32(const float *u, const float *Wg, const float *Wu, int M, int d,
+                                  int F, float *hid, hipStream_t st);
+hipError_t launch_ffw_down_f32(const float *hid, const float *Wd, int M, int d, int F, int C,
+                               const int32_t *frozen, const float *z_t, float *z, hipStream_t st);
 hipError_t launch_lmhead_f32(const float *h1, const float *E, const StepParams *prm,
                              const Shape &s, uint64_t seed, void *work, float *p0, bool entropy,
                              hipStream_t st);

@@ -125,6 +125,50 @@ __global__ void __launch_bounds__(256) oproj_f32_kernel(const float *__restrict_
   }
 }
 
+// Gated self-conditioning block: hid[m, f] = gelu(u_m . Wg_f) * (u_m . Wu_f).
+__global__ void __launch_bounds__(256) ffw_gate_up_f32_kernel(const float *__restrict__ u,
+                                                              const float *__restrict__ Wg,
+                                                              const float *__restrict__ Wu, int R,
+                                                              int d, int F, float *__restrict__ hid) {
+  const int64_t total = static_cast<int64_t>(R) * F;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int m = static_cast<int>(idx / F), f = static_cast<int>(idx - static_cast<int64_t>(m) * F);
+    const float *x = u + static_cast<int64_t>(m) * d;
+    const float *wg = Wg + static_cast<int64_t>(f) * d;
+    const float *wu = Wu + static_cast<int64_t>(f) * d;
+    float g = 0.f, v = 0.f;
+    for (int c = 0; c < d; ++c) {
+      g = fmaf(x[c], wg[c], g);
+      v = fmaf(x[c], wu[c], v);
+    }
+    hid[idx] = gelu_tanh(g) * v;
+  }
+}
+
+// z[m, n] = hid_m . Wd_n; rows of canvases marked in `frozen` copy z_t.
+__global__ void __launch_bounds__(256) ffw_down_f32_kernel(const float *__restrict__ hid,
+                                                           const float *__restrict__ Wd, int R, int d,
+                                                           int F, int C,
+                                                           const int32_t *__restrict__ frozen,
+                                                           const float *__restrict__ zt,
+                                                           float *__restrict__ z) {
+  const int64_t total = static_cast<int64_t>(R) * d;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int m = static_cast<int>(idx / d), n = static_cast<int>(idx - static_cast<int64_t>(m) * d);
+    if (frozen && frozen[m / C]) {
+      z[idx] = zt[idx];
+      continue;
+    }
+    const float *x = hid + static_cast<int64_t>(m) * F;
+    const float *w = Wd + static_cast<int64_t>(n) * F;
+    float acc = 0.f;
+    for (int c = 0; c < F; ++c) acc = fmaf(x[c], w[c], acc);
+    z[idx] = acc;
+  }
+}
+
 // LM head for one row per block, vocabulary in chunks of 256: scaled logits,
 // online max / sum (log2 units, rescaled every chunk), Gumbel argmax for a
 // resampling row, z accumulated by the threads that own its columns.
@@ -295,6 +339,28 @@ hipError_t launch_oproj_f32(const float *o, const float *Wo, const float *h0, co
   if (blocks > 16384) blocks = 16384;
   hipLaunchKernelGGL(oproj_f32_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, o,
                      Wo, h0, s.R(), s.d, s.Hq * s.hd, h1);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffw_gate_up_f32(const float *u, const float *Wg, const float *Wu, int M, int d,
+                                  int F, float *hid, hipStream_t st) {
+  const int64_t total = static_cast<int64_t>(M) * F;
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(ffw_gate_up_f32_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, u,
+                     Wg, Wu, M, d, F, hid);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffw_down_f32(const float *hid, const float *Wd, int M, int d, int F, int C,
+                               const int32_t *frozen, const float *z_t, float *z, hipStream_t st) {
+  const int64_t total = static_cast<int64_t>(M) * d;
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(ffw_down_f32_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, hid,
+                     Wd, M, d, F, C, frozen, z_t, z);
   return hipGetLastError();
 }
 

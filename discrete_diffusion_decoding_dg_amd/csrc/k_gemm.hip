@@ -1,6 +1,8 @@
-// bf16 MFMA GEMMs of the decoder block: the fused q/k/v projection and the
-// output projection with the residual add. Both are C = A B^T with A [M, K]
-// and B [N, K] row-major (K contiguous in both, the layout MFMA operands want).
+// bf16 MFMA GEMMs of the decoder block: the fused q/k/v projection, the
+// output projection with the residual add, and the two halves of the gated
+// self-conditioning block (gate and up projections with the GELU product;
+// down projection). All are C = A B^T with A [M, K] and B [N, K] row-major
+// (K contiguous in both, the layout MFMA operands want).
 //
 // Tiling: 64 x 64 output tile per 256-thread block (2 x 2 waves, 32 x 32 per
 // wave via v_mfma_f32_32x32x16_bf16), K staged through LDS in 64-wide slabs,
@@ -17,7 +19,10 @@ constexpr int PAD = 8;                  // bf16 elements of row padding in LDS
 constexpr int LDW = BK + PAD;           // LDS row pitch (elements)
 
 // Where row n of the virtual B matrix comes from, and where C goes.
+// kPair: the tile's output columns come in gate/up pairs (see GegluEpi) and
+// are stored through store_pair(m, n, gate, up) instead of store(m, n, acc).
 struct QkvEpi {
+  static constexpr bool kPair = false;
   const uint16_t *Wq, *Wk, *Wv;
   uint16_t *q, *k, *v;
   int Nq, Nkv, C, Hkv, hd;
@@ -47,6 +52,7 @@ struct QkvEpi {
 };
 
 struct ResidualEpi {
+  static constexpr bool kPair = false;
   const uint16_t *W;
   const uint16_t *res;
   uint16_t *out;
@@ -55,6 +61,40 @@ struct ResidualEpi {
   __device__ void store(int m, int n, float acc) const {
     const int64_t idx = static_cast<int64_t>(m) * N + n;
     out[idx] = f32_to_bf16(bf16_to_f32(res[idx]) + acc);
+  }
+};
+
+// Gate and up projections of the self-conditioning block in one GEMM over
+// the packed matrix W [2F, K]: rows 64 j + [0, 32) are gate rows 32 j + [0, 32)
+// and rows 64 j + 32 + [0, 32) the up rows of the same hidden units, so a
+// 32-column MFMA block of gate outputs and the block of up outputs of the
+// same units sit side by side in every tile. hid[m, f] = round(gelu(g) * u).
+struct GegluEpi {
+  static constexpr bool kPair = true;
+  const uint16_t *W;
+  uint16_t *hid;
+  int F;
+  __device__ const uint16_t *brow(int n, int K) const { return W + static_cast<int64_t>(n) * K; }
+  // n: the packed column of the gate value
+  __device__ void store_pair(int m, int n, float g, float u) const {
+    const int f = (n >> 6) * 32 + (n & 31);
+    hid[static_cast<int64_t>(m) * F + f] = f32_to_bf16(gelu_tanh(g) * u);
+  }
+};
+
+// Down projection of the self-conditioning block, z = hid W^T; rows of
+// canvases marked in `frozen` (nullable) copy z_t instead.
+struct DownEpi {
+  static constexpr bool kPair = false;
+  const uint16_t *W;
+  uint16_t *out;
+  const uint16_t *zt;
+  const int32_t *frozen;
+  int N, C;
+  __device__ const uint16_t *brow(int n, int K) const { return W + static_cast<int64_t>(n) * K; }
+  __device__ void store(int m, int n, float acc) const {
+    const int64_t idx = static_cast<int64_t>(m) * N + n;
+    out[idx] = (frozen && frozen[m / C]) ? zt[idx] : f32_to_bf16(acc);
   }
 };
 
@@ -256,19 +296,46 @@ __global__ void __launch_bounds__(512) gemm_tn_bf16_dma_kernel(const uint16_t *_
     for (int i = 0; i < 16; ++i) part[i * 64 + lane] = acc[i];
   }
   __syncthreads();
-  if (wk == 1) return;
+  if constexpr (Epi::kPair) {
+    // the gate quadrant (wn = 0) and the up quadrant (wn = 1) of the same
+    // hidden units meet in LDS as well
+    if (wk == 0) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] += part[i * 64 + lane];
+      for (int i = 0; i < 16; ++i) acc[i] += part[i * 64 + lane];
+    }
+    __syncthreads();                                // `part` fully read
+    float *upv = reinterpret_cast<float *>(As) + (wm * 16) * 64;
+    if (wk == 0 && wn == 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) upv[i * 64 + lane] = acc[i];
+    }
+    __syncthreads();
+    if (wk != 0 || wn != 0) return;
+    const int n = n0 + (lane & 31);
+    if (n < N) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + wm * 32 + 8 * j + 4 * (lane >> 5) + i;
+          if (m < M) epi.store_pair(m, n, acc[4 * j + i], upv[(4 * j + i) * 64 + lane]);
+        }
+    }
+  } else {
+    if (wk == 1) return;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] += part[i * 64 + lane];
 
-  const int n = n0 + wn * 32 + (lane & 31);
-  if (n < N) {
+    const int n = n0 + wn * 32 + (lane & 31);
+    if (n < N) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm * 32 + 8 * j + 4 * (lane >> 5) + i;
-        if (m < M) epi.store(m, n, acc[4 * j + i]);
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + wm * 32 + 8 * j + 4 * (lane >> 5) + i;
+          if (m < M) epi.store(m, n, acc[4 * j + i]);
+        }
+    }
   }
 }
 
@@ -390,19 +457,36 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(const uint16_t *__restric
 
   // C layout of the 32x32 MFMA: lane holds column lane % 32 and rows
   // 8 j + 4 (lane / 32) + i in register 4 j + i
+  if constexpr (Epi::kPair) {
+    // a wave's 64 columns are one gate block (ni = 0) and the up block of
+    // the same hidden units (ni = 1): the pair meets in registers
+    const int n = n0 + wn * 64 + (lane & 31);
+    if (n < N) {
 #pragma unroll
-  for (int ni = 0; ni < 2; ++ni) {
-    const int n = n0 + wn * 64 + ni * 32 + (lane & 31);
-    if (n >= N) continue;
+      for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+          for (int i = 0; i < 4; ++i) {
+            const int m = m0 + wm * 128 + mi * 32 + 8 * j + 4 * (lane >> 5) + i;
+            if (m < M) epi.store_pair(m, n, acc[mi][0][4 * j + i], acc[mi][1][4 * j + i]);
+          }
+    }
+  } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = m0 + wm * 128 + mi * 32 + 8 * j + 4 * (lane >> 5) + i;
-          if (m < M) epi.store(m, n, acc[mi][ni][4 * j + i]);
-        }
+    for (int ni = 0; ni < 2; ++ni) {
+      const int n = n0 + wn * 64 + ni * 32 + (lane & 31);
+      if (n >= N) continue;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = m0 + wm * 128 + mi * 32 + 8 * j + 4 * (lane >> 5) + i;
+            if (m < M) epi.store(m, n, acc[mi][ni][4 * j + i]);
+          }
+    }
   }
 }
 }  // namespace big
@@ -427,6 +511,37 @@ hipError_t launch_qkv_bf16(const uint16_t *h0, const uint16_t *Wq, const uint16_
     hipLaunchKernelGGL(gemm_tn_bf16_dma_kernel<QkvEpi>, grid, dim3(512), 0, st, h0, M, N, s.d, epi);
   else
     hipLaunchKernelGGL(gemm_tn_bf16_kernel<QkvEpi>, grid, dim3(256), 0, st, h0, M, N, s.d, epi);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffw_gate_up_bf16(const uint16_t *u, const uint16_t *Wgu, int M, int d, int F,
+                                   uint16_t *hid, hipStream_t st) {
+  GegluEpi epi{Wgu, hid, F};
+  const int N = 2 * F, K = d;
+  if (M == 0) return hipSuccess;
+  if (K % 64 != 0 || F % 32 != 0) return hipErrorInvalidValue;
+  if (M >= kBigRows && N % big::BNB == 0)
+    hipLaunchKernelGGL(big::gemm_big_kernel<GegluEpi>, dim3(N / big::BNB, (M + big::BMB - 1) / big::BMB),
+                       dim3(512), 0, st, u, M, N, K, epi);
+  else
+    hipLaunchKernelGGL(gemm_tn_bf16_dma_kernel<GegluEpi>, dim3(N / BN, (M + BM - 1) / BM), dim3(512), 0,
+                       st, u, M, N, K, epi);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffw_down_bf16(const uint16_t *hid, const uint16_t *Wd, int M, int d, int F, int C,
+                                const int32_t *frozen, const uint16_t *z_t, uint16_t *z,
+                                hipStream_t st) {
+  DownEpi epi{Wd, z, z_t, frozen, d, C};
+  const int N = d, K = F;
+  if (M == 0) return hipSuccess;
+  if (K % 64 != 0 || N % 64 != 0) return hipErrorInvalidValue;
+  if (M >= kBigRows && N % big::BNB == 0)
+    hipLaunchKernelGGL(big::gemm_big_kernel<DownEpi>, dim3(N / big::BNB, (M + big::BMB - 1) / big::BMB),
+                       dim3(512), 0, st, hid, M, N, K, epi);
+  else
+    hipLaunchKernelGGL(gemm_tn_bf16_dma_kernel<DownEpi>, dim3(N / BN, (M + BM - 1) / BM), dim3(512), 0,
+                       st, hid, M, N, K, epi);
   return hipGetLastError();
 }
 

@@ -13,7 +13,8 @@
  *   - tau_t anneals linearly from 0.8 to 0.4 (sampler paragraph).
  * Readings where the pages stop short: Step is the Euler step of the
  * uniform-path CTMC, (1 - lambda) delta(y, x_t) + lambda p0(y) with
- * lambda = clamp(dt (-dkappa/dt) / (1 - kappa_t), 0, 1); FFW is the identity;
+ * lambda = clamp(dt (-dkappa/dt) / (1 - kappa_t), 0, 1); FFW is the identity
+ * unless a gated feed-forward block is attached (dg_set_ffw);
  * the decoder is one residual attention block (h0 = E[x] + z; q,k,v = h0 W^T;
  * one joint unmasked softmax over [prefix ; canvas] keys, scale 1/sqrt(hd),
  * query head h reads kv head h / (Hq/Hkv); h1 = h0 + o Wo^T) with the LM head
@@ -95,11 +96,14 @@ typedef struct dg_weights {
  *   o [B,C,Hq,hd] act (attention output); h1 [B,C,d] act;
  *   lse [B,C] f32 = logsumexp_v(s_v) of the scaled logits s = (h1 E^T)/tau_b;
  *   p0 [B,C,V] f32 = exp(s - lse) (extra passes; for checking only);
- *   best [B,C] int32 = Gumbel argmax for rows that resampled, -1 for kept rows. */
+ *   best [B,C] int32 = Gumbel argmax for rows that resampled, -1 for kept rows;
+ *   p0E [B,C,d] act = p0 E, the input of the feed-forward block (written only
+ *   while a block is attached; z_out then holds FFW(p0E)). */
 typedef struct dg_taps {
   void *h0, *q, *k, *v, *o, *h1;
   float *lse, *p0;
   int32_t *best;
+  void *p0E;
 } dg_taps;
 
 typedef struct dg_model dg_model;
@@ -139,7 +143,8 @@ dg_status dg_corrupt_batch(const int32_t *x0, const float *kappa_dev, int32_t B,
  *   (the prompt KV cache H); t host [B], each in (0, 1]; dt in (0, 1];
  *   seed = the Philox key of this step.
  *   Outputs: x_out [B,C] int32 (the Step draw), z_out [B,C,d] act
- *   (z = p0 E), optional lse_out [B,C] f32, optional p0_out [B,C,V] f32
+ *   (z = FFW(p0 E): p0 E itself unless a block is attached with dg_set_ffw),
+ *   optional lse_out [B,C] f32, optional p0_out [B,C,V] f32
  *   (p0_out requires lse_out). x_out / z_out must not overlap x_t / z_t;
  *   bf16 tensors must be 16-byte aligned. The C x V logits are never written
  *   unless p0_out is given. Tokens outside [0, V) embed as a zero row. */
@@ -198,17 +203,41 @@ dg_status dg_generate_canvas_entropy(dg_model *m, const void *K_pre, const void 
                                      float eps_stop, int32_t *x_out, void *z_out,
                                      int32_t *steps_out, void *stream);
 
+/* Gated feed-forward self-conditioning block (TR summary, Method, three-line
+ * update: z = FFW(p0 E) with a standard feed-forward network; the pages give
+ * no structure, the reading here is the Gemma family's gated form):
+ *   FFW(u) = W_down (gelu(W_gate u) * (W_up u)), gelu in its tanh form
+ *   a/2 (1 + tanh(sqrt(2/pi) (a + 0.044715 a^3))), no biases, no residual;
+ *   the hidden activations are rounded to act before W_down.
+ * dg_set_ffw attaches the block to every later step and generation of the
+ * model (hidden = 0 detaches it: z = p0 E again).
+ *   W_gate, W_up [hidden, d] and W_down [d, hidden]: device pointers in act
+ *   dtype, row-major, 16-byte aligned, caller-owned and unchanged while
+ *   attached. The library allocates its own buffers for the block (the
+ *   input and hidden activations, and for bf16 a copy of W_gate and W_up
+ *   with their rows interleaved in groups of 32), freed on detach or
+ *   dg_destroy. Waits for the device before and after (set-up call).
+ *   bf16 needs hidden % 64 == 0 (DG_ERR_UNSUPPORTED); B*C*hidden and
+ *   hidden*d must be < 2^31. */
+dg_status dg_set_ffw(dg_model *m, int32_t hidden, const void *W_gate, const void *W_up,
+                     const void *W_down);
+
+/* z_out [B,C,d] act = FFW(u) for u [B,C,d] act through the attached block
+ * (DG_ERR_INVALID_ARG if none); z_out must not overlap u. */
+dg_status dg_ffw(dg_model *m, const void *u, void *z_out, void *stream);
+
 /* Per-stage GPU time of the calls made while profiling is on, measured with a
  * HIP event pair recorded on the call's stream around each stage's launches.
  * Stages: 0 embed, 1 q/k/v projection, 2 attention (+ split merge),
  * 3 output projection, 4 LM head (logits, softmax statistics, z partials,
- * Gumbel argmax), 5 split merge + Step select, 6 corruption.
+ * Gumbel argmax), 5 split merge + Step select, 6 corruption, 7 feed-forward
+ * self-conditioning block.
  * dg_profile_enable(m, mask) times the stages whose bit (1 << stage) is set
  * in mask (0 turns profiling off; every event pair adds a few microseconds of
  * queue time between kernels, so time only the stages you need).
  * dg_profile_read waits for the recorded events, returns the summed
  * milliseconds and the number of timed launches per stage, and clears them. */
-#define DG_NUM_STAGES 7
+#define DG_NUM_STAGES 8
 typedef struct dg_profile {
   double ms[DG_NUM_STAGES];
   int64_t count[DG_NUM_STAGES];
