@@ -95,7 +95,7 @@ bool lmhead_supported(const Shape &s);
 int lmhead_splits(const Shape &s);
 size_t lmhead_workspace_bytes(const Shape &s);
 // Fused LM head over V splits; writes RowPartial [splits, R] and z partials
-// [splits, R, d] fp32 into `work`, and raw scaled logits into p0 when non-null.
+// [splits, R, d] bf16 into `work`, and raw scaled logits into p0 when non-null.
 // With `entropy` every row draws (no Bernoulli) and the entropy statistics
 // of RowPartial are filled in.
 hipError_t launch_lmhead_bf16(const uint16_t *h1, const uint16_t *E, const int32_t *x_t,

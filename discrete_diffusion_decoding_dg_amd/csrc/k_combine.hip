@@ -16,6 +16,7 @@
 // Grid: (row, strip of 1024 columns). The first wave of each block merges
 // the row's split statistics (one split per lane, wave-wide max / sum /
 // argmax); then every thread streams 4 consecutive columns of all splits.
+// z partials are bf16 from the MFMA LM head and fp32 from the fp32 path.
 #include "dg_device.hpp"
 #include "dg_kernels.hpp"
 
@@ -24,9 +25,18 @@ namespace {
 
 constexpr int kMaxSplits = 64;
 
-template <typename T>
+__device__ __forceinline__ float4 load4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float4 load4(const uint16_t *p) {
+  const uint2 v = *reinterpret_cast<const uint2 *>(p);
+  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+}
+__device__ __forceinline__ float load1(const float *p) { return *p; }
+__device__ __forceinline__ float load1(const uint16_t *p) { return bf16_to_f32(*p); }
+
+template <typename T, typename ZP>
 __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restrict__ part,
-                                                      const float *__restrict__ zpart, int splits,
+                                                      const ZP *__restrict__ zpart, int splits,
                                                       const int32_t *__restrict__ x_t,
                                                       const StepParams *__restrict__ prm, int R,
                                                       int C, int d, uint32_t k0, uint32_t k1,
@@ -115,11 +125,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restri
   const int64_t rowoff = static_cast<int64_t>(r) * d;
   if (c0 + 4 <= d && (d & 3) == 0) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float *zp = zpart + rowoff + c0;
+    const ZP *zp = zpart + rowoff + c0;
     const int64_t sstride = static_cast<int64_t>(R) * d;
 #pragma unroll 8
     for (int s = 0; s < splits; ++s) {
-      const float4 v = *reinterpret_cast<const float4 *>(zp + s * sstride);
+      const float4 v = load4(zp + s * sstride);
       const float w = wsh[s];
       acc.x += w * v.x;
       acc.y += w * v.y;
@@ -134,7 +144,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restri
     for (int c = c0; c < d && c < c0 + 4; ++c) {
       float acc = 0.f;
       for (int s = 0; s < splits; ++s)
-        acc += wsh[s] * zpart[(static_cast<int64_t>(s) * R + r) * d + c];
+        acc += wsh[s] * load1(zpart + (static_cast<int64_t>(s) * R + r) * d + c);
       Act<T>::store(z_out, rowoff + c, acc * il);
     }
   }
@@ -150,18 +160,19 @@ hipError_t launch_combine(bool bf16, const void *work, int splits, const int32_t
   if (R == 0) return hipSuccess;
   if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
   const RowPartial *part = static_cast<const RowPartial *>(work);
-  const float *zpart = reinterpret_cast<const float *>(static_cast<const char *>(work) +
-                                                       static_cast<size_t>(splits) * R * sizeof(RowPartial));
+  const char *zbase = static_cast<const char *>(work) + static_cast<size_t>(splits) * R * sizeof(RowPartial);
   const uint32_t k0 = static_cast<uint32_t>(seed), k1 = static_cast<uint32_t>(seed >> 32);
   const dim3 grid(R, (s.d + 1023) / 1024);
   const EntropyRows er = ent ? *ent : EntropyRows{nullptr, nullptr, nullptr};
   if (frozen && !z_t) return hipErrorInvalidValue;
   if (bf16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, st, part, zpart, splits,
+    hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st, part,
+                       reinterpret_cast<const uint16_t *>(zbase), splits,
                        x_t, prm, R, s.C, s.d, k0, k1, x_out, static_cast<uint16_t *>(z_out), lse,
                        best, er, frozen, static_cast<const uint16_t *>(z_t));
   else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, st, part, zpart, splits, x_t,
+    hipLaunchKernelGGL((combine_kernel<float, float>), grid, dim3(256), 0, st, part,
+                       reinterpret_cast<const float *>(zbase), splits, x_t,
                        prm, R, s.C, s.d, k0, k1, x_out, static_cast<float *>(z_out), lse, best,
                        er, frozen, static_cast<const float *>(z_t));
   return hipGetLastError();

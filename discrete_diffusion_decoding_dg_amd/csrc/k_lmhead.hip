@@ -56,7 +56,7 @@ struct LmArgs {
   const int32_t *x_t;
   const StepParams *prm;
   RowPartial *part;   // [splits][R]
-  float *zpart;       // [splits][R][d]
+  uint16_t *zpart;    // [splits][R][d] bf16: the split's sum of p E
   float *p0;          // optional [R][V] raw scaled logits
   int R, C, d, V, splits, tiles_per_split;
   uint32_t k0, k1;
@@ -475,7 +475,9 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
       a.part[static_cast<int64_t>(split) * a.R + grow] = p;
     }
   }
-  float *zs = a.zpart + static_cast<int64_t>(split) * a.R * a.d;
+  // z partials travel in bf16: each is rescaled and summed in fp32 by the
+  // merge, and the result is rounded to bf16 anyway; half the bytes of fp32
+  uint16_t *zs = a.zpart + static_cast<int64_t>(split) * a.R * a.d;
   if constexpr (MT == 32) {
     // accumulator element 4 jj + i: row 8 jj + 4 (lane >> 5) + i, column lane & 31
 #pragma unroll
@@ -484,9 +486,9 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
       for (int i = 0; i < 4; ++i) {
         const int r = row0 + 8 * jj + 4 * (lane >> 5) + i;
         if (r >= a.R) continue;
-        float *zr = zs + static_cast<int64_t>(r) * a.d + dcol0 + (lane & 31);
+        uint16_t *zr = zs + static_cast<int64_t>(r) * a.d + dcol0 + (lane & 31);
 #pragma unroll
-        for (int c = 0; c < NKS; ++c) zr[32 * c] = zacc[c][4 * jj + i];
+        for (int c = 0; c < NKS; ++c) zr[32 * c] = f32_to_bf16(zacc[c][4 * jj + i]);
       }
   } else {
     // accumulator element i: row 4 (lane >> 4) + i, column lane & 15
@@ -494,9 +496,9 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
     for (int i = 0; i < 4; ++i) {
       const int r = row0 + 4 * (lane >> 4) + i;
       if (r >= a.R) continue;
-      float *zr = zs + static_cast<int64_t>(r) * a.d + dcol0 + (lane & 15);
+      uint16_t *zr = zs + static_cast<int64_t>(r) * a.d + dcol0 + (lane & 15);
 #pragma unroll
-      for (int n = 0; n < NZ; ++n) zr[16 * n] = zacc[n][i];
+      for (int n = 0; n < NZ; ++n) zr[16 * n] = f32_to_bf16(zacc[n][i]);
     }
   }
 }
@@ -545,7 +547,7 @@ size_t lmhead_workspace_bytes(const Shape &s) {
   Plan p;
   if (!plan(s, p)) return 0;
   const size_t R = static_cast<size_t>(s.R());
-  return p.splits * R * (sizeof(RowPartial) + static_cast<size_t>(s.d) * sizeof(float));
+  return p.splits * R * (sizeof(RowPartial) + static_cast<size_t>(s.d) * sizeof(uint16_t));
 }
 
 hipError_t launch_lmhead_bf16(const uint16_t *h1, const uint16_t *E, const int32_t *x_t,
@@ -560,7 +562,7 @@ hipError_t launch_lmhead_bf16(const uint16_t *h1, const uint16_t *E, const int32
   a.splits = p.splits; a.tiles_per_split = p.tps;
   a.k0 = static_cast<uint32_t>(seed); a.k1 = static_cast<uint32_t>(seed >> 32);
   a.part = static_cast<RowPartial *>(work);
-  a.zpart = reinterpret_cast<float *>(static_cast<char *>(work) +
+  a.zpart = reinterpret_cast<uint16_t *>(static_cast<char *>(work) +
                                       static_cast<size_t>(p.splits) * s.R() * sizeof(RowPartial));
   const int rblocks = (s.R() + p.MT - 1) / p.MT;
   const dim3 grid(rblocks * p.splits);
