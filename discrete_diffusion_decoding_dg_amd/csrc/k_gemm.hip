@@ -4,10 +4,15 @@
 // down projection). All are C = A B^T with A [M, K] and B [N, K] row-major
 // (K contiguous in both, the layout MFMA operands want).
 //
-// Tiling: 64 x 64 output tile per 256-thread block (2 x 2 waves, 32 x 32 per
-// wave via v_mfma_f32_32x32x16_bf16), K staged through LDS in 64-wide slabs,
-// double-buffered: the next slab is fetched into registers while the current
-// one feeds the matrix cores.
+// Kernels, by row count (all v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+//   - rows >= 2048 (batched canvases): 256 x 256 tiles, K in 32-wide slabs
+//     through four LDS stages (big::);
+//   - fewer rows with K % 128 == 0: 64 x 64 or 64 x 32 tiles, K in 128-wide
+//     slabs, the eight waves splitting K (skinny::);
+//   - K % 64 == 0 otherwise: 64 x 64 tiles, 64-wide slabs, nine stages;
+//   - anything else: 64 x 64 tiles, register double buffering.
+// Operand slabs reach LDS through direct global->LDS loads except in the
+// last kernel.
 #include "dg_device.hpp"
 #include "dg_kernels.hpp"
 
@@ -491,6 +496,162 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(const uint16_t *__restric
 }
 }  // namespace big
 
+// ---------------------------------------------------------------------------
+// Few-row variant (up to a couple of thousand rows: one canvas, or a few):
+// 64 x BN output tile per block, the chip filled by N / BN x M / 64 tiles.
+// K streams through LDS in 128-wide slabs (direct global->LDS loads, whole
+// 256-byte row segments), and the eight waves split each slab by K instead
+// of splitting the tile: wave w multiplies k-step w (16 wide) of every slab
+// for the whole 64 x BN tile, so each element staged in LDS is read exactly
+// once. The eight partial tiles meet once, through LDS, at the end.
+namespace skinny {
+constexpr int BM = 64, BK = 128;
+constexpr int PITCH64 = 72, PITCH32 = 40;   // LDS row pitch (floats) of a wave's partial tile:
+                                            // rows 4 apart fall 32 banks apart
+
+// slab row r (256 bytes, 16 pieces of 8 elements): logical piece p sits at
+// physical piece p ^ (r & 15), which keeps the 16-row operand reads of one
+// k-step on 16 distinct pieces (all 64 banks)
+__device__ __forceinline__ int sk_off(int r, int p) { return r * BK + ((p ^ (r & 15)) << 3); }
+
+template <int BN>
+struct Cfg {
+  static constexpr int NS = BN == 64 ? 4 : 5;                 // slab stages
+  static constexpr int STAGE = (BM + BN) * BK;                // elements per stage
+  static constexpr int PITCH = BN == 64 ? PITCH64 : PITCH32;
+  static constexpr int RED = 8 * BM * PITCH * 4;              // bytes of the partial-tile buffer
+  static constexpr int LDS = (NS * STAGE * 2 > RED) ? NS * STAGE * 2 : RED;
+  static constexpr int DMA = (BM + BN) / 32;                  // direct loads per wave and slab
+};
+
+template <class Epi, int BN>
+__global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__restrict__ A, int M,
+                                                          int N, int K, Epi epi) {
+  using G = Cfg<BN>;
+  constexpr int NR = BN / 32;                       // 32-column blocks per tile
+  constexpr int NS = G::NS, PITCH = G::PITCH;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[G::LDS / 2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // XCD-aware order (block b runs on XCD b % 8): consecutive tiles in the
+  // regrouped order share an XCD, and row tiles run fastest, so the blocks
+  // that read the same weight rows share that XCD's L2
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int mt = (M + BM - 1) / BM;
+  const int tn = bid / mt, tm = bid - tn * mt;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // loads: one direct load fills 4 slab rows (1 KB); the slab's A rows and
+  // then its B rows are dealt to the waves, G::DMA loads each. Lane i fills
+  // row 4 g + i / 16 at physical piece i % 16. Rows past M (N) re-read the
+  // last valid row; their results are never stored.
+  const uint16_t *src[G::DMA];
+  int dst[G::DMA];
+#pragma unroll
+  for (int j = 0; j < G::DMA; ++j) {
+    const int g = wave * G::DMA + j;                // load index within the slab
+    const int r = 4 * g + (lane >> 4);              // slab row, A rows first
+    const int lp = (lane & 15) ^ (r & 15);          // logical piece this lane fetches
+    if (r < BM) {
+      const int m = (m0 + r < M) ? m0 + r : M - 1;
+      src[j] = A + static_cast<int64_t>(m) * K + 8 * lp;
+    } else {
+      const int n = (n0 + r - BM < N) ? n0 + r - BM : N - 1;
+      src[j] = epi.brow(n, K) + 8 * lp;
+    }
+    dst[j] = 4 * g * BK;                            // element offset of the load within a stage
+  }
+  auto issue = [&](int it) {
+    uint16_t *stage = smem + (it % NS) * G::STAGE;
+#pragma unroll
+    for (int j = 0; j < G::DMA; ++j) big::dma16_va(src[j] + it * BK, stage + dst[j]);
+  };
+  const int nk = K / BK;
+  for (int it = 0; it < NS - 1 && it < nk; ++it) issue(it);
+
+  f32x16 acc[2][NR];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NR; ++j) acc[i][j] = f32x16{};
+  const int p = 2 * wave + (lane >> 5);             // logical piece of this lane's k-step half
+  for (int it = 0; it < nk; ++it) {
+    int younger = nk - 1 - it;                      // slabs issued after this one
+    if (younger > NS - 2) younger = NS - 2;
+    vm_wait_steps<G::DMA, NS - 2>(younger);
+    __syncthreads();                                // every wave's part of slab `it` landed
+    if (it + NS - 1 < nk) issue(it + NS - 1);       // refill the stage every wave finished reading
+    const uint16_t *as = smem + (it % NS) * G::STAGE;
+    const uint16_t *bs = as + BM * BK;
+    bf16x8 a[2], b[NR];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(as + sk_off(32 * i + (lane & 31), p));
+#pragma unroll
+    for (int j = 0; j < NR; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(bs + sk_off(32 * j + (lane & 31), p));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < NR; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+
+  // the eight partial tiles meet in LDS (the stages are free once everyone is
+  // here); MFMA C layout: lane holds column lane % 32 of each 32-column block
+  // and rows 8 q + 4 (lane / 32) + e in register 4 q + e
+  __syncthreads();
+  float *red = reinterpret_cast<float *>(smem);
+  float *mine = red + wave * BM * PITCH;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NR; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          mine[(32 * i + 8 * q + 4 * (lane >> 5) + e) * PITCH + 32 * j + (lane & 31)] = acc[i][j][4 * q + e];
+  __syncthreads();
+  auto sum8 = [&](int r, int col) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) s += red[w * BM * PITCH + r * PITCH + col];
+    return s;
+  };
+  if constexpr (Epi::kPair) {
+    // columns [0, 32) of the tile are gate values, [32, 64) the up values of the same units
+    static_assert(BN == 64, "gate/up pairs need 64-column tiles");
+    for (int e = tid; e < BM * 32; e += 512) {
+      const int r = e >> 5, col = e & 31;
+      const int m = m0 + r, n = n0 + col;
+      if (m < M && n < N) epi.store_pair(m, n, sum8(r, col), sum8(r, col + 32));
+    }
+  } else {
+    for (int e = tid; e < BM * BN; e += 512) {
+      const int r = e / BN, col = e - r * BN;
+      const int m = m0 + r, n = n0 + col;
+      if (m < M && n < N) epi.store(m, n, sum8(r, col));
+    }
+  }
+}
+
+// 64-column tiles (fewest operand bytes per output) once they cover most of
+// the 256 CUs, 32-column ones below that (twice the tiles). K % 128 == 0.
+template <class Epi>
+hipError_t launch(const uint16_t *A, int M, int N, int K, const Epi &epi, hipStream_t st) {
+  const int mt = (M + BM - 1) / BM;
+  if (Epi::kPair || static_cast<int64_t>(mt) * ((N + 63) / 64) >= 160) {
+    const int blocks = mt * ((N + 63) / 64);
+    hipLaunchKernelGGL((gemm_skinny_kernel<Epi, 64>), dim3(blocks), dim3(512), 0, st, A, M, N, K, epi);
+  } else if constexpr (!Epi::kPair) {
+    const int blocks = mt * ((N + 31) / 32);
+    hipLaunchKernelGGL((gemm_skinny_kernel<Epi, 32>), dim3(blocks), dim3(512), 0, st, A, M, N, K, epi);
+  }
+  return hipGetLastError();
+}
+}  // namespace skinny
+
 }  // namespace
 
 // below this many rows the 256-row tiles would leave most of the chip idle
@@ -507,6 +668,8 @@ hipError_t launch_qkv_bf16(const uint16_t *h0, const uint16_t *Wq, const uint16_
       (s.Hkv * s.hd) % big::BNB == 0)
     hipLaunchKernelGGL(big::gemm_big_kernel<QkvEpi>, dim3(N / big::BNB, (M + big::BMB - 1) / big::BMB),
                        dim3(512), 0, st, h0, M, N, s.d, epi);
+  else if (s.d % skinny::BK == 0)
+    return skinny::launch(h0, M, N, s.d, epi, st);
   else if (s.d % 64 == 0 && (s.Hq * s.hd) % 64 == 0 && (s.Hkv * s.hd) % 64 == 0)
     hipLaunchKernelGGL(gemm_tn_bf16_dma_kernel<QkvEpi>, grid, dim3(512), 0, st, h0, M, N, s.d, epi);
   else
@@ -523,6 +686,8 @@ hipError_t launch_ffw_gate_up_bf16(const uint16_t *u, const uint16_t *Wgu, int M
   if (M >= kBigRows && N % big::BNB == 0)
     hipLaunchKernelGGL(big::gemm_big_kernel<GegluEpi>, dim3(N / big::BNB, (M + big::BMB - 1) / big::BMB),
                        dim3(512), 0, st, u, M, N, K, epi);
+  else if (K % skinny::BK == 0)
+    return skinny::launch(u, M, N, K, epi, st);
   else
     hipLaunchKernelGGL(gemm_tn_bf16_dma_kernel<GegluEpi>, dim3(N / BN, (M + BM - 1) / BM), dim3(512), 0,
                        st, u, M, N, K, epi);
@@ -539,6 +704,8 @@ hipError_t launch_ffw_down_bf16(const uint16_t *hid, const uint16_t *Wd, int M, 
   if (M >= kBigRows && N % big::BNB == 0)
     hipLaunchKernelGGL(big::gemm_big_kernel<DownEpi>, dim3(N / big::BNB, (M + big::BMB - 1) / big::BMB),
                        dim3(512), 0, st, hid, M, N, K, epi);
+  else if (K % skinny::BK == 0)
+    return skinny::launch(hid, M, N, K, epi, st);
   else
     hipLaunchKernelGGL(gemm_tn_bf16_dma_kernel<DownEpi>, dim3(N / BN, (M + BM - 1) / BM), dim3(512), 0,
                        st, hid, M, N, K, epi);
@@ -554,6 +721,8 @@ hipError_t launch_oproj_bf16(const uint16_t *o, const uint16_t *Wo, const uint16
   if (M >= kBigRows && K % big::BKB == 0 && N % big::BNB == 0)
     hipLaunchKernelGGL(big::gemm_big_kernel<ResidualEpi>, dim3(N / big::BNB, (M + big::BMB - 1) / big::BMB),
                        dim3(512), 0, st, o, M, N, K, epi);
+  else if (K % skinny::BK == 0)
+    return skinny::launch(o, M, N, K, epi, st);
   else if (K % 64 == 0)
     hipLaunchKernelGGL(gemm_tn_bf16_dma_kernel<ResidualEpi>, grid, dim3(512), 0, st, o, M, N, K, epi);
   else
