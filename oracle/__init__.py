@@ -15,7 +15,10 @@ It follows the DiffusionGemma Technical Report as summarised on hyper.ai
     x_{t-dt} ~ Step(x_t, p0);
   * sampler paragraph: tau anneals linearly from 0.8 to 0.4; the
     entropy-bounded acceptance, uniform re-noising and adaptive stopping of
-    the recommended sampler (entropy.py).
+    the recommended sampler (entropy.py);
+  * block-autoregressive paragraph and pipeline figure: prompt prefill,
+    canvas commit to the KV cache and canvas-by-canvas generation
+    (blocks.py).
 
 Readings taken where the pages stop short (each documented where used):
 Step is the Euler step of the uniform-path CTMC,
@@ -43,6 +46,7 @@ from .sampling import bernoulli_uniforms, gumbel_noise, step_select
 from .corrupt import corrupt
 from .step import denoise_step, generate_canvas, self_condition
 from .ffw import gelu_tanh, ffw, ffw_hidden
+from .blocks import encode_kv, generate_blocks
 from .entropy import (row_entropy, accept_mask, renoise_tokens, entropy_step,
                       generate_canvas_entropy)
 
@@ -52,5 +56,5 @@ __all__ = [
     "qkv_proj", "attention", "out_proj", "lm_head", "bernoulli_uniforms", "gumbel_noise",
     "step_select", "corrupt", "denoise_step", "generate_canvas", "row_entropy", "accept_mask",
     "renoise_tokens", "entropy_step", "generate_canvas_entropy", "self_condition", "gelu_tanh",
-    "ffw", "ffw_hidden",
+    "ffw", "ffw_hidden", "encode_kv", "generate_blocks",
 ]
