@@ -33,8 +33,8 @@ class dg_taps(ctypes.Structure):
                 ("p0E", ctypes.c_void_p)]
 
 
-NUM_STAGES = 8
-STAGES = ["embed", "qkv", "attention", "oproj", "lmhead", "combine", "corrupt", "ffw"]
+NUM_STAGES = 9
+STAGES = ["embed", "qkv", "attention", "oproj", "lmhead", "combine", "corrupt", "ffw", "encode"]
 
 
 class dg_profile(ctypes.Structure):
@@ -44,6 +44,7 @@ class dg_profile(ctypes.Structure):
 EXPORTS = ["dg_create", "dg_destroy", "dg_workspace_bytes", "dg_corrupt", "dg_corrupt_batch",
            "dg_denoise_step", "dg_denoise_step_taps", "dg_generate_canvas",
            "dg_denoise_step_entropy", "dg_generate_canvas_entropy", "dg_set_ffw", "dg_ffw",
+           "dg_encode_kv", "dg_generate_blocks",
            "dg_profile_enable",
            "dg_profile_read", "dg_status_string", "dg_last_error"]
 
@@ -78,6 +79,8 @@ def load_library():
     lib.dg_denoise_step_entropy.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(f32), u64, f32, f32,
                                             vp, vp, vp, vp, vp, vp, vp]
     lib.dg_generate_canvas_entropy.argtypes = [vp, vp, vp, i32, u64, f32, f32, vp, vp, vp, vp]
+    lib.dg_encode_kv.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+    lib.dg_generate_blocks.argtypes = [vp, vp, vp, i32, i32, i32, u64, vp, vp]
     lib.dg_set_ffw.argtypes = [vp, i32, vp, vp, vp]
     lib.dg_ffw.argtypes = [vp, vp, vp, vp]
     lib.dg_profile_enable.argtypes = [vp, ctypes.c_int]
@@ -223,6 +226,18 @@ def dg_generate_canvas_entropy(model, K_pre, V_pre, max_steps, seed, eps_accept,
                                                      int(max_steps), int(seed), float(eps_accept),
                                                      float(eps_stop), _ptr(x_out), _ptr(z_out),
                                                      _ptr(steps_out), _stream(stream)))
+
+
+def dg_encode_kv(model, tokens, pos, K_cache, V_cache, stream=None):
+    """Encoder cache entries of tokens [B, n] into rows [pos, pos + n) of the caches."""
+    _check(load_library().dg_encode_kv(model.handle, _ptr(tokens), int(tokens.shape[1]), int(pos),
+                                       _ptr(K_cache), _ptr(V_cache), _stream(stream)))
+
+
+def dg_generate_blocks(model, K_cache, V_cache, P0, n_canvases, steps, seed, x_out, stream=None):
+    _check(load_library().dg_generate_blocks(model.handle, _ptr(K_cache), _ptr(V_cache), int(P0),
+                                             int(n_canvases), int(steps), int(seed), _ptr(x_out),
+                                             _stream(stream)))
 
 
 def dg_set_ffw(model, W_gate=None, W_up=None, W_down=None):

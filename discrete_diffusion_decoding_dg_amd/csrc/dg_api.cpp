@@ -56,7 +56,7 @@ dg::Shape shape_of(const dg_config &c) {
 
 // Workspace layout, in carve order.
 struct Layout {
-  size_t h0, q, k, v, o, h1, attn, lm, prm, kappa, genx, genz, ent, gendet, flags, total;
+  size_t h0, q, k, v, o, h1, attn, lm, prm, kappa, genx, genz, ent, gendet, flags, blkx, total;
 };
 
 Layout layout_of(const dg_config &c) {
@@ -71,7 +71,17 @@ Layout layout_of(const dg_config &c) {
   L.o = L.q;
   L.h1 = L.h0;
   if (c.dtype == DG_DTYPE_BF16) {
-    L.attn = align_up(dg::attention_workspace_bytes(s));
+    // attention partials for any prefix length up to P (block generation
+    // attends to a growing prefix; the split count is not monotone in it)
+    size_t attn = 0;
+    dg::Shape sp = s;
+    for (int p = 0;; p += 64) {
+      sp.P = p < s.P ? p : s.P;
+      const size_t a = dg::attention_workspace_bytes(sp);
+      if (a > attn) attn = a;
+      if (sp.P == s.P) break;
+    }
+    L.attn = align_up(attn);
     L.lm = align_up(dg::lmhead_workspace_bytes(s));
   } else {
     L.attn = 0;
@@ -84,8 +94,9 @@ Layout layout_of(const dg_config &c) {
   L.ent = align_up(3 * R * sizeof(int32_t));        // entropy step: H, draw, argmax per row
   L.gendet = align_up(2 * R * sizeof(int32_t));     // generation: argmax predictions, ping-pong
   L.flags = align_up(2 * static_cast<size_t>(s.B) * sizeof(int32_t));   // stopped, stop
+  L.blkx = align_up(R * sizeof(int32_t));           // block generation: the canvas being committed
   L.total = L.h0 + L.q + L.k + L.v + L.o + L.h1 + L.attn + L.lm + L.prm + L.kappa + L.genx + L.genz +
-            L.ent + L.gendet + L.flags;
+            L.ent + L.gendet + L.flags + L.blkx;
   return L;
 }
 
@@ -168,6 +179,7 @@ struct dg_model {
   dg::EntropyRows ent;      // per-row entropy-step results
   int32_t *gendet;          // [2][R] argmax predictions during generation
   int32_t *stopped, *stopbuf;   // [B] each
+  int32_t *blkx;                // [B, C] canvas being committed (block generation)
   int32_t *host_stopped = nullptr;   // pinned [B], allocated on first use
   // gated self-conditioning block (dg_set_ffw); ffw_F == 0 is the identity
   int ffw_F = 0;
@@ -241,8 +253,15 @@ dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void 
                    const void *Vp, dg::StepParams *prm, const dg::StepParams *inline_prm,
                    int n_inline, uint64_t seed, int32_t *x_out, void *z_out,
                    const dg_taps *taps, float *lse, float *p0, hipStream_t st,
-                   const dg::EntropyRows *ent = nullptr, const int32_t *frozen = nullptr) {
+                   const dg::EntropyRows *ent = nullptr, const int32_t *frozen = nullptr,
+                   int P_cur = -1) {
   const dg::Shape &s = m->s;
+  // attention over the first P_cur rows of caches with s.P rows per slice
+  dg::Shape sa = s;
+  if (P_cur >= 0) {
+    sa.P = P_cur;
+    sa.Pst = s.P;
+  }
   const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
   void *h0 = taps && taps->h0 ? taps->h0 : m->h0;
   void *q = taps && taps->q ? taps->q : m->q;
@@ -279,7 +298,7 @@ dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void 
       StageTimer tm(m, 2, st);
       DG_HIP(dg::launch_attention_bf16(static_cast<const u16 *>(q), static_cast<const u16 *>(k),
                                      static_cast<const u16 *>(v), static_cast<const u16 *>(Kp),
-                                     static_cast<const u16 *>(Vp), s, m->attn,
+                                     static_cast<const u16 *>(Vp), sa, m->attn,
                                      static_cast<u16 *>(o), st),
            "attention launch");
     }
@@ -314,7 +333,7 @@ dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void 
       StageTimer tm(m, 2, st);
       DG_HIP(dg::launch_attention_f32(static_cast<const float *>(q), static_cast<const float *>(k),
                                     static_cast<const float *>(v), static_cast<const float *>(Kp),
-                                    static_cast<const float *>(Vp), s, static_cast<float *>(o), st),
+                                    static_cast<const float *>(Vp), sa, static_cast<float *>(o), st),
            "attention launch");
     }
     {
@@ -366,6 +385,73 @@ dg_status check_times(const float *t, int B, float dt) {
 dg_status upload_params(dg_model *m, dg::StepParams *dst, const std::vector<dg::StepParams> &p,
                         hipStream_t st) {
   DG_HIP(dg::launch_set_params(dst, p.data(), static_cast<int>(p.size()), st), "parameter upload");
+  return DG_OK;
+}
+
+// Step-sampler generation of one batch of canvases from noise (see
+// dg_generate_canvas), attending to the first P_cur cache rows (-1: all P).
+dg_status generate_steps(dg_model *m, const void *K_pre, const void *V_pre, int P_cur, int steps,
+                         uint64_t seed, int32_t *x_out, void *z_out, hipStream_t st) {
+  const dg::Shape &s = m->s;
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  const size_t es = bf16 ? 2 : 4;
+  const size_t R = static_cast<size_t>(s.R());
+  const size_t nz = R * s.d * es;
+
+  // per-step constants for every canvas, uploaded once
+  std::vector<dg::StepParams> prm(static_cast<size_t>(steps) * s.B);
+  const float dt = static_cast<float>(1.0 / steps);
+  for (int k = 0; k < steps; ++k) {
+    const float tk = static_cast<float>(1.0 - static_cast<double>(k) / steps);
+    const dg::StepParams p = step_params(tk, dt, m->cfg.schedule);
+    for (int b = 0; b < s.B; ++b) prm[static_cast<size_t>(k) * s.B + b] = p;
+  }
+  if (dg_status e = upload_params(m, m->prm, prm, st)) return e;
+
+  int32_t *xb[2] = {m->genx, m->genx + R};
+  char *zb[2] = {m->genz, m->genz + nz};
+  // x_init: corruption of a zero canvas at kappa = 0 (every token uniform)
+  DG_HIP(dg::launch_fill_zero(m->kappa, align_up(s.B * sizeof(float)), st), "fill");
+  DG_HIP(dg::launch_fill_zero(xb[0], R * sizeof(int32_t), st), "fill");
+  DG_HIP(dg::launch_corrupt(xb[0], m->kappa, s.B, s.C, s.V, seed, xb[0], st), "corrupt launch");
+  DG_HIP(dg::launch_fill_zero(zb[0], nz, st), "fill");
+  for (int k = 0; k < steps; ++k) {
+    const int cur = k & 1, nxt = cur ^ 1;
+    const bool last = k == steps - 1;
+    int32_t *xo = last ? x_out : xb[nxt];
+    void *zo = (last && z_out) ? z_out : zb[nxt];
+    if (dg_status e = run_step(m, xb[cur], zb[cur], K_pre, V_pre, m->prm + static_cast<size_t>(k) * s.B,
+                               nullptr, 0, seed + static_cast<uint64_t>(k), xo, zo, nullptr, nullptr,
+                               nullptr, st, nullptr, nullptr, P_cur))
+      return e;
+  }
+  return DG_OK;
+}
+
+// Encoder cache entries of tokens [B, ld] (columns [0, n)) into cache rows
+// [pos, pos + n): key and value projections of the token embeddings.
+dg_status encode_kv(dg_model *m, const int32_t *tokens, int n, int ld, int pos, void *K, void *V,
+                    hipStream_t st) {
+  const dg::Shape &s = m->s;
+  StageTimer tm(m, 8, st);
+  if (m->cfg.dtype == DG_DTYPE_BF16) {
+    using u16 = uint16_t;
+    // chunks of at most C tokens per canvas fit the step's h0 buffer
+    for (int c0 = 0; c0 < n; c0 += s.C) {
+      const int nc = n - c0 < s.C ? n - c0 : s.C;
+      DG_HIP(dg::launch_embed_tokens(true, m->w.E, tokens + c0, ld, s.B, nc, s.d, s.V, m->h0, st),
+             "encoder embedding launch");
+      DG_HIP(dg::launch_kv_encode_bf16(static_cast<const u16 *>(m->h0), static_cast<const u16 *>(m->w.Wk),
+                                       static_cast<const u16 *>(m->w.Wv), s, nc, pos + c0, s.P,
+                                       static_cast<u16 *>(K), static_cast<u16 *>(V), st),
+             "encoder projection launch");
+    }
+  } else {
+    DG_HIP(dg::launch_kv_encode_f32(static_cast<const float *>(m->w.E), tokens, ld,
+                                    static_cast<const float *>(m->w.Wk), static_cast<const float *>(m->w.Wv),
+                                    s, n, pos, s.P, static_cast<float *>(K), static_cast<float *>(V), st),
+           "encoder projection launch");
+  }
   return DG_OK;
 }
 
@@ -441,6 +527,7 @@ dg_status dg_create(const dg_config *cfg, const dg_weights *w, dg_model **out) {
   m->stopped = reinterpret_cast<int32_t *>(p);
   m->stopbuf = m->stopped + m->s.B;
   p += L.flags;
+  m->blkx = reinterpret_cast<int32_t *>(p); p += L.blkx;
   *out = m;
   return DG_OK;
 }
@@ -659,37 +746,54 @@ dg_status dg_generate_canvas(dg_model *m, const void *K_pre, const void *V_pre, 
   if (bf16 && ((K_pre && !aligned16(K_pre)) || (V_pre && !aligned16(V_pre)) ||
                (z_out && !aligned16(z_out))))
     return fail(DG_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
-  const size_t es = bf16 ? 2 : 4;
-  const size_t R = static_cast<size_t>(s.R());
-  const size_t nz = R * s.d * es;
+  return generate_steps(m, K_pre, V_pre, -1, steps, seed, x_out, z_out, static_cast<hipStream_t>(stream));
+}
+
+dg_status dg_encode_kv(dg_model *m, const int32_t *tokens, int32_t n, int32_t pos, void *K_cache,
+                       void *V_cache, void *stream) {
+  g_err.clear();
+  if (dg_status s = check_model(m)) return s;
+  const dg::Shape &s = m->s;
+  if (n < 0 || pos < 0 || static_cast<int64_t>(pos) + n > s.P)
+    return fail(DG_ERR_INVALID_ARG, "need n >= 0, pos >= 0 and pos + n <= P (n=%d pos=%d P=%d)", n, pos, s.P);
+  if (n == 0) return DG_OK;
+  if (!tokens || !K_cache || !V_cache) return fail(DG_ERR_INVALID_ARG, "tokens, K_cache and V_cache must be non-NULL");
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  if (bf16 && (!aligned16(K_cache) || !aligned16(V_cache)))
+    return fail(DG_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+  return encode_kv(m, tokens, n, n, pos, K_cache, V_cache, static_cast<hipStream_t>(stream));
+}
+
+dg_status dg_generate_blocks(dg_model *m, void *K_cache, void *V_cache, int32_t P0,
+                             int32_t n_canvases, int32_t steps, uint64_t seed, int32_t *x_out,
+                             void *stream) {
+  g_err.clear();
+  if (dg_status s = check_model(m)) return s;
+  const dg::Shape &s = m->s;
+  if (!x_out) return fail(DG_ERR_INVALID_ARG, "x_out is NULL");
+  if (n_canvases < 1 || P0 < 0 || static_cast<int64_t>(P0) + static_cast<int64_t>(n_canvases) * s.C > s.P)
+    return fail(DG_ERR_INVALID_ARG, "need n_canvases >= 1, P0 >= 0 and P0 + n_canvases * C <= P "
+                "(P0=%d n_canvases=%d C=%d P=%d)", P0, n_canvases, s.C, s.P);
+  if (!K_cache || !V_cache) return fail(DG_ERR_INVALID_ARG, "K_cache and V_cache must be non-NULL");
+  if (steps < 1 || steps > kMaxSteps)
+    return fail(DG_ERR_INVALID_ARG, "steps must be in [1, %d] (got %d)", kMaxSteps, steps);
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  if (bf16 && (!aligned16(K_cache) || !aligned16(V_cache)))
+    return fail(DG_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
-
-  // per-step constants for every canvas, uploaded once
-  std::vector<dg::StepParams> prm(static_cast<size_t>(steps) * s.B);
-  const float dt = static_cast<float>(1.0 / steps);
-  for (int k = 0; k < steps; ++k) {
-    const float tk = static_cast<float>(1.0 - static_cast<double>(k) / steps);
-    const dg::StepParams p = step_params(tk, dt, m->cfg.schedule);
-    for (int b = 0; b < s.B; ++b) prm[static_cast<size_t>(k) * s.B + b] = p;
-  }
-  if (dg_status e = upload_params(m, m->prm, prm, st)) return e;
-
-  int32_t *xb[2] = {m->genx, m->genx + R};
-  char *zb[2] = {m->genz, m->genz + nz};
-  // x_init: corruption of a zero canvas at kappa = 0 (every token uniform)
-  DG_HIP(dg::launch_fill_zero(m->kappa, align_up(s.B * sizeof(float)), st), "fill");
-  DG_HIP(dg::launch_fill_zero(xb[0], R * sizeof(int32_t), st), "fill");
-  DG_HIP(dg::launch_corrupt(xb[0], m->kappa, s.B, s.C, s.V, seed, xb[0], st), "corrupt launch");
-  DG_HIP(dg::launch_fill_zero(zb[0], nz, st), "fill");
-  for (int k = 0; k < steps; ++k) {
-    const int cur = k & 1, nxt = cur ^ 1;
-    const bool last = k == steps - 1;
-    int32_t *xo = last ? x_out : xb[nxt];
-    void *zo = (last && z_out) ? z_out : zb[nxt];
-    if (dg_status e = run_step(m, xb[cur], zb[cur], K_pre, V_pre, m->prm + static_cast<size_t>(k) * s.B,
-                               nullptr, 0, seed + static_cast<uint64_t>(k), xo, zo, nullptr, nullptr,
-                               nullptr, st))
+  const size_t row = static_cast<size_t>(s.C) * sizeof(int32_t);
+  for (int j = 0; j < n_canvases; ++j) {
+    const int Pj = P0 + j * s.C;
+    // canvas j: a whole generation against the first Pj cache rows
+    if (dg_status e = generate_steps(m, K_cache, V_cache, Pj, steps,
+                                     seed + static_cast<uint64_t>(j) * static_cast<uint64_t>(steps),
+                                     m->blkx, nullptr, st))
       return e;
+    // commit: its clean tokens through the encoder into rows [Pj, Pj + C)
+    if (dg_status e = encode_kv(m, m->blkx, s.C, s.C, Pj, K_cache, V_cache, st)) return e;
+    DG_HIP(hipMemcpy2DAsync(x_out + static_cast<size_t>(j) * s.C, row * n_canvases, m->blkx, row, row,
+                            s.B, hipMemcpyDeviceToDevice, st),
+           "canvas copy");
   }
   return DG_OK;
 }

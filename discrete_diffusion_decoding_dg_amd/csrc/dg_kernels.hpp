@@ -15,11 +15,14 @@ struct StepParams {
   float inv_tau;
 };
 
-// Shapes of the decoder stand-in.
+// Shapes of the decoder stand-in. The prefix cache of canvas b and kv head g
+// holds P keys (and values) at rows [0, P) of a slice of pstride() rows.
 struct Shape {
   int B, C, P, d, Hq, Hkv, hd, V;
+  int Pst = 0;   // cache rows per (canvas, kv head) slice; 0: P
   int R() const { return B * C; }
   int G() const { return Hq / Hkv; }
+  int pstride() const { return Pst ? Pst : P; }
 };
 
 // Partial results of the split-V LM head, one record per (split, row).
@@ -53,6 +56,9 @@ constexpr int kInlineParams = 32;
 hipError_t launch_embed(bool bf16, const void *E, const int32_t *x, const void *z, int R, int d,
                         int V, void *h0, StepParams *prm, const StepParams *prm_src, int np,
                         hipStream_t st);
+// h [B * n, d] = E[x[b * ld + i]] for i < n (no self-conditioning input).
+hipError_t launch_embed_tokens(bool bf16, const void *E, const int32_t *x, int ld, int B, int n,
+                               int d, int V, void *h, hipStream_t st);
 // p0[r, v] = exp(p0[r, v] - lse[r]) in place (p0 holds scaled logits on entry).
 hipError_t launch_p0_from_logits(float *p0, const float *lse, int R, int V, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
@@ -83,6 +89,13 @@ hipError_t launch_ffw_down_bf16(const uint16_t *hid, const uint16_t *Wd, int M, 
                                 const int32_t *frozen, const uint16_t *z_t, uint16_t *z,
                                 hipStream_t st);
 
+// Encoder cache entries: for rows m = b * n + i of h [B * n, d], k = h Wk^T
+// and v = h Wv^T go to rows pos + i of the (b, kv head) slices of the caches
+// K, V [B, Hkv, Pst, hd].
+hipError_t launch_kv_encode_bf16(const uint16_t *h, const uint16_t *Wk, const uint16_t *Wv,
+                                 const Shape &s, int n, int pos, int Pst, uint16_t *K, uint16_t *V,
+                                 hipStream_t st);
+
 // ---- k_attention.hip (bf16 MFMA) ----
 int attention_splits(const Shape &s);
 size_t attention_workspace_bytes(const Shape &s);
@@ -107,6 +120,11 @@ hipError_t launch_qkv_f32(const float *h0, const float *Wq, const float *Wk, con
                           const Shape &s, float *q, float *k, float *v, hipStream_t st);
 hipError_t launch_attention_f32(const float *q, const float *k, const float *v, const float *Kp,
                                 const float *Vp, const Shape &s, float *o, hipStream_t st);
+// Encoder cache entries from tokens x[b * ld + i], i < n (out-of-range tokens
+// embed as zero rows), into rows pos + i of K, V [B, Hkv, Pst, hd].
+hipError_t launch_kv_encode_f32(const float *E, const int32_t *x, int ld, const float *Wk,
+                                const float *Wv, const Shape &s, int n, int pos, int Pst, float *K,
+                                float *V, hipStream_t st);
 hipError_t launch_oproj_f32(const float *o, const float *Wo, const float *h0, const Shape &s,
                             float *h1, hipStream_t st);
 size_t lmhead_f32_workspace_bytes(const Shape &s);

@@ -57,7 +57,7 @@ struct AttnArgs {
   uint16_t *o;
   float *opart;   // [splits][R][Hq][hd] unnormalised, when splits > 1
   float2 *ml;     // [splits][R][Hq] (m, l), log2 units
-  int B, C, P, Hq, Hkv, G, splits, tiles_per_split;
+  int B, C, P, Pst, Hq, Hkv, G, splits, tiles_per_split;   // Pst: cache rows per (b, g)
   float scale_log2;   // log2(e) / sqrt(hd)
 };
 
@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(AttnArgs a) {
     }
   }
 
-  const int64_t kvp_base = (static_cast<int64_t>(b) * a.Hkv + g) * a.P * HD;
+  const int64_t kvp_base = (static_cast<int64_t>(b) * a.Hkv + g) * a.Pst * HD;
   const int64_t kvc_base = (static_cast<int64_t>(b) * a.Hkv + g) * a.C * HD;
   const int tile0 = split * a.tiles_per_split;
   const int total_tiles = (Lk + BK - 1) / BK;
@@ -435,7 +435,7 @@ hipError_t launch_attention_bf16(const uint16_t *q, const uint16_t *k, const uin
   if (s.R() == 0) return hipSuccess;
   AttnArgs a;
   a.q = q; a.k = k; a.v = v; a.Kp = Kp; a.Vp = Vp; a.o = o;
-  a.B = s.B; a.C = s.C; a.P = s.P; a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G();
+  a.B = s.B; a.C = s.C; a.P = s.P; a.Pst = s.pstride(); a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G();
   plan(s, a.splits, a.tiles_per_split);
   const size_t rows = static_cast<size_t>(s.R()) * s.Hq;
   a.opart = static_cast<float *>(work);

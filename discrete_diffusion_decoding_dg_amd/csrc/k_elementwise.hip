@@ -123,6 +123,33 @@ __global__ void __launch_bounds__(256) embed_bf16_vec_kernel(const uint16_t *__r
   }
 }
 
+// Token rows for the encoder: row m = b * n + i embeds x[b * ld + i] (a token
+// outside [0, V) reads as a zero row).
+template <typename T>
+__global__ void __launch_bounds__(256) embed_tokens_kernel(const T *__restrict__ E,
+                                                           const int32_t *__restrict__ x, int ld,
+                                                           int n, int d, int V, T *__restrict__ h) {
+  const int m = blockIdx.x;
+  const int b = m / n, i = m - b * n;
+  const int32_t tok = x[static_cast<int64_t>(b) * ld + i];
+  const bool in = tok >= 0 && tok < V;
+  const T *er = E + static_cast<int64_t>(in ? tok : 0) * d;
+  T *hr = h + static_cast<int64_t>(m) * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) hr[c] = in ? er[c] : T(0);
+}
+
+hipError_t launch_embed_tokens(bool bf16, const void *E, const int32_t *x, int ld, int B, int n,
+                               int d, int V, void *h, hipStream_t st) {
+  if (static_cast<int64_t>(B) * n == 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(embed_tokens_kernel<uint16_t>, dim3(B * n), dim3(256), 0, st,
+                       static_cast<const uint16_t *>(E), x, ld, n, d, V, static_cast<uint16_t *>(h));
+  else
+    hipLaunchKernelGGL(embed_tokens_kernel<float>, dim3(B * n), dim3(256), 0, st,
+                       static_cast<const float *>(E), x, ld, n, d, V, static_cast<float *>(h));
+  return hipGetLastError();
+}
+
 hipError_t launch_embed(bool bf16, const void *E, const int32_t *x, const void *z, int R, int d,
                         int V, void *h0, StepParams *prm, const StepParams *prm_src, int np,
                         hipStream_t st) {

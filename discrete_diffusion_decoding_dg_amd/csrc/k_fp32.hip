@@ -55,7 +55,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(const float *__restrict__
                                                        const float *__restrict__ v,
                                                        const float *__restrict__ Kp,
                                                        const float *__restrict__ Vp, int C, int P,
-                                                       int Hq, int Hkv, int hd, float scale,
+                                                       int Pst, int Hq, int Hkv, int hd, float scale,
                                                        float *__restrict__ o) {
   extern __shared__ float sc[];   // P + C scores
   __shared__ float red[256];
@@ -64,8 +64,8 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(const float *__restrict__
   const int g = h / (Hq / Hkv);
   const int Lk = P + C;
   const float *qr = q + (static_cast<int64_t>(r) * Hq + h) * hd;
-  const float *kp = Kp + (static_cast<int64_t>(b) * Hkv + g) * P * hd;
-  const float *vp = Vp + (static_cast<int64_t>(b) * Hkv + g) * P * hd;
+  const float *kp = Kp + (static_cast<int64_t>(b) * Hkv + g) * Pst * hd;
+  const float *vp = Vp + (static_cast<int64_t>(b) * Hkv + g) * Pst * hd;
   const float *kc = k + (static_cast<int64_t>(b) * Hkv + g) * C * hd;
   const float *vc = v + (static_cast<int64_t>(b) * Hkv + g) * C * hd;
   float mx = -INFINITY;
@@ -122,6 +122,37 @@ __global__ void __launch_bounds__(256) oproj_f32_kernel(const float *__restrict_
     float acc = 0.f;
     for (int c = 0; c < K; ++c) acc = fmaf(x[c], w[c], acc);
     h1[idx] = h0[idx] + acc;
+  }
+}
+
+// Encoder cache entries: row m = b * n + i embeds token x[b * ld + i] (zero
+// row when out of range) and its k (v) projection goes to row pos + i of the
+// (b, kv head) slice of K (V) [B, Hkv, Pst, hd].
+__global__ void __launch_bounds__(256) kv_encode_f32_kernel(const float *__restrict__ E,
+                                                            const int32_t *__restrict__ x, int ld,
+                                                            const float *__restrict__ Wk,
+                                                            const float *__restrict__ Wv, int B,
+                                                            int n, int d, int V, int Hkv, int hd,
+                                                            int pos, int Pst, float *__restrict__ K,
+                                                            float *__restrict__ Vc) {
+  const int Nkv = Hkv * hd;
+  const int64_t total = static_cast<int64_t>(B) * n * 2 * Nkv;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int m = static_cast<int>(idx / (2 * Nkv));
+    int c = static_cast<int>(idx - static_cast<int64_t>(m) * 2 * Nkv);
+    const bool is_v = c >= Nkv;
+    if (is_v) c -= Nkv;
+    const int b = m / n, i = m - b * n;
+    const int32_t tok = x[static_cast<int64_t>(b) * ld + i];
+    const int g = c / hd, e = c - g * hd;
+    float acc = 0.f;
+    if (tok >= 0 && tok < V) {
+      const float *er = E + static_cast<int64_t>(tok) * d;
+      const float *w = (is_v ? Wv : Wk) + static_cast<int64_t>(c) * d;
+      for (int t = 0; t < d; ++t) acc = fmaf(er[t], w[t], acc);
+    }
+    (is_v ? Vc : K)[((static_cast<int64_t>(b) * Hkv + g) * Pst + pos + i) * hd + e] = acc;
   }
 }
 
@@ -327,7 +358,8 @@ hipError_t launch_attention_f32(const float *q, const float *k, const float *v, 
   if (s.R() == 0) return hipSuccess;
   const size_t shm = static_cast<size_t>(s.P + s.C) * sizeof(float);
   hipLaunchKernelGGL(attn_f32_kernel, dim3(s.R(), s.Hq), dim3(256), shm, st, q, k, v, Kp, Vp,
-                     s.C, s.P, s.Hq, s.Hkv, s.hd, static_cast<float>(1.0 / sqrt((double)s.hd)), o);
+                     s.C, s.P, s.pstride(), s.Hq, s.Hkv, s.hd,
+                     static_cast<float>(1.0 / sqrt((double)s.hd)), o);
   return hipGetLastError();
 }
 
@@ -339,6 +371,18 @@ hipError_t launch_oproj_f32(const float *o, const float *Wo, const float *h0, co
   if (blocks > 16384) blocks = 16384;
   hipLaunchKernelGGL(oproj_f32_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, o,
                      Wo, h0, s.R(), s.d, s.Hq * s.hd, h1);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_encode_f32(const float *E, const int32_t *x, int ld, const float *Wk,
+                                const float *Wv, const Shape &s, int n, int pos, int Pst, float *K,
+                                float *V, hipStream_t st) {
+  const int64_t total = static_cast<int64_t>(s.B) * n * 2 * s.Hkv * s.hd;
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(kv_encode_f32_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, E,
+                     x, ld, Wk, Wv, s.B, n, s.d, s.V, s.Hkv, s.hd, pos, Pst, K, V);
   return hipGetLastError();
 }
 

@@ -69,6 +69,29 @@ struct ResidualEpi {
   }
 };
 
+// Encoder cache entries: rows m = b * n + i of the token embeddings, columns
+// [0, Nkv) the k projection and [Nkv, 2 Nkv) the v projection; results go to
+// row pos + i of the (b, kv head) slices of the caches [B, Hkv, Pst, hd].
+struct KvCacheEpi {
+  static constexpr bool kPair = false;
+  const uint16_t *Wk, *Wv;
+  uint16_t *K, *V;
+  int Nkv, n, pos, Pst, Hkv, hd;
+  __device__ const uint16_t *brow(int c, int Kd) const {
+    return (c < Nkv ? Wk + static_cast<int64_t>(c) * Kd : Wv + static_cast<int64_t>(c - Nkv) * Kd);
+  }
+  __device__ void store(int m, int c, float acc) const {
+    uint16_t *dst = K;
+    if (c >= Nkv) {
+      c -= Nkv;
+      dst = V;
+    }
+    const int b = m / n, i = m - b * n;
+    const int g = c / hd, e = c - g * hd;
+    dst[((static_cast<int64_t>(b) * Hkv + g) * Pst + pos + i) * hd + e] = f32_to_bf16(acc);
+  }
+};
+
 // Gate and up projections of the self-conditioning block in one GEMM over
 // the packed matrix W [2F, K]: rows 64 j + [0, 32) are gate rows 32 j + [0, 32)
 // and rows 64 j + 32 + [0, 32) the up rows of the same hidden units, so a
@@ -674,6 +697,24 @@ hipError_t launch_qkv_bf16(const uint16_t *h0, const uint16_t *Wq, const uint16_
     hipLaunchKernelGGL(gemm_tn_bf16_dma_kernel<QkvEpi>, grid, dim3(512), 0, st, h0, M, N, s.d, epi);
   else
     hipLaunchKernelGGL(gemm_tn_bf16_kernel<QkvEpi>, grid, dim3(256), 0, st, h0, M, N, s.d, epi);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_encode_bf16(const uint16_t *h, const uint16_t *Wk, const uint16_t *Wv,
+                                 const Shape &s, int n, int pos, int Pst, uint16_t *K, uint16_t *V,
+                                 hipStream_t st) {
+  const int Nkv = s.Hkv * s.hd;
+  KvCacheEpi epi{Wk, Wv, K, V, Nkv, n, pos, Pst, s.Hkv, s.hd};
+  const int M = s.B * n, N = 2 * Nkv;
+  if (M == 0) return hipSuccess;
+  if (M >= kBigRows && s.d % big::BKB == 0 && Nkv % big::BNB == 0)
+    hipLaunchKernelGGL(big::gemm_big_kernel<KvCacheEpi>, dim3(N / big::BNB, (M + big::BMB - 1) / big::BMB),
+                       dim3(512), 0, st, h, M, N, s.d, epi);
+  else if (s.d % skinny::BK == 0)
+    return skinny::launch(h, M, N, s.d, epi, st);
+  else
+    hipLaunchKernelGGL(gemm_tn_bf16_kernel<KvCacheEpi>, dim3((N + BN - 1) / BN, (M + BM - 1) / BM),
+                       dim3(256), 0, st, h, M, N, s.d, epi);
   return hipGetLastError();
 }
 

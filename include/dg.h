@@ -203,6 +203,33 @@ dg_status dg_generate_canvas_entropy(dg_model *m, const void *K_pre, const void 
                                      float eps_stop, int32_t *x_out, void *z_out,
                                      int32_t *steps_out, void *stream);
 
+/* Prompt prefill and canvas commit (TR summary, Method: the pipeline
+ * figure's causal encoder fills the KV cache from the prompt, and each clean
+ * canvas goes back through it and is appended to the cache). Reading: the
+ * encoder shares the decoder's weights, and a single attention block's cache
+ * entries of a token are its key and value projections with no
+ * self-conditioning input, k = E[x] Wk^T and v = E[x] Wv^T (rounded to act),
+ * so prefill and commit are one operation.
+ *   tokens [B, n] int32 (a token outside [0, V) embeds as a zero row);
+ *   K_cache, V_cache [B, Hkv, P, hd] act: the model's P is the cache
+ *   capacity; rows [pos, pos + n) of every (canvas, kv head) slice are
+ *   written, nothing else. Needs n >= 0, pos >= 0 and pos + n <= P. */
+dg_status dg_encode_kv(dg_model *m, const int32_t *tokens, int32_t n, int32_t pos, void *K_cache,
+                       void *V_cache, void *stream);
+
+/* Block-autoregressive generation (TR summary, Method: one canvas of C
+ * tokens at a time; a finished canvas is committed to the cache and the next
+ * one starts). With the prompt's entries in cache rows [0, P0), canvas
+ * j = 0 .. n_canvases-1 is generated exactly as dg_generate_canvas with
+ * `steps` steps and seed seed + j * steps, attending to cache rows
+ * [0, P0 + j C) only; its final tokens are then encoded into rows
+ * [P0 + j C, P0 + (j + 1) C) (dg_encode_kv).
+ *   K_cache, V_cache [B, Hkv, P, hd] act, read and extended in place;
+ *   P0 + n_canvases * C <= P; x_out [B, n_canvases, C] int32. */
+dg_status dg_generate_blocks(dg_model *m, void *K_cache, void *V_cache, int32_t P0,
+                             int32_t n_canvases, int32_t steps, uint64_t seed, int32_t *x_out,
+                             void *stream);
+
 /* Gated feed-forward self-conditioning block (TR summary, Method, three-line
  * update: z = FFW(p0 E) with a standard feed-forward network; the pages give
  * no structure, the reading here is the Gemma family's gated form):
@@ -231,13 +258,13 @@ dg_status dg_ffw(dg_model *m, const void *u, void *z_out, void *stream);
  * Stages: 0 embed, 1 q/k/v projection, 2 attention (+ split merge),
  * 3 output projection, 4 LM head (logits, softmax statistics, z partials,
  * Gumbel argmax), 5 split merge + Step select, 6 corruption, 7 feed-forward
- * self-conditioning block.
+ * self-conditioning block, 8 encoder (prefill / commit).
  * dg_profile_enable(m, mask) times the stages whose bit (1 << stage) is set
  * in mask (0 turns profiling off; every event pair adds a few microseconds of
  * queue time between kernels, so time only the stages you need).
  * dg_profile_read waits for the recorded events, returns the summed
  * milliseconds and the number of timed launches per stage, and clears them. */
-#define DG_NUM_STAGES 8
+#define DG_NUM_STAGES 9
 typedef struct dg_profile {
   double ms[DG_NUM_STAGES];
   int64_t count[DG_NUM_STAGES];

@@ -1,0 +1,161 @@
+"""GPU parity of prompt prefill / canvas commit (dg_encode_kv) against the
+oracle's encoder entries, and of block-autoregressive generation
+(dg_generate_blocks): each canvas equals a single-canvas generation against
+exactly its prefix, each commit equals the encoder entries of that canvas,
+and the first canvas follows the oracle's trajectory up to Gumbel near-ties."""
+import numpy as np
+import pytest
+
+from oracle import denoise_step, encode_kv
+from tests.dg_harness import RTOL_BF16, RTOL_F32, GpuModel, assert_close, to_dev, to_host, token_gate
+from workloads import get_config, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+ENCODE = {
+    # fp32 kernel, more tokens than a canvas, written at an offset
+    "c1-n20": dict(base="c1", P=40, n=20, pos=5),
+    # bf16, three chunks of at most C tokens, 64 x 32 tiles
+    "bf16-n100": dict(base="c2", B=2, C=40, P=120, d=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                      V=4096, n=100, pos=7),
+    # width 2816 and head_dim 176
+    "bf16-hd176": dict(base="c4", B=1, C=24, P=40, d=2816, n_q_heads=16, n_kv_heads=8, head_dim=176,
+                       V=1024, n=24, pos=0),
+    # 2250 rows: the 256 x 256-tile kernel
+    "bf16-rows2250": dict(base="c5", B=9, C=250, P=260, d=256, n_q_heads=4, n_kv_heads=4,
+                          head_dim=64, V=4096, n=250, pos=3),
+}
+
+
+def _split(spec):
+    spec = dict(spec)
+    base = spec.pop("base")
+    extra = {k: spec.pop(k) for k in ["n", "pos", "P0", "n_canvases"] if k in spec}
+    return get_config(base, **spec), extra
+
+
+def _act_dev(a, cfg):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    return t.to(torch.bfloat16) if cfg.dtype == "bf16" else t
+
+
+def _sentinel_cache(cfg):
+    import torch
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    shape = (cfg.B, cfg.n_kv_heads, cfg.P, cfg.head_dim)
+    return torch.full(shape, 7.0, dtype=dt, device="cuda"), torch.full(shape, -3.0, dtype=dt, device="cuda")
+
+
+@pytest.mark.parametrize("name", list(ENCODE))
+def test_encode_kv_matches_oracle(name):
+    import torch
+    import discrete_diffusion_decoding_dg_amd as dg
+    cfg, ex = _split(ENCODE[name])
+    n, pos = ex["n"], ex["pos"]
+    inp = make_inputs(cfg, ["E", "Wq", "Wk", "Wv", "Wo"])
+    m = GpuModel(cfg, inp)
+    tok = np.random.default_rng(5).integers(0, cfg.V, size=(cfg.B, n)).astype(np.int32)
+    K, V = _sentinel_cache(cfg)
+    print(f"[gpu] encode {name} B={cfg.B} n={n} pos={pos} P={cfg.P}", flush=True)
+    dg.dg_encode_kv(m.model, torch.from_numpy(tok).cuda(), pos, K, V)
+    torch.cuda.synchronize()
+    m.close()
+    Kh, Vh = to_host(K), to_host(V)
+    w = {k: inp[k] for k in ["E", "Wk", "Wv"]}
+    k, v = encode_kv(cfg, w, tok)
+    rt = RTOL_F32 if cfg.dtype == "f32" else RTOL_BF16
+    assert_close("k", Kh[:, :, pos:pos + n], k, rt)
+    assert_close("v", Vh[:, :, pos:pos + n], v, rt)
+    # nothing outside rows [pos, pos + n) is touched
+    rest = np.ones(cfg.P, bool)
+    rest[pos:pos + n] = False
+    assert (Kh[:, :, rest] == 7.0).all() and (Vh[:, :, rest] == -3.0).all()
+
+
+BLOCKS = {
+    "c1": dict(base="c1", P=8 + 3 * 16, P0=8, n_canvases=3),
+    "c1-no-prompt": dict(base="c1", P=2 * 16, P0=0, n_canvases=2),
+    "bf16-small": dict(base="c2", B=2, C=40, P=100 + 2 * 40, d=256, n_q_heads=4, n_kv_heads=2,
+                       head_dim=64, V=512, P0=100, n_canvases=2),
+}
+
+
+@pytest.mark.parametrize("name", list(BLOCKS))
+def test_generate_blocks(name):
+    import torch
+    import discrete_diffusion_decoding_dg_amd as dg
+    cfg, ex = _split(BLOCKS[name])
+    P0, nb = ex["P0"], ex["n_canvases"]
+    steps, seed = 4, 21
+    inp = make_inputs(cfg)
+    w = {k: inp[k] for k in ["E", "Wq", "Wk", "Wv", "Wo"]}
+    m = GpuModel(cfg, inp)
+    # prompt entries in rows [0, P0); every later row starts as garbage
+    K, V = to_dev(inp, "K_pre", cfg), to_dev(inp, "V_pre", cfg)
+    K[:, :, P0:] = 100.0
+    V[:, :, P0:] = -100.0
+    x = torch.empty((cfg.B, nb, cfg.C), dtype=torch.int32, device="cuda")
+    print(f"[gpu] generate blocks {name} P0={P0} canvases={nb} steps={steps}", flush=True)
+    dg.dg_generate_blocks(m.model, K, V, P0, nb, steps, seed, x)
+    torch.cuda.synchronize()
+    m.close()
+    xh, Kh, Vh = x.cpu().numpy(), to_host(K), to_host(V)
+    rt = RTOL_F32 if cfg.dtype == "f32" else RTOL_BF16
+    for j in range(nb):
+        Pj = P0 + j * cfg.C
+        # canvas j: the same kernels on a model whose prefix is exactly Pj rows
+        cj = cfg.with_(P=Pj)
+        mj = GpuModel(cj, inp)
+        Kj = K[:, :, :Pj].contiguous()
+        Vj = V[:, :, :Pj].contiguous()
+        xj = torch.empty((cfg.B, cfg.C), dtype=torch.int32, device="cuda")
+        dg.dg_generate_canvas(mj.model, Kj, Vj, steps, seed + j * steps, xj)
+        torch.cuda.synchronize()
+        mj.close()
+        assert np.array_equal(xh[:, j], xj.cpu().numpy()), f"canvas {j} differs from a single-canvas generation"
+        # the commit holds the encoder entries of that canvas
+        k, v = encode_kv(cfg, w, xh[:, j])
+        assert_close(f"k rows of canvas {j}", Kh[:, :, Pj:Pj + cfg.C], k, rt)
+        assert_close(f"v rows of canvas {j}", Vh[:, :, Pj:Pj + cfg.C], v, rt)
+    assert np.array_equal(Kh[:, :, :P0], to_host(to_dev(inp, "K_pre", cfg))[:, :, :P0])
+    # canvas 0 against the oracle, step by step from the oracle's own state,
+    # until the first Gumbel near-tie
+    from oracle import corrupt
+    xo = corrupt(np.zeros((cfg.B, cfg.C), np.int32), np.zeros(cfg.B, np.float32), seed, cfg.V)
+    zo = np.zeros((cfg.B, cfg.C, cfg.d))
+    dt = float(np.float32(1.0 / steps))
+    mj = GpuModel(cfg.with_(P=P0), inp)
+    xg = torch.from_numpy(xo).cuda()
+    zg = _act_dev(zo, cfg)
+    Kp, Vp = to_dev(inp, "K_pre", cfg)[:, :, :P0].contiguous(), to_dev(inp, "V_pre", cfg)[:, :, :P0].contiguous()
+    Kpo, Vpo = inp["K_pre"][:, :, :P0], inp["V_pre"][:, :, :P0]
+    for k in range(steps):
+        t = np.full(cfg.B, np.float32(1.0 - k / steps), np.float32)
+        g = mj.step(xg, zg, Kp, Vp, t, dt, seed + k, taps=False)
+        r = denoise_step(cfg.with_(P=P0), w, xo, zo, Kpo, Vpo, t, dt, seed + k)
+        if not np.array_equal(g["x_out"], r["x_out"]):
+            token_gate(g["x_out"], r, name=f"canvas 0 step {k}")
+            break
+        xo, zo = r["x_out"], r["z_out"]
+        xg = torch.from_numpy(g["x_out"]).cuda()
+        zg = _act_dev(g["z_out"], cfg)
+    else:
+        assert np.array_equal(xo, xh[:, 0])
+    mj.close()
+
+
+def test_generate_blocks_argument_checks():
+    import torch
+    import discrete_diffusion_decoding_dg_amd as dg
+    cfg, _ = _split(BLOCKS["c1"])
+    inp = make_inputs(cfg)
+    m = GpuModel(cfg, inp)
+    K, V = to_dev(inp, "K_pre", cfg), to_dev(inp, "V_pre", cfg)
+    x = torch.empty((cfg.B, 4, cfg.C), dtype=torch.int32, device="cuda")
+    with pytest.raises(dg.DgError, match="INVALID_ARG"):
+        dg.dg_generate_blocks(m.model, K, V, 8, 4, 4, 0, x)          # 8 + 4 * 16 > P
+    tok = torch.zeros((cfg.B, 10), dtype=torch.int32, device="cuda")
+    with pytest.raises(dg.DgError, match="INVALID_ARG"):
+        dg.dg_encode_kv(m.model, tok, cfg.P - 5, K, V)              # rows past P
+    m.close()
