@@ -111,6 +111,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-corrupt", action="store_true")
     ap.add_argument("--no-ffw", action="store_true", help="skip the feed-forward block timings")
+    ap.add_argument("--no-blocks", action="store_true", help="skip the block-autoregressive timings")
     ap.add_argument("--copy-mib", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device to device three times (a plain copy kernel "
                          "of known size, to scale HBM byte counters)")
@@ -277,6 +278,43 @@ def main():
             dg.dg_set_ffw(model)
             del fw
 
+    # block-autoregressive pipeline on the same shapes: prefill of the P-token
+    # prompt into a cache with room for 4 more canvases, then 4 canvases of
+    # cfg.steps steps, each committed to the cache before the next starts
+    blocks_res = None
+    if not args.no_blocks and cfg.B * (cfg.P + 4 * cfg.C) * cfg.n_kv_heads * cfg.head_dim * 2 < (8 << 30):
+        nb = 4
+        cb = cfg.with_(P=cfg.P + nb * cfg.C)
+        mb = dg.dg_create(config_args(cb), wdev["E"], wdev["Wq"], wdev["Wk"], wdev["Wv"], wdev["Wo"])
+        shape = (cfg.B, cfg.n_kv_heads, cb.P, cfg.head_dim)
+        Kc = torch.zeros(shape, dtype=Kp.dtype, device="cuda")
+        Vc = torch.zeros(shape, dtype=Kp.dtype, device="cuda")
+        prompt = torch.from_numpy(
+            np.random.default_rng(1).integers(0, cfg.V, size=(cfg.B, cfg.P)).astype(np.int32)).cuda()
+        xb = torch.empty((cfg.B, nb, cfg.C), dtype=torch.int32, device="cuda")
+        dg.dg_encode_kv(mb, prompt, 0, Kc, Vc)
+        dg.dg_generate_blocks(mb, Kc, Vc, cfg.P, nb, cfg.steps, 5, xb)
+        torch.cuda.synchronize()
+        b0, b1, b2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        b0.record()
+        dg.dg_encode_kv(mb, prompt, 0, Kc, Vc)
+        b1.record()
+        dg.dg_generate_blocks(mb, Kc, Vc, cfg.P, nb, cfg.steps, 5, xb)
+        b2.record()
+        torch.cuda.synchronize()
+        dg.dg_profile_enable(mb, ["encode"])
+        dg.dg_generate_blocks(mb, Kc, Vc, cfg.P, nb, cfg.steps, 5, xb)
+        torch.cuda.synchronize()
+        dg.dg_profile_enable(mb, [])
+        enc_ms, enc_n = dg.dg_profile_read(mb)["encode"]
+        gen_blocks_ms = b1.elapsed_time(b2)
+        blocks_res = {"prompt_tokens": cfg.P, "canvases": nb, "steps_per_canvas": cfg.steps,
+                      "prefill_ms": b0.elapsed_time(b1), "generate_ms": gen_blocks_ms,
+                      "commit_ms": enc_ms / max(1, enc_n),
+                      "canvas_tokens_per_s": cfg.B * nb * cfg.C / (gen_blocks_ms * 1e-3)}
+        mb.close()
+        del Kc, Vc
+
     fl = cfg.flops_per_step()
     lm_ms, lm_n = prof["lmhead"]
     lm_avg_ms = lm_ms / max(1, lm_n)
@@ -316,6 +354,8 @@ def main():
     }
     if ffw_res is not None:
         result["ffw_block"] = ffw_res
+    if blocks_res is not None:
+        result["blocks"] = blocks_res
     if not args.no_corrupt:
         result["corrupt"] = corrupt_bandwidth()
     model.close()
