@@ -380,25 +380,39 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-// o[r, h, e] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// o[r, h, e] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s. One thread
+// per four consecutive columns of a row (hd % 4 == 0): the split weights are
+// computed once per thread and the partials stream as 16-byte loads.
 __global__ void __launch_bounds__(256) attn_combine_kernel(const float *__restrict__ opart,
                                                            const float2 *__restrict__ ml,
                                                            int splits, int64_t rows, int hd,
                                                            uint16_t *__restrict__ o) {
-  const int64_t total = rows * hd;   // rows = R * Hq
-  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
-       idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t row = idx / hd;
+  const int q4 = hd / 4;
+  const int64_t total = rows * hd, total4 = rows * q4;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total4;
+       t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t row = t / q4;
+    const int64_t idx = row * hd + 4 * (t - row * q4);
     float M = -INFINITY;
     for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[s * rows + row].x);
-    float num = 0.f, den = 0.f;
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    float den = 0.f;
+#pragma unroll 8
     for (int s = 0; s < splits; ++s) {
       const float2 v = ml[s * rows + row];
       const float w = exp2f(v.x - M);
-      num += w * opart[s * total + idx];
+      const float4 x = *reinterpret_cast<const float4 *>(opart + s * total + idx);
+      num.x += w * x.x;
+      num.y += w * x.y;
+      num.z += w * x.z;
+      num.w += w * x.w;
       den += w * v.y;
     }
-    o[idx] = f32_to_bf16(num / den);
+    const float inv = 1.f / den;
+    uint2 out;
+    out.x = pack_bf16x2(num.x * inv, num.y * inv);
+    out.y = pack_bf16x2(num.z * inv, num.w * inv);
+    *reinterpret_cast<uint2 *>(o + idx) = out;
   }
 }
 
@@ -451,8 +465,8 @@ hipError_t launch_attention_bf16(const uint16_t *q, const uint16_t *k, const uin
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  const int64_t total = static_cast<int64_t>(rows) * s.hd;
-  int64_t blocks = (total + 255) / 256;
+  const int64_t total4 = static_cast<int64_t>(rows) * (s.hd / 4);
+  int64_t blocks = (total4 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st,
                      a.opart, a.ml, a.splits, static_cast<int64_t>(rows), s.hd, o);
