@@ -18,7 +18,9 @@ It follows the DiffusionGemma Technical Report as summarised on hyper.ai
     the recommended sampler (entropy.py);
   * block-autoregressive paragraph and pipeline figure: prompt prefill,
     canvas commit to the KV cache and canvas-by-canvas generation
-    (blocks.py).
+    (blocks.py);
+  * the decoder as a deeper pre-norm stack with a gated MLP per layer
+    (stack.py).
 
 Readings taken where the pages stop short (each documented where used):
 Step is the Euler step of the uniform-path CTMC,
@@ -47,6 +49,7 @@ from .corrupt import corrupt
 from .step import denoise_step, generate_canvas, self_condition
 from .ffw import gelu_tanh, ffw, ffw_hidden
 from .blocks import encode_kv, generate_blocks
+from .stack import rmsnorm, layer, stack_step
 from .entropy import (row_entropy, accept_mask, renoise_tokens, entropy_step,
                       generate_canvas_entropy)
 
@@ -56,5 +59,5 @@ __all__ = [
     "qkv_proj", "attention", "out_proj", "lm_head", "bernoulli_uniforms", "gumbel_noise",
     "step_select", "corrupt", "denoise_step", "generate_canvas", "row_entropy", "accept_mask",
     "renoise_tokens", "entropy_step", "generate_canvas_entropy", "self_condition", "gelu_tanh",
-    "ffw", "ffw_hidden", "encode_kv", "generate_blocks",
+    "ffw", "ffw_hidden", "encode_kv", "generate_blocks", "rmsnorm", "layer", "stack_step",
 ]

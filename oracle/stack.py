@@ -1,0 +1,85 @@
+"""Multi-layer decoder stack for the denoising step -- TEST INFRASTRUCTURE.
+
+TR summary, Method: the decoder is a transformer (weight-shared
+encoder-decoder, initialised from a Gemma mixture-of-experts checkpoint)
+that maps the noisy canvas, the self-conditioning signal and the KV cache H
+to logits; its layers are not described. This stack is the plainest deeper
+stand-in built from the same parts as the single block, with the Gemma
+family's pre-norm layout. Readings:
+  * h0 = E[x] + z (as the single block);
+  * layer l (own prefix cache K_l, V_l):
+        a = rmsnorm(h) g_attn_l,   q, k, v = a Wq_l^T, a Wk_l^T, a Wv_l^T,
+        h = h + attention(q, [K_l ; k], [V_l ; v]) Wo_l^T,
+        m = rmsnorm(h) g_mlp_l,    h = h + W_down_l (gelu(W_gate_l m) * (W_up_l m));
+    with rmsnorm(x) = x / sqrt(mean(x^2) + 1e-6), no biases;
+  * the LM head reads rmsnorm(h_L) g_final through the tied embedding;
+  * everything after the logits (temperature, p0, z = FFW(p0 E), Step) is
+    the single block's.
+Rounding points (act dtype): h0, each normalised activation, q, k, v, o, each
+residual sum, the MLP hidden activations, the final normalised activation;
+sums in float64.
+"""
+import numpy as np
+
+from .decoder import attention, embed, lm_head
+from .ffw import gelu_tanh
+from .rounding import round_act
+from .sampling import step_select
+from .schedule import inv_temperature, step_lambda
+from .step import self_condition
+
+RMS_EPS = 1e-6
+
+
+def rmsnorm(x, g, act):
+    """round(x / sqrt(mean(x^2) + eps) * g) over the last axis."""
+    x = np.asarray(x, np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + RMS_EPS)
+    return round_act(x * r * np.asarray(g, np.float64), act)
+
+
+def layer(cfg, lw, h, K_pre, V_pre):
+    """One pre-norm layer on h [B, C, d]; returns (h_out, parts)."""
+    act = cfg.dtype
+    B, C, d = h.shape
+    Hq, Hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    a = rmsnorm(h, lw["g_attn"], act)
+    x = a.reshape(B * C, d)
+    q = round_act(x @ np.asarray(lw["Wq"], np.float64).T, act).reshape(B, C, Hq, hd)
+    k = round_act(x @ np.asarray(lw["Wk"], np.float64).T, act).reshape(B, C, Hkv, hd).transpose(0, 2, 1, 3)
+    v = round_act(x @ np.asarray(lw["Wv"], np.float64).T, act).reshape(B, C, Hkv, hd).transpose(0, 2, 1, 3)
+    o = attention(q, k, v, K_pre, V_pre, act)
+    h1 = round_act(h + (o.reshape(B * C, Hq * hd) @ np.asarray(lw["Wo"], np.float64).T).reshape(B, C, d), act)
+    m = rmsnorm(h1, lw["g_mlp"], act).reshape(B * C, d)
+    g = m @ np.asarray(lw["W_gate"], np.float64).T
+    u = m @ np.asarray(lw["W_up"], np.float64).T
+    hid = round_act(gelu_tanh(g) * u, act)
+    h2 = round_act(h1 + (hid @ np.asarray(lw["W_down"], np.float64).T).reshape(B, C, d), act)
+    return h2, dict(a=a, q=q, k=k, v=v, o=o, h_attn=h1, m=m.reshape(B, C, d), h=h2)
+
+
+def stack_step(cfg, w, sw, x_t, z_t, K_pre, V_pre, t, dt, seed, canvas_ids=None):
+    """One denoising step through the stack. `w` holds E (and optionally the
+    FFW block); `sw` holds the per-layer weights as lists (Wq, Wk, Wv, Wo,
+    g_attn, g_mlp, W_gate, W_up, W_down) and g_final; K_pre, V_pre are
+    [L, B, Hkv, P, hd]."""
+    act = cfg.dtype
+    Bp = x_t.shape[0]
+    cid = np.arange(Bp) if canvas_ids is None else np.asarray(canvas_ids)
+    t = np.asarray(t, dtype=np.float32)
+    lam = np.array([step_lambda(float(tb), float(dt), cfg.schedule) for tb in t], dtype=np.float32)
+    inv_tau = np.array([inv_temperature(float(tb)) for tb in t], dtype=np.float32)
+    h = embed(w["E"], x_t, z_t, act)
+    layers = []
+    for l in range(len(sw["Wq"])):
+        lw = {n: sw[n][l] for n in ["Wq", "Wk", "Wv", "Wo", "g_attn", "g_mlp", "W_gate", "W_up", "W_down"]}
+        h, parts = layer(cfg, lw, h, K_pre[l], V_pre[l])
+        layers.append(parts)
+    hf = rmsnorm(h, sw["g_final"], act)
+    head = lm_head(hf, w["E"], inv_tau, act)
+    smp = step_select(x_t, head["s"], lam, seed, cid)
+    out = dict(h0=embed(w["E"], x_t, z_t, act), layers=layers, h_final=hf, lam=lam, inv_tau=inv_tau,
+               **head, **smp)
+    out["p0E"] = head["z"]
+    out["z_out"] = self_condition(w, head["z"], act)
+    return out

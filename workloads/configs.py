@@ -33,6 +33,8 @@ class Config:
     note: str = ""
     ffw_hidden: int = 0           # width F of the gated self-conditioning block (0: identity)
     ffw_gain: float = 1.0         # W_gate, W_up ~ N(0, (gain / sqrt(d))^2); W_down ~ N(0, 1 / F)
+    n_layers: int = 0             # layers of the pre-norm decoder stack (0: the single block)
+    mlp_hidden: int = 0           # hidden width of each stack layer's gated MLP
 
     @property
     def R(self):
@@ -54,8 +56,10 @@ class Config:
         oproj = 2 * R * Hq * hd * d
         lm = 4 * R * self.V * d
         ffw = 6 * R * d * self.ffw_hidden
-        return dict(qkv=qkv, attn=attn, oproj=oproj, lm=lm, ffw=ffw,
-                    total=qkv + attn + oproj + lm + ffw)
+        L = max(1, self.n_layers)
+        mlp = 6 * R * d * self.mlp_hidden * self.n_layers
+        return dict(qkv=L * qkv, attn=L * attn, oproj=L * oproj, lm=lm, ffw=ffw, mlp=mlp,
+                    total=L * (qkv + attn + oproj) + lm + ffw + mlp)
 
 
 CONFIGS = {

@@ -9,7 +9,9 @@ import numpy as np
 
 # New streams go at the end: child i of the spawn does not depend on the count.
 STREAMS = ["E", "Wq", "Wk", "Wv", "Wo", "K_pre", "V_pre", "x", "t", "z_mask", "z",
-           "W_gate", "W_up", "W_down"]
+           "W_gate", "W_up", "W_down",
+           "S_Wq", "S_Wk", "S_Wv", "S_Wo", "S_g_attn", "S_g_mlp", "S_g_final", "S_W_gate", "S_W_up",
+           "S_W_down", "S_K_pre", "S_V_pre"]
 
 
 def bf16_bits_from_f32(a):
@@ -45,10 +47,16 @@ def make_inputs(cfg, which=None):
     Layouts (row-major): E [V, d]; Wq [Hq*hd, d]; Wk, Wv [Hkv*hd, d];
     Wo [d, Hq*hd]; K_pre, V_pre [B, Hkv, P, hd]; x [B, C] int32;
     z [B, C, d]; t [B] float32 (per-canvas t when the config asks for it);
-    with a self-conditioning block of width F: W_gate, W_up [F, d], W_down [d, F].
+    with a self-conditioning block of width F: W_gate, W_up [F, d], W_down [d, F];
+    with a decoder stack of L layers and MLP width F: S_Wq [L, Hq*hd, d],
+    S_Wk, S_Wv [L, Hkv*hd, d], S_Wo [L, d, Hq*hd], S_g_attn, S_g_mlp [L, d],
+    S_g_final [d], S_W_gate, S_W_up [L, F, d], S_W_down [L, d, F],
+    S_K_pre, S_V_pre [L, B, Hkv, P, hd]. Norm gains ~ N(1, 0.1^2); the stack's
+    matrices ~ N(0, w_std^2).
     """
     names = which or (["E", "Wq", "Wk", "Wv", "Wo", "K_pre", "V_pre", "x", "t", "z"] +
-                      (["W_gate", "W_up", "W_down"] if cfg.ffw_hidden else []))
+                      (["W_gate", "W_up", "W_down"] if cfg.ffw_hidden else []) +
+                      (STREAMS[14:] if cfg.n_layers else []))
     out = Inputs()
     hq, hkv, hd = cfg.n_q_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim, cfg.head_dim
     shapes = {
@@ -60,13 +68,30 @@ def make_inputs(cfg, which=None):
         "K_pre": ((cfg.B, cfg.n_kv_heads, cfg.P, hd), cfg.kv_std),
         "V_pre": ((cfg.B, cfg.n_kv_heads, cfg.P, hd), cfg.kv_std),
     }
+    if cfg.n_layers:
+        L, Fm = cfg.n_layers, cfg.mlp_hidden
+        shapes.update({
+            "S_Wq": ((L, hq, cfg.d), cfg.w_std), "S_Wk": ((L, hkv, cfg.d), cfg.w_std),
+            "S_Wv": ((L, hkv, cfg.d), cfg.w_std), "S_Wo": ((L, cfg.d, hq), cfg.w_std),
+            "S_W_gate": ((L, Fm, cfg.d), cfg.w_std), "S_W_up": ((L, Fm, cfg.d), cfg.w_std),
+            "S_W_down": ((L, cfg.d, Fm), cfg.w_std),
+            "S_K_pre": ((L, cfg.B, cfg.n_kv_heads, cfg.P, hd), cfg.kv_std),
+            "S_V_pre": ((L, cfg.B, cfg.n_kv_heads, cfg.P, hd), cfg.kv_std)})
+    gains = {"S_g_attn": (cfg.n_layers, cfg.d), "S_g_mlp": (cfg.n_layers, cfg.d), "S_g_final": (cfg.d,)}
     if cfg.ffw_hidden:
         F = cfg.ffw_hidden
         shapes["W_gate"] = ((F, cfg.d), cfg.ffw_gain / np.sqrt(cfg.d))
         shapes["W_up"] = ((F, cfg.d), cfg.ffw_gain / np.sqrt(cfg.d))
         shapes["W_down"] = ((cfg.d, F), 1.0 / np.sqrt(F))
     for n in names:
-        if n in shapes:
+        if n in gains:
+            a = np.float32(1.0) + _normal(cfg, n, gains[n], 0.1)
+            if cfg.dtype == "bf16":
+                bits = bf16_bits_from_f32(a)
+                out[n + "_bits"] = bits
+                a = f32_from_bf16_bits(bits).reshape(gains[n])
+            out[n] = a
+        elif n in shapes:
             shape, std = shapes[n]
             a = _normal(cfg, n, shape, std)
             if cfg.dtype == "bf16":
