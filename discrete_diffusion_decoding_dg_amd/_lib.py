@@ -33,8 +33,14 @@ class dg_taps(ctypes.Structure):
                 ("p0E", ctypes.c_void_p)]
 
 
-NUM_STAGES = 9
-STAGES = ["embed", "qkv", "attention", "oproj", "lmhead", "combine", "corrupt", "ffw", "encode"]
+NUM_STAGES = 10
+STAGES = ["embed", "qkv", "attention", "oproj", "lmhead", "combine", "corrupt", "ffw", "encode",
+          "stack_mlp"]
+
+
+class dg_layer_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ["Wq", "Wk", "Wv", "Wo", "g_attn", "g_mlp", "W_gate", "W_up", "W_down"]]
 
 
 class dg_profile(ctypes.Structure):
@@ -44,7 +50,7 @@ class dg_profile(ctypes.Structure):
 EXPORTS = ["dg_create", "dg_destroy", "dg_workspace_bytes", "dg_corrupt", "dg_corrupt_batch",
            "dg_denoise_step", "dg_denoise_step_taps", "dg_generate_canvas",
            "dg_denoise_step_entropy", "dg_generate_canvas_entropy", "dg_set_ffw", "dg_ffw",
-           "dg_encode_kv", "dg_generate_blocks",
+           "dg_encode_kv", "dg_generate_blocks", "dg_set_stack",
            "dg_profile_enable",
            "dg_profile_read", "dg_status_string", "dg_last_error"]
 
@@ -82,6 +88,7 @@ def load_library():
     lib.dg_encode_kv.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     lib.dg_generate_blocks.argtypes = [vp, vp, vp, i32, i32, i32, u64, vp, vp]
     lib.dg_set_ffw.argtypes = [vp, i32, vp, vp, vp]
+    lib.dg_set_stack.argtypes = [vp, i32, i32, ctypes.POINTER(dg_layer_weights), vp]
     lib.dg_ffw.argtypes = [vp, vp, vp, vp]
     lib.dg_profile_enable.argtypes = [vp, ctypes.c_int]
     lib.dg_profile_read.argtypes = [vp, ctypes.POINTER(dg_profile)]
@@ -238,6 +245,22 @@ def dg_generate_blocks(model, K_cache, V_cache, P0, n_canvases, steps, seed, x_o
     _check(load_library().dg_generate_blocks(model.handle, _ptr(K_cache), _ptr(V_cache), int(P0),
                                              int(n_canvases), int(steps), int(seed), _ptr(x_out),
                                              _stream(stream)))
+
+
+def dg_set_stack(model, layers=None, g_final=None):
+    """Attach a decoder stack: `layers` is a list of dicts with tensors Wq, Wk,
+    Wv, Wo, g_attn, g_mlp, W_gate, W_up, W_down; no layers detach it. The
+    model keeps references to the tensors."""
+    if not layers:
+        _check(load_library().dg_set_stack(model.handle, 0, 0, None, None))
+        model._stack = None
+        return
+    names = [f[0] for f in dg_layer_weights._fields_]
+    arr = (dg_layer_weights * len(layers))(
+        *[dg_layer_weights(*[lw[n].data_ptr() for n in names]) for lw in layers])
+    _check(load_library().dg_set_stack(model.handle, len(layers), int(layers[0]["W_gate"].shape[0]), arr,
+                                       _ptr(g_final)))
+    model._stack = (layers, g_final)
 
 
 def dg_set_ffw(model, W_gate=None, W_up=None, W_down=None):

@@ -38,6 +38,8 @@ dg_status hip_fail(hipError_t e, const char *what) {
   } while (0)
 
 constexpr int kMaxSteps = 4096;
+constexpr float kRmsEps = 1e-6f;   // RMSNorm epsilon of the decoder stack
+constexpr int kMaxLayers = 256;
 constexpr int kPoll = 4;   // adaptive generation tests for early termination every kPoll steps
 constexpr size_t kAlign = 256;
 
@@ -186,6 +188,13 @@ struct dg_model {
   const void *ffw_wg = nullptr, *ffw_wu = nullptr, *ffw_wd = nullptr;
   char *ffw_mem = nullptr;   // owned: packed gate/up rows (bf16), u [R, d], hid [R, F]
   void *ffw_gu = nullptr, *ffw_u = nullptr, *ffw_hid = nullptr;
+  // decoder stack (dg_set_stack); st_L == 0 is the single attention block
+  int st_L = 0, st_F = 0;
+  std::vector<dg_layer_weights> st_w;
+  const void *st_gfinal = nullptr;
+  char *st_mem = nullptr;   // owned: packed gate/up rows (bf16), a, h_attn, two h [R, d], hid [R, F]
+  void *st_gu = nullptr, *st_a = nullptr, *st_ha = nullptr, *st_hb = nullptr, *st_hc = nullptr,
+       *st_hid = nullptr;
   // profiling: event pairs recorded around stage launches while enabled
   int prof_mask = 0;
   struct Mark {
@@ -244,11 +253,125 @@ dg_status run_ffw(dg_model *m, const void *u, void *z, const int32_t *frozen, co
   return DG_OK;
 }
 
+// One attention block: q, k, v = x W^T; attention over [prefix ; canvas];
+// out = res + o Wo^T (res may equal x). Stages 1-3 of the profile.
+dg_status attn_block(dg_model *m, const void *x, const void *res, const void *Wq, const void *Wk,
+                     const void *Wv, const void *Wo, const void *Kp, const void *Vp,
+                     const dg::Shape &sa, void *q, void *k, void *v, void *o, void *out,
+                     hipStream_t st) {
+  const dg::Shape &s = m->s;
+  if (m->cfg.dtype == DG_DTYPE_BF16) {
+    using u16 = uint16_t;
+    {
+      StageTimer tm(m, 1, st);
+      DG_HIP(dg::launch_qkv_bf16(static_cast<const u16 *>(x), static_cast<const u16 *>(Wq),
+                                 static_cast<const u16 *>(Wk), static_cast<const u16 *>(Wv), s,
+                                 static_cast<u16 *>(q), static_cast<u16 *>(k), static_cast<u16 *>(v), st),
+             "qkv launch");
+    }
+    {
+      StageTimer tm(m, 2, st);
+      DG_HIP(dg::launch_attention_bf16(static_cast<const u16 *>(q), static_cast<const u16 *>(k),
+                                       static_cast<const u16 *>(v), static_cast<const u16 *>(Kp),
+                                       static_cast<const u16 *>(Vp), sa, m->attn, static_cast<u16 *>(o), st),
+             "attention launch");
+    }
+    {
+      StageTimer tm(m, 3, st);
+      DG_HIP(dg::launch_residual_gemm_bf16(static_cast<const u16 *>(o), static_cast<const u16 *>(Wo),
+                                           static_cast<const u16 *>(res), s.R(), s.d, s.Hq * s.hd,
+                                           static_cast<u16 *>(out), st),
+             "out-projection launch");
+    }
+  } else {
+    {
+      StageTimer tm(m, 1, st);
+      DG_HIP(dg::launch_qkv_f32(static_cast<const float *>(x), static_cast<const float *>(Wq),
+                                static_cast<const float *>(Wk), static_cast<const float *>(Wv), s,
+                                static_cast<float *>(q), static_cast<float *>(k), static_cast<float *>(v), st),
+             "qkv launch");
+    }
+    {
+      StageTimer tm(m, 2, st);
+      DG_HIP(dg::launch_attention_f32(static_cast<const float *>(q), static_cast<const float *>(k),
+                                      static_cast<const float *>(v), static_cast<const float *>(Kp),
+                                      static_cast<const float *>(Vp), sa, static_cast<float *>(o), st),
+             "attention launch");
+    }
+    {
+      StageTimer tm(m, 3, st);
+      DG_HIP(dg::launch_oproj_f32(static_cast<const float *>(o), static_cast<const float *>(Wo),
+                                  static_cast<const float *>(res), s, static_cast<float *>(out), st),
+             "out-projection launch");
+    }
+  }
+  return DG_OK;
+}
+
+// The decoder stack from h0 (embedding + z) to the LM head's input hf:
+// per layer a = rmsnorm(h) g_attn; h = h + attention block(a); a =
+// rmsnorm(h) g_mlp; h = h + MLP(a); then hf = rmsnorm(h) g_final. Layer l
+// reads cache slice l of Kp, Vp ([L, B, Hkv, P, hd]). Stage 9 of the profile
+// covers the norms and the MLP.
+dg_status run_stack(dg_model *m, const void *h0, const void *Kp, const void *Vp, const dg::Shape &sa,
+                    void *q, void *k, void *v, void *o, void *hf, hipStream_t st) {
+  const dg::Shape &s = m->s;
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  const size_t es = bf16 ? 2 : 4;
+  const size_t cache = static_cast<size_t>(s.B) * s.Hkv * s.P * s.hd * es;
+  const int R = s.R(), d = s.d, F = m->st_F;
+  const void *h = h0;
+  void *hb[2] = {m->st_hb, m->st_hc};
+  for (int l = 0; l < m->st_L; ++l) {
+    const dg_layer_weights &lw = m->st_w[l];
+    {
+      StageTimer tm(m, 9, st);
+      DG_HIP(dg::launch_rmsnorm(bf16, h, lw.g_attn, R, d, kRmsEps, m->st_a, st), "norm launch");
+    }
+    if (dg_status e = attn_block(m, m->st_a, h, lw.Wq, lw.Wk, lw.Wv, lw.Wo,
+                                 static_cast<const char *>(Kp) + l * cache,
+                                 static_cast<const char *>(Vp) + l * cache, sa, q, k, v, o, m->st_ha, st))
+      return e;
+    StageTimer tm(m, 9, st);
+    DG_HIP(dg::launch_rmsnorm(bf16, m->st_ha, lw.g_mlp, R, d, kRmsEps, m->st_a, st), "norm launch");
+    void *hn = hb[l & 1];
+    if (bf16) {
+      using u16 = uint16_t;
+      const u16 *gu = static_cast<const u16 *>(m->st_gu) + static_cast<size_t>(l) * 2 * F * d;
+      DG_HIP(dg::launch_ffw_gate_up_bf16(static_cast<const u16 *>(m->st_a), gu, R, d, F,
+                                         static_cast<u16 *>(m->st_hid), st),
+             "MLP gate/up launch");
+      DG_HIP(dg::launch_residual_gemm_bf16(static_cast<const u16 *>(m->st_hid),
+                                           static_cast<const u16 *>(lw.W_down),
+                                           static_cast<const u16 *>(m->st_ha), R, d, F,
+                                           static_cast<u16 *>(hn), st),
+             "MLP down launch");
+    } else {
+      DG_HIP(dg::launch_ffw_gate_up_f32(static_cast<const float *>(m->st_a),
+                                        static_cast<const float *>(lw.W_gate),
+                                        static_cast<const float *>(lw.W_up), R, d, F,
+                                        static_cast<float *>(m->st_hid), st),
+             "MLP gate/up launch");
+      DG_HIP(dg::launch_ffw_down_f32(static_cast<const float *>(m->st_hid),
+                                     static_cast<const float *>(lw.W_down), R, d, F, s.C, nullptr,
+                                     nullptr, static_cast<float *>(hn), st,
+                                     static_cast<const float *>(m->st_ha)),
+             "MLP down launch");
+    }
+    h = hn;
+  }
+  StageTimer tm(m, 9, st);
+  DG_HIP(dg::launch_rmsnorm(bf16, h, m->st_gfinal, R, d, kRmsEps, hf, st), "norm launch");
+  return DG_OK;
+}
+
 // prm: device step constants of every canvas; when n_inline > 0 the embedding
 // launch first stores them there from the host array `inline_prm`.
 // With `ent` the step is the entropy-bounded one: every row draws and the
 // merge writes per-row entropy, draw and argmax to *ent (the select kernel
 // then produces the tokens); rows of canvases marked in `frozen` keep z_t.
+// With a decoder stack attached the body between the embedding and the LM
+// head is the stack, and h1 holds the final normalised activation.
 dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void *Kp,
                    const void *Vp, dg::StepParams *prm, const dg::StepParams *inline_prm,
                    int n_inline, uint64_t seed, int32_t *x_out, void *z_out,
@@ -284,30 +407,15 @@ dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void 
                             st),
            "embed launch");
   }
+  if (m->st_L) {
+    if (dg_status e = run_stack(m, h0, Kp, Vp, sa, q, k, v, o, h1, st)) return e;
+  } else {
+    if (dg_status e = attn_block(m, h0, h0, m->w.Wq, m->w.Wk, m->w.Wv, m->w.Wo, Kp, Vp, sa, q, k, v, o,
+                                 h1, st))
+      return e;
+  }
   if (bf16) {
     using u16 = uint16_t;
-    {
-      StageTimer tm(m, 1, st);
-      DG_HIP(dg::launch_qkv_bf16(static_cast<const u16 *>(h0), static_cast<const u16 *>(m->w.Wq),
-                               static_cast<const u16 *>(m->w.Wk), static_cast<const u16 *>(m->w.Wv),
-                               s, static_cast<u16 *>(q), static_cast<u16 *>(k),
-                               static_cast<u16 *>(v), st),
-           "qkv launch");
-    }
-    {
-      StageTimer tm(m, 2, st);
-      DG_HIP(dg::launch_attention_bf16(static_cast<const u16 *>(q), static_cast<const u16 *>(k),
-                                     static_cast<const u16 *>(v), static_cast<const u16 *>(Kp),
-                                     static_cast<const u16 *>(Vp), sa, m->attn,
-                                     static_cast<u16 *>(o), st),
-           "attention launch");
-    }
-    {
-      StageTimer tm(m, 3, st);
-      DG_HIP(dg::launch_oproj_bf16(static_cast<const u16 *>(o), static_cast<const u16 *>(m->w.Wo),
-                                 static_cast<const u16 *>(h0), s, static_cast<u16 *>(h1), st),
-           "out-projection launch");
-    }
     {
       StageTimer tm(m, 4, st);
       DG_HIP(dg::launch_lmhead_bf16(static_cast<const u16 *>(h1), static_cast<const u16 *>(m->w.E),
@@ -321,27 +429,6 @@ dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void 
            "combine launch");
     }
   } else {
-    {
-      StageTimer tm(m, 1, st);
-      DG_HIP(dg::launch_qkv_f32(static_cast<const float *>(h0), static_cast<const float *>(m->w.Wq),
-                              static_cast<const float *>(m->w.Wk),
-                              static_cast<const float *>(m->w.Wv), s, static_cast<float *>(q),
-                              static_cast<float *>(k), static_cast<float *>(v), st),
-           "qkv launch");
-    }
-    {
-      StageTimer tm(m, 2, st);
-      DG_HIP(dg::launch_attention_f32(static_cast<const float *>(q), static_cast<const float *>(k),
-                                    static_cast<const float *>(v), static_cast<const float *>(Kp),
-                                    static_cast<const float *>(Vp), sa, static_cast<float *>(o), st),
-           "attention launch");
-    }
-    {
-      StageTimer tm(m, 3, st);
-      DG_HIP(dg::launch_oproj_f32(static_cast<const float *>(o), static_cast<const float *>(m->w.Wo),
-                                static_cast<const float *>(h0), s, static_cast<float *>(h1), st),
-           "out-projection launch");
-    }
     {
       StageTimer tm(m, 4, st);
       DG_HIP(dg::launch_lmhead_f32(static_cast<const float *>(h1), static_cast<const float *>(m->w.E),
@@ -570,6 +657,7 @@ dg_status dg_destroy(dg_model *m) {
   }
   hipError_t f = hipFree(m->ws);
   if (m->ffw_mem) (void)hipFree(m->ffw_mem);
+  if (m->st_mem) (void)hipFree(m->st_mem);
   if (m->host_stopped) (void)hipHostFree(m->host_stopped);
   delete m;
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
@@ -707,6 +795,80 @@ dg_status dg_set_ffw(dg_model *m, int32_t hidden, const void *W_gate, const void
   return DG_OK;
 }
 
+dg_status dg_set_stack(dg_model *m, int32_t n_layers, int32_t mlp_hidden,
+                       const dg_layer_weights *layers, const void *g_final) {
+  g_err.clear();
+  if (dg_status s = check_model(m)) return s;
+  const dg::Shape &s = m->s;
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  if (n_layers < 0 || n_layers > kMaxLayers)
+    return fail(DG_ERR_INVALID_ARG, "n_layers must be in [0, %d] (got %d)", kMaxLayers, n_layers);
+  if (n_layers > 0) {
+    if (!layers || !g_final) return fail(DG_ERR_INVALID_ARG, "layers and g_final must be non-NULL");
+    if (mlp_hidden < 1) return fail(DG_ERR_INVALID_ARG, "mlp_hidden must be >= 1 (got %d)", mlp_hidden);
+    if (static_cast<int64_t>(s.R()) * mlp_hidden >= (int64_t(1) << 31) ||
+        static_cast<int64_t>(mlp_hidden) * s.d >= (int64_t(1) << 31))
+      return fail(DG_ERR_INVALID_ARG, "B*C*mlp_hidden and mlp_hidden*d must be < 2^31");
+    if (bf16 && (mlp_hidden % 64 != 0 || s.d % 64 != 0))
+      return fail(DG_ERR_UNSUPPORTED, "the bf16 MLP kernels need mlp_hidden %% 64 == 0 (got %d)", mlp_hidden);
+    if (!aligned16(g_final)) return fail(DG_ERR_INVALID_ARG, "g_final must be 16-byte aligned");
+    for (int l = 0; l < n_layers; ++l) {
+      const dg_layer_weights &w = layers[l];
+      const void *p[9] = {w.Wq, w.Wk, w.Wv, w.Wo, w.g_attn, w.g_mlp, w.W_gate, w.W_up, w.W_down};
+      for (const void *x : p) {
+        if (!x) return fail(DG_ERR_INVALID_ARG, "a weight pointer of layer %d is NULL", l);
+        if (!aligned16(x)) return fail(DG_ERR_INVALID_ARG, "weight pointers of layer %d must be 16-byte aligned", l);
+      }
+    }
+  }
+  // queued steps may still read the old stack
+  DG_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize");
+  if (m->st_mem) {
+    DG_HIP(hipFree(m->st_mem), "hipFree");
+    m->st_mem = nullptr;
+  }
+  m->st_L = m->st_F = 0;
+  m->st_w.clear();
+  m->st_gfinal = nullptr;
+  m->st_gu = m->st_a = m->st_ha = m->st_hb = m->st_hc = m->st_hid = nullptr;
+  if (n_layers == 0) return DG_OK;
+
+  const size_t es = bf16 ? 2 : 4;
+  const size_t R = static_cast<size_t>(s.R()), F = static_cast<size_t>(mlp_hidden), d = static_cast<size_t>(s.d);
+  const size_t n_gu = bf16 ? align_up(static_cast<size_t>(n_layers) * 2 * F * d * es) : 0;
+  const size_t n_act = align_up(R * d * es), n_hid = align_up(R * F * es);
+  char *mem = nullptr;
+  hipError_t e = hipMalloc(&mem, n_gu + 4 * n_act + n_hid);
+  if (e != hipSuccess)
+    return fail(DG_ERR_OOM, "decoder stack buffers of %zu bytes: %s", n_gu + 4 * n_act + n_hid, hipGetErrorString(e));
+  if (bf16) {
+    // per layer, gate/up rows interleaved in groups of 32 (the GEGLU GEMM's layout)
+    const size_t grp = 32 * d * es;
+    for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
+      char *dst = mem + static_cast<size_t>(l) * 2 * F * d * es;
+      e = hipMemcpy2D(dst, 2 * grp, layers[l].W_gate, grp, grp, F / 32, hipMemcpyDeviceToDevice);
+      if (e == hipSuccess) e = hipMemcpy2D(dst + grp, 2 * grp, layers[l].W_up, grp, grp, F / 32, hipMemcpyDeviceToDevice);
+    }
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      (void)hipFree(mem);
+      return hip_fail(e, "MLP weight packing");
+    }
+  }
+  m->st_mem = mem;
+  m->st_L = n_layers;
+  m->st_F = mlp_hidden;
+  m->st_w.assign(layers, layers + n_layers);
+  m->st_gfinal = g_final;
+  m->st_gu = bf16 ? mem : nullptr;
+  m->st_a = mem + n_gu;
+  m->st_ha = mem + n_gu + n_act;
+  m->st_hb = mem + n_gu + 2 * n_act;
+  m->st_hc = mem + n_gu + 3 * n_act;
+  m->st_hid = mem + n_gu + 4 * n_act;
+  return DG_OK;
+}
+
 dg_status dg_ffw(dg_model *m, const void *u, void *z_out, void *stream) {
   g_err.clear();
   if (dg_status s = check_model(m)) return s;
@@ -756,6 +918,8 @@ dg_status dg_encode_kv(dg_model *m, const int32_t *tokens, int32_t n, int32_t po
   const dg::Shape &s = m->s;
   if (n < 0 || pos < 0 || static_cast<int64_t>(pos) + n > s.P)
     return fail(DG_ERR_INVALID_ARG, "need n >= 0, pos >= 0 and pos + n <= P (n=%d pos=%d P=%d)", n, pos, s.P);
+  if (m->st_L)
+    return fail(DG_ERR_UNSUPPORTED, "cache entries of a multi-layer stack need its causal encoder pass (not built)");
   if (n == 0) return DG_OK;
   if (!tokens || !K_cache || !V_cache) return fail(DG_ERR_INVALID_ARG, "tokens, K_cache and V_cache must be non-NULL");
   const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
@@ -775,6 +939,8 @@ dg_status dg_generate_blocks(dg_model *m, void *K_cache, void *V_cache, int32_t 
     return fail(DG_ERR_INVALID_ARG, "need n_canvases >= 1, P0 >= 0 and P0 + n_canvases * C <= P "
                 "(P0=%d n_canvases=%d C=%d P=%d)", P0, n_canvases, s.C, s.P);
   if (!K_cache || !V_cache) return fail(DG_ERR_INVALID_ARG, "K_cache and V_cache must be non-NULL");
+  if (m->st_L)
+    return fail(DG_ERR_UNSUPPORTED, "block generation with a multi-layer stack needs its causal encoder pass (not built)");
   if (steps < 1 || steps > kMaxSteps)
     return fail(DG_ERR_INVALID_ARG, "steps must be in [1, %d] (got %d)", kMaxSteps, steps);
   const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;

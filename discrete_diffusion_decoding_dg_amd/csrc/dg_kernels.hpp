@@ -59,6 +59,9 @@ hipError_t launch_embed(bool bf16, const void *E, const int32_t *x, const void *
 // h [B * n, d] = E[x[b * ld + i]] for i < n (no self-conditioning input).
 hipError_t launch_embed_tokens(bool bf16, const void *E, const int32_t *x, int ld, int B, int n,
                                int d, int V, void *h, hipStream_t st);
+// y [R, d] = round(x / sqrt(mean(x^2) + eps) * g) per row.
+hipError_t launch_rmsnorm(bool bf16, const void *x, const void *g, int R, int d, float eps, void *y,
+                          hipStream_t st);
 // p0[r, v] = exp(p0[r, v] - lse[r]) in place (p0 holds scaled logits on entry).
 hipError_t launch_p0_from_logits(float *p0, const float *lse, int R, int V, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
@@ -72,6 +75,9 @@ hipError_t launch_set_floats(float *dst, const float *src, int n, hipStream_t st
 hipError_t launch_qkv_bf16(const uint16_t *h0, const uint16_t *Wq, const uint16_t *Wk,
                            const uint16_t *Wv, const Shape &s, uint16_t *q, uint16_t *k,
                            uint16_t *v, hipStream_t st);
+// out [M, N] = res + A W^T (A [M, K], W [N, K]).
+hipError_t launch_residual_gemm_bf16(const uint16_t *A, const uint16_t *W, const uint16_t *res, int M,
+                                    int N, int K, uint16_t *out, hipStream_t st);
 // h1 [R, d] = h0 + o Wo^T.
 hipError_t launch_oproj_bf16(const uint16_t *o, const uint16_t *Wo, const uint16_t *h0,
                              const Shape &s, uint16_t *h1, hipStream_t st);
@@ -130,8 +136,10 @@ hipError_t launch_oproj_f32(const float *o, const float *Wo, const float *h0, co
 size_t lmhead_f32_workspace_bytes(const Shape &s);
 hipError_t launch_ffw_gate_up_f32(const float *u, const float *Wg, const float *Wu, int M, int d,
                                   int F, float *hid, hipStream_t st);
+// z = res + hid Wd^T (res may be null: 0).
 hipError_t launch_ffw_down_f32(const float *hid, const float *Wd, int M, int d, int F, int C,
-                               const int32_t *frozen, const float *z_t, float *z, hipStream_t st);
+                               const int32_t *frozen, const float *z_t, float *z, hipStream_t st,
+                               const float *res = nullptr);
 hipError_t launch_lmhead_f32(const float *h1, const float *E, const StepParams *prm,
                              const Shape &s, uint64_t seed, void *work, float *p0, bool entropy,
                              hipStream_t st);

@@ -123,6 +123,43 @@ __global__ void __launch_bounds__(256) embed_bf16_vec_kernel(const uint16_t *__r
   }
 }
 
+// RMSNorm of the decoder stack: y = round(x / sqrt(mean(x^2) + eps) * g), one
+// block per row, fp32 sums.
+template <typename T>
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const T *__restrict__ x,
+                                                      const T *__restrict__ g, int d, float eps,
+                                                      T *__restrict__ y) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const T *xr = x + static_cast<int64_t>(r) * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) {
+    const float v = Act<T>::load(xr, c);
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = 1.f / sqrtf(tot / static_cast<float>(d) + eps);
+  T *yr = y + static_cast<int64_t>(r) * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x)
+    Act<T>::store(yr, c, Act<T>::load(xr, c) * inv * Act<T>::load(g, c));
+}
+
+hipError_t launch_rmsnorm(bool bf16, const void *x, const void *g, int R, int d, float eps, void *y,
+                          hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(rmsnorm_kernel<uint16_t>, dim3(R), dim3(256), 0, st,
+                       static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(g), d, eps,
+                       static_cast<uint16_t *>(y));
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(R), dim3(256), 0, st, static_cast<const float *>(x),
+                       static_cast<const float *>(g), d, eps, static_cast<float *>(y));
+  return hipGetLastError();
+}
+
 // Token rows for the encoder: row m = b * n + i embeds x[b * ld + i] (a token
 // outside [0, V) reads as a zero row).
 template <typename T>

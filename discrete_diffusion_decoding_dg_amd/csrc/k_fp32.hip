@@ -177,12 +177,14 @@ __global__ void __launch_bounds__(256) ffw_gate_up_f32_kernel(const float *__res
   }
 }
 
-// z[m, n] = hid_m . Wd_n; rows of canvases marked in `frozen` copy z_t.
+// z[m, n] = res[m, n] + hid_m . Wd_n (res nullable: 0); rows of canvases
+// marked in `frozen` copy z_t.
 __global__ void __launch_bounds__(256) ffw_down_f32_kernel(const float *__restrict__ hid,
                                                            const float *__restrict__ Wd, int R, int d,
                                                            int F, int C,
                                                            const int32_t *__restrict__ frozen,
                                                            const float *__restrict__ zt,
+                                                           const float *__restrict__ res,
                                                            float *__restrict__ z) {
   const int64_t total = static_cast<int64_t>(R) * d;
   for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
@@ -196,7 +198,7 @@ __global__ void __launch_bounds__(256) ffw_down_f32_kernel(const float *__restri
     const float *w = Wd + static_cast<int64_t>(n) * F;
     float acc = 0.f;
     for (int c = 0; c < F; ++c) acc = fmaf(x[c], w[c], acc);
-    z[idx] = acc;
+    z[idx] = res ? res[idx] + acc : acc;
   }
 }
 
@@ -398,13 +400,14 @@ hipError_t launch_ffw_gate_up_f32(const float *u, const float *Wg, const float *
 }
 
 hipError_t launch_ffw_down_f32(const float *hid, const float *Wd, int M, int d, int F, int C,
-                               const int32_t *frozen, const float *z_t, float *z, hipStream_t st) {
+                               const int32_t *frozen, const float *z_t, float *z, hipStream_t st,
+                               const float *res) {
   const int64_t total = static_cast<int64_t>(M) * d;
   if (total == 0) return hipSuccess;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 16384) blocks = 16384;
   hipLaunchKernelGGL(ffw_down_f32_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, hid,
-                     Wd, M, d, F, C, frozen, z_t, z);
+                     Wd, M, d, F, C, frozen, z_t, res, z);
   return hipGetLastError();
 }
 

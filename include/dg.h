@@ -249,6 +249,38 @@ dg_status dg_generate_blocks(dg_model *m, void *K_cache, void *V_cache, int32_t 
 dg_status dg_set_ffw(dg_model *m, int32_t hidden, const void *W_gate, const void *W_up,
                      const void *W_down);
 
+/* Multi-layer decoder stack (the TR summary's decoder is a deep transformer
+ * whose layers the pages do not describe; this stand-in uses the Gemma
+ * family's pre-norm layout with the parts of the single block). With a stack
+ * of L layers attached, every step and generation computes, from
+ * h = E[x] + z:
+ *   per layer l: a = rmsnorm(h) g_attn; q, k, v = a W^T; attention over
+ *   [cache slice l ; canvas]; h = h + o Wo^T; a = rmsnorm(h) g_mlp;
+ *   h = h + W_down (gelu(W_gate a) * (W_up a));
+ *   LM head input = rmsnorm(h_L) g_final;
+ * rmsnorm(x) = x / sqrt(mean(x^2) + 1e-6), everything rounded to act at each
+ * tensor. K_pre / V_pre of the step and generation calls are then
+ * [L, B, Hkv, P, hd] (one cache slice per layer). dg_weights' Wq..Wo are not
+ * used while a stack is attached (E still is). Taps: h0 is the embedding,
+ * q, k, v, o those of the last layer, h1 the LM head's input.
+ *   layers: host array [n_layers] of device pointers in act dtype, 16-byte
+ *   aligned, caller-owned and unchanged while attached: Wq..Wo as dg_weights,
+ *   g_attn, g_mlp [d], W_gate, W_up [mlp_hidden, d], W_down [d, mlp_hidden];
+ *   g_final [d]. n_layers = 0 detaches (the single block again).
+ * The library allocates the stack's activations and, for bf16, a copy of
+ * each layer's W_gate/W_up with rows interleaved in groups of 32; waits for
+ * the device (set-up call). bf16 needs mlp_hidden % 64 == 0
+ * (DG_ERR_UNSUPPORTED). dg_encode_kv and dg_generate_blocks return
+ * DG_ERR_UNSUPPORTED while a stack is attached (its cache entries need the
+ * stack's causal encoder pass, which is not built). */
+typedef struct dg_layer_weights {
+  const void *Wq, *Wk, *Wv, *Wo;
+  const void *g_attn, *g_mlp;
+  const void *W_gate, *W_up, *W_down;
+} dg_layer_weights;
+dg_status dg_set_stack(dg_model *m, int32_t n_layers, int32_t mlp_hidden,
+                       const dg_layer_weights *layers, const void *g_final);
+
 /* z_out [B,C,d] act = FFW(u) for u [B,C,d] act through the attached block
  * (DG_ERR_INVALID_ARG if none); z_out must not overlap u. */
 dg_status dg_ffw(dg_model *m, const void *u, void *z_out, void *stream);
@@ -258,13 +290,14 @@ dg_status dg_ffw(dg_model *m, const void *u, void *z_out, void *stream);
  * Stages: 0 embed, 1 q/k/v projection, 2 attention (+ split merge),
  * 3 output projection, 4 LM head (logits, softmax statistics, z partials,
  * Gumbel argmax), 5 split merge + Step select, 6 corruption, 7 feed-forward
- * self-conditioning block, 8 encoder (prefill / commit).
+ * self-conditioning block, 8 encoder (prefill / commit), 9 decoder-stack norms
+ * and MLPs (the stack's attention blocks count under 1-3).
  * dg_profile_enable(m, mask) times the stages whose bit (1 << stage) is set
  * in mask (0 turns profiling off; every event pair adds a few microseconds of
  * queue time between kernels, so time only the stages you need).
  * dg_profile_read waits for the recorded events, returns the summed
  * milliseconds and the number of timed launches per stage, and clears them. */
-#define DG_NUM_STAGES 9
+#define DG_NUM_STAGES 10
 typedef struct dg_profile {
   double ms[DG_NUM_STAGES];
   int64_t count[DG_NUM_STAGES];
