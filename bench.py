@@ -112,6 +112,7 @@ def main():
     ap.add_argument("--no-corrupt", action="store_true")
     ap.add_argument("--no-ffw", action="store_true", help="skip the feed-forward block timings")
     ap.add_argument("--no-blocks", action="store_true", help="skip the block-autoregressive timings")
+    ap.add_argument("--no-stack", action="store_true", help="skip the decoder-stack timings")
     ap.add_argument("--copy-mib", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device to device three times (a plain copy kernel "
                          "of known size, to scale HBM byte counters)")
@@ -315,6 +316,50 @@ def main():
         mb.close()
         del Kc, Vc
 
+    # the step through a 4-layer pre-norm stack with gated MLPs of width 4 d
+    # (per-layer caches of the workload's prefix length); not part of `value`
+    stack_res = None
+    if not args.no_stack and 4 * cfg.B * cfg.n_kv_heads * cfg.P * cfg.head_dim <= (64 << 20):
+        L = 4
+        cs = cfg.with_(n_layers=L, mlp_hidden=4 * cfg.d)
+        names = ["S_Wq", "S_Wk", "S_Wv", "S_Wo", "S_g_attn", "S_g_mlp", "S_g_final", "S_W_gate",
+                 "S_W_up", "S_W_down", "S_K_pre", "S_V_pre"]
+        sin = make_inputs(cs, names)
+        sdev = {n: to_dev(sin, n, cs) for n in names}
+        layers = [{n: sdev["S_" + n][l].contiguous() for n in
+                   ["Wq", "Wk", "Wv", "Wo", "g_attn", "g_mlp", "W_gate", "W_up", "W_down"]} for l in range(L)]
+        dg.dg_set_stack(model, layers, sdev["S_g_final"])
+        Ks, Vs = sdev["S_K_pre"], sdev["S_V_pre"]
+
+        def sstep(k):
+            a, b = k & 1, (k & 1) ^ 1
+            dg.dg_denoise_step(model, xs[a], zs[a], Ks, Vs, tvec(k), dt, 3000 + k, xs[b], zs[b])
+
+        nsteps = min(args.steps, 50)
+        for k in range(args.warmup):
+            sstep(k)
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for k in range(nsteps):
+            sstep(k)
+        s1.record()
+        torch.cuda.synchronize()
+        dg.dg_profile_read(model)
+        dg.dg_profile_enable(model, None)
+        for k in range(10):
+            sstep(k)
+        torch.cuda.synchronize()
+        dg.dg_profile_enable(model, [])
+        sp = dg.dg_profile_read(model)
+        dg.dg_set_stack(model)
+        sfl = cs.flops_per_step()
+        sms = s0.elapsed_time(s1) / nsteps
+        stack_res = {"layers": L, "mlp_hidden": 4 * cfg.d, "ms_per_step": sms,
+                     "step_tflops": sfl["total"] / (sms * 1e-3) / 1e12,
+                     "stage_ms_per_step": {k: v[0] / 10 for k, v in sp.items() if v[1]}}
+        del layers, sdev, Ks, Vs
+
     fl = cfg.flops_per_step()
     lm_ms, lm_n = prof["lmhead"]
     lm_avg_ms = lm_ms / max(1, lm_n)
@@ -356,6 +401,8 @@ def main():
         result["ffw_block"] = ffw_res
     if blocks_res is not None:
         result["blocks"] = blocks_res
+    if stack_res is not None:
+        result["stack"] = stack_res
     if not args.no_corrupt:
         result["corrupt"] = corrupt_bandwidth()
     model.close()

@@ -78,9 +78,6 @@ hipError_t launch_qkv_bf16(const uint16_t *h0, const uint16_t *Wq, const uint16_
 // out [M, N] = res + A W^T (A [M, K], W [N, K]).
 hipError_t launch_residual_gemm_bf16(const uint16_t *A, const uint16_t *W, const uint16_t *res, int M,
                                     int N, int K, uint16_t *out, hipStream_t st);
-// h1 [R, d] = h0 + o Wo^T.
-hipError_t launch_oproj_bf16(const uint16_t *o, const uint16_t *Wo, const uint16_t *h0,
-                             const Shape &s, uint16_t *h1, hipStream_t st);
 
 // ---- gated self-conditioning block z = FFW(u) (k_gemm.hip bf16 MFMA) ----
 // hid [M, F] = round(gelu(u Wg^T) * (u Wu^T)) from the packed gate/up matrix

@@ -770,22 +770,4 @@ hipError_t launch_residual_gemm_bf16(const uint16_t *A, const uint16_t *W, const
   return hipGetLastError();
 }
 
-hipError_t launch_oproj_bf16(const uint16_t *o, const uint16_t *Wo, const uint16_t *h0,
-                             const Shape &s, uint16_t *h1, hipStream_t st) {
-  ResidualEpi epi{Wo, h0, h1, s.d};
-  const int M = s.R(), N = s.d, K = s.Hq * s.hd;
-  if (M == 0) return hipSuccess;
-  dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
-  if (M >= kBigRows && K % big::BKB == 0 && N % big::BNB == 0)
-    hipLaunchKernelGGL(big::gemm_big_kernel<ResidualEpi>, dim3(N / big::BNB, (M + big::BMB - 1) / big::BMB),
-                       dim3(512), 0, st, o, M, N, K, epi);
-  else if (K % skinny::BK == 0)
-    return skinny::launch(o, M, N, K, epi, st);
-  else if (K % 64 == 0)
-    hipLaunchKernelGGL(gemm_tn_bf16_dma_kernel<ResidualEpi>, grid, dim3(512), 0, st, o, M, N, K, epi);
-  else
-    hipLaunchKernelGGL(gemm_tn_bf16_kernel<ResidualEpi>, grid, dim3(256), 0, st, o, M, N, K, epi);
-  return hipGetLastError();
-}
-
 }  // namespace dg
