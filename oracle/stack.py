@@ -12,6 +12,13 @@ family's pre-norm layout. Readings:
         h = h + attention(q, [K_l ; k], [V_l ; v]) Wo_l^T,
         m = rmsnorm(h) g_mlp_l,    h = h + W_down_l (gelu(W_gate_l m) * (W_up_l m));
     with rmsnorm(x) = x / sqrt(mean(x^2) + 1e-6), no biases;
+  * mixture-of-experts variant of the MLP (the pages' model routes each
+    token to a few of many experts; they give no routing rule): router
+    logits r = m W_router^T in float32, the top_k experts by logit (ties to
+    the lower expert index), weights = softmax over the top_k selected
+    logits, h = h + sum_j w_j W_down_e (gelu(W_gate_e m) * (W_up_e m)) with
+    each expert's hidden activations rounded to act and the weighted sum
+    rounded once into h;
   * the LM head reads rmsnorm(h_L) g_final through the tied embedding;
   * everything after the logits (temperature, p0, z = FFW(p0 E), Step) is
     the single block's.
@@ -38,6 +45,35 @@ def rmsnorm(x, g, act):
     return round_act(x * r * np.asarray(g, np.float64), act)
 
 
+def route(m, W_router, top_k):
+    """Experts [R, top_k] (by float32 logit, ties to the lower index) and
+    their softmax weights [R, top_k] (float64), plus the float32 logits."""
+    r = (np.asarray(m, np.float64) @ np.asarray(W_router, np.float64).T).astype(np.float32)
+    X = r.shape[1]
+    idx = np.broadcast_to(np.arange(X), r.shape)
+    order = np.lexsort((idx, -r.astype(np.float64)), axis=1)
+    sel = order[:, :top_k]
+    lg = np.take_along_axis(r, sel, axis=1).astype(np.float64)
+    e = np.exp(lg - lg.max(axis=1, keepdims=True))
+    return sel, e / e.sum(axis=1, keepdims=True), r
+
+
+def moe_mlp(m, W_router, W_gate, W_up, W_down, top_k, act):
+    """sum_j w_j expert_{e_j}(m) per row of m [R, d] (float64, unrounded)."""
+    sel, wts, _ = route(m, W_router, top_k)
+    out = np.zeros_like(np.asarray(m, np.float64))
+    for e in range(np.shape(W_router)[0]):
+        rows, slot = np.nonzero(sel == e)
+        if rows.size == 0:
+            continue
+        x = np.asarray(m, np.float64)[rows]
+        g = x @ np.asarray(W_gate[e], np.float64).T
+        u = x @ np.asarray(W_up[e], np.float64).T
+        hid = round_act(gelu_tanh(g) * u, act)
+        out[rows] += wts[rows, slot][:, None] * (hid @ np.asarray(W_down[e], np.float64).T)
+    return out
+
+
 def layer(cfg, lw, h, K_pre, V_pre):
     """One pre-norm layer on h [B, C, d]; returns (h_out, parts)."""
     act = cfg.dtype
@@ -51,18 +87,22 @@ def layer(cfg, lw, h, K_pre, V_pre):
     o = attention(q, k, v, K_pre, V_pre, act)
     h1 = round_act(h + (o.reshape(B * C, Hq * hd) @ np.asarray(lw["Wo"], np.float64).T).reshape(B, C, d), act)
     m = rmsnorm(h1, lw["g_mlp"], act).reshape(B * C, d)
-    g = m @ np.asarray(lw["W_gate"], np.float64).T
-    u = m @ np.asarray(lw["W_up"], np.float64).T
-    hid = round_act(gelu_tanh(g) * u, act)
-    h2 = round_act(h1 + (hid @ np.asarray(lw["W_down"], np.float64).T).reshape(B, C, d), act)
+    if lw.get("W_router") is not None:
+        y = moe_mlp(m, lw["W_router"], lw["W_gate"], lw["W_up"], lw["W_down"], lw["top_k"], act)
+    else:
+        g = m @ np.asarray(lw["W_gate"], np.float64).T
+        u = m @ np.asarray(lw["W_up"], np.float64).T
+        y = round_act(gelu_tanh(g) * u, act) @ np.asarray(lw["W_down"], np.float64).T
+    h2 = round_act(h1 + y.reshape(B, C, d), act)
     return h2, dict(a=a, q=q, k=k, v=v, o=o, h_attn=h1, m=m.reshape(B, C, d), h=h2)
 
 
 def stack_step(cfg, w, sw, x_t, z_t, K_pre, V_pre, t, dt, seed, canvas_ids=None):
     """One denoising step through the stack. `w` holds E (and optionally the
     FFW block); `sw` holds the per-layer weights as lists (Wq, Wk, Wv, Wo,
-    g_attn, g_mlp, W_gate, W_up, W_down) and g_final; K_pre, V_pre are
-    [L, B, Hkv, P, hd]."""
+    g_attn, g_mlp, W_gate, W_up, W_down; with experts also W_router and the
+    expert-major W_gate, W_up [X, F, d], W_down [X, d, F]) and g_final (and
+    top_k with experts); K_pre, V_pre are [L, B, Hkv, P, hd]."""
     act = cfg.dtype
     Bp = x_t.shape[0]
     cid = np.arange(Bp) if canvas_ids is None else np.asarray(canvas_ids)
@@ -73,6 +113,8 @@ def stack_step(cfg, w, sw, x_t, z_t, K_pre, V_pre, t, dt, seed, canvas_ids=None)
     layers = []
     for l in range(len(sw["Wq"])):
         lw = {n: sw[n][l] for n in ["Wq", "Wk", "Wv", "Wo", "g_attn", "g_mlp", "W_gate", "W_up", "W_down"]}
+        if sw.get("W_router") is not None:
+            lw["W_router"], lw["top_k"] = sw["W_router"][l], sw["top_k"]
         h, parts = layer(cfg, lw, h, K_pre[l], V_pre[l])
         layers.append(parts)
     hf = rmsnorm(h, sw["g_final"], act)

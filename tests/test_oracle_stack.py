@@ -92,3 +92,53 @@ def test_layers_apply_in_order_with_their_own_caches():
     r2 = stack_step(cfg, {"E": inp["E"]}, sw, inp["x"], inp["z"], inp["S_K_pre"][::-1], inp["S_V_pre"][::-1],
                     t, 0.125, 3)
     assert not np.array_equal(r2["layers"][1]["h"], r["layers"][1]["h"])
+
+
+def test_route_picks_top_k_with_ties_to_the_lower_expert():
+    from oracle.stack import route
+    W = np.eye(4)
+    m = np.array([[0.5, 2.0, 2.0, -1.0],      # tie between experts 1 and 2
+                  [3.0, 1.0, 2.0, 0.0]])
+    sel, w, r = route(m, W, 2)
+    assert sel.tolist() == [[1, 2], [0, 2]]
+    assert np.allclose(w.sum(axis=1), 1.0)
+    assert np.allclose(w[1], np.exp([3.0, 2.0]) / np.exp([3.0, 2.0]).sum())
+    # brute force on random logits
+    rng = np.random.default_rng(3)
+    m = rng.standard_normal((50, 6))
+    W = rng.standard_normal((8, 6))
+    sel, w, r = route(m, W, 3)
+    for i in range(50):
+        want = sorted(range(8), key=lambda e: (-float(r[i, e]), e))[:3]
+        assert sel[i].tolist() == want
+
+
+def _expert_brute(x, Wg, Wu, Wd):
+    c = math.sqrt(2 / math.pi)
+    hid = []
+    for f in range(Wg.shape[0]):
+        g = float(np.dot(Wg[f], x))
+        u = float(np.dot(Wu[f], x))
+        hid.append(0.5 * g * (1 + math.tanh(c * (g + 0.044715 * g ** 3))) * u)
+    return np.array([sum(float(Wd[e, f]) * hid[f] for f in range(len(hid))) for e in range(Wd.shape[0])])
+
+
+def test_moe_mlp_against_brute_force_and_special_cases():
+    from oracle.stack import moe_mlp, route
+    rng = np.random.default_rng(4)
+    R, d, F, X = 5, 6, 7, 4
+    m = rng.standard_normal((R, d))
+    Wr = rng.standard_normal((X, d))
+    Wg, Wu = rng.standard_normal((X, F, d)), rng.standard_normal((X, F, d))
+    Wd = rng.standard_normal((X, d, F))
+    for k in (1, 2, X):
+        got = moe_mlp(m, Wr, Wg, Wu, Wd, k, "f64")
+        sel, w, r = route(m, Wr, k)
+        for i in range(R):
+            want = sum(w[i, j] * _expert_brute(m[i], Wg[sel[i, j]], Wu[sel[i, j]], Wd[sel[i, j]])
+                       for j in range(k))
+            assert np.allclose(got[i], want, rtol=1e-12, atol=1e-12)
+    # one expert, top-1: the dense gated MLP
+    one = moe_mlp(m, Wr[:1], Wg[:1], Wu[:1], Wd[:1], 1, "f64")
+    from oracle import ffw
+    assert np.allclose(one, ffw(m, Wg[0], Wu[0], Wd[0], "f64"), rtol=1e-12, atol=1e-12)

@@ -34,7 +34,9 @@ class Config:
     ffw_hidden: int = 0           # width F of the gated self-conditioning block (0: identity)
     ffw_gain: float = 1.0         # W_gate, W_up ~ N(0, (gain / sqrt(d))^2); W_down ~ N(0, 1 / F)
     n_layers: int = 0             # layers of the pre-norm decoder stack (0: the single block)
-    mlp_hidden: int = 0           # hidden width of each stack layer's gated MLP
+    mlp_hidden: int = 0           # hidden width of each stack layer's gated MLP (per expert)
+    n_experts: int = 0            # experts of each stack layer's MLP (0: one dense MLP)
+    top_k: int = 0                # experts per token
 
     @property
     def R(self):
@@ -57,7 +59,7 @@ class Config:
         lm = 4 * R * self.V * d
         ffw = 6 * R * d * self.ffw_hidden
         L = max(1, self.n_layers)
-        mlp = 6 * R * d * self.mlp_hidden * self.n_layers
+        mlp = 6 * R * d * self.mlp_hidden * self.n_layers * (self.top_k if self.n_experts else 1)
         return dict(qkv=L * qkv, attn=L * attn, oproj=L * oproj, lm=lm, ffw=ffw, mlp=mlp,
                     total=L * (qkv + attn + oproj) + lm + ffw + mlp)
 

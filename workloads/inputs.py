@@ -11,7 +11,7 @@ import numpy as np
 STREAMS = ["E", "Wq", "Wk", "Wv", "Wo", "K_pre", "V_pre", "x", "t", "z_mask", "z",
            "W_gate", "W_up", "W_down",
            "S_Wq", "S_Wk", "S_Wv", "S_Wo", "S_g_attn", "S_g_mlp", "S_g_final", "S_W_gate", "S_W_up",
-           "S_W_down", "S_K_pre", "S_V_pre"]
+           "S_W_down", "S_K_pre", "S_V_pre", "S_W_router"]
 
 
 def bf16_bits_from_f32(a):
@@ -51,12 +51,15 @@ def make_inputs(cfg, which=None):
     with a decoder stack of L layers and MLP width F: S_Wq [L, Hq*hd, d],
     S_Wk, S_Wv [L, Hkv*hd, d], S_Wo [L, d, Hq*hd], S_g_attn, S_g_mlp [L, d],
     S_g_final [d], S_W_gate, S_W_up [L, F, d], S_W_down [L, d, F],
-    S_K_pre, S_V_pre [L, B, Hkv, P, hd]. Norm gains ~ N(1, 0.1^2); the stack's
-    matrices ~ N(0, w_std^2).
+    S_K_pre, S_V_pre [L, B, Hkv, P, hd]; with X experts per layer the MLP
+    weights are expert-major (S_W_gate, S_W_up [L, X, F, d], S_W_down
+    [L, X, d, F]) and S_W_router is [L, X, d]. Norm gains ~ N(1, 0.1^2); the
+    stack's matrices ~ N(0, w_std^2).
     """
     names = which or (["E", "Wq", "Wk", "Wv", "Wo", "K_pre", "V_pre", "x", "t", "z"] +
                       (["W_gate", "W_up", "W_down"] if cfg.ffw_hidden else []) +
-                      (STREAMS[14:] if cfg.n_layers else []))
+                      (STREAMS[14:26] if cfg.n_layers else []) +
+                      (["S_W_router"] if cfg.n_layers and cfg.n_experts else []))
     out = Inputs()
     hq, hkv, hd = cfg.n_q_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim, cfg.head_dim
     shapes = {
@@ -75,8 +78,13 @@ def make_inputs(cfg, which=None):
             "S_Wv": ((L, hkv, cfg.d), cfg.w_std), "S_Wo": ((L, cfg.d, hq), cfg.w_std),
             "S_W_gate": ((L, Fm, cfg.d), cfg.w_std), "S_W_up": ((L, Fm, cfg.d), cfg.w_std),
             "S_W_down": ((L, cfg.d, Fm), cfg.w_std),
+            "S_W_router": ((L, max(1, cfg.n_experts), cfg.d), cfg.w_std),
             "S_K_pre": ((L, cfg.B, cfg.n_kv_heads, cfg.P, hd), cfg.kv_std),
             "S_V_pre": ((L, cfg.B, cfg.n_kv_heads, cfg.P, hd), cfg.kv_std)})
+        if cfg.n_experts:
+            X = cfg.n_experts
+            shapes.update({"S_W_gate": ((L, X, Fm, cfg.d), cfg.w_std), "S_W_up": ((L, X, Fm, cfg.d), cfg.w_std),
+                           "S_W_down": ((L, X, cfg.d, Fm), cfg.w_std)})
     gains = {"S_g_attn": (cfg.n_layers, cfg.d), "S_g_mlp": (cfg.n_layers, cfg.d), "S_g_final": (cfg.d,)}
     if cfg.ffw_hidden:
         F = cfg.ffw_hidden
