@@ -50,7 +50,7 @@ class dg_profile(ctypes.Structure):
 EXPORTS = ["dg_create", "dg_destroy", "dg_workspace_bytes", "dg_corrupt", "dg_corrupt_batch",
            "dg_denoise_step", "dg_denoise_step_taps", "dg_generate_canvas",
            "dg_denoise_step_entropy", "dg_generate_canvas_entropy", "dg_set_ffw", "dg_ffw",
-           "dg_encode_kv", "dg_generate_blocks", "dg_set_stack",
+           "dg_encode_kv", "dg_generate_blocks", "dg_set_stack", "dg_set_stack_moe",
            "dg_profile_enable",
            "dg_profile_read", "dg_status_string", "dg_last_error"]
 
@@ -89,6 +89,8 @@ def load_library():
     lib.dg_generate_blocks.argtypes = [vp, vp, vp, i32, i32, i32, u64, vp, vp]
     lib.dg_set_ffw.argtypes = [vp, i32, vp, vp, vp]
     lib.dg_set_stack.argtypes = [vp, i32, i32, ctypes.POINTER(dg_layer_weights), vp]
+    lib.dg_set_stack_moe.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(dg_layer_weights),
+                                     ctypes.POINTER(vp), vp]
     lib.dg_ffw.argtypes = [vp, vp, vp, vp]
     lib.dg_profile_enable.argtypes = [vp, ctypes.c_int]
     lib.dg_profile_read.argtypes = [vp, ctypes.POINTER(dg_profile)]
@@ -247,10 +249,11 @@ def dg_generate_blocks(model, K_cache, V_cache, P0, n_canvases, steps, seed, x_o
                                              _stream(stream)))
 
 
-def dg_set_stack(model, layers=None, g_final=None):
+def dg_set_stack(model, layers=None, g_final=None, top_k=0):
     """Attach a decoder stack: `layers` is a list of dicts with tensors Wq, Wk,
-    Wv, Wo, g_attn, g_mlp, W_gate, W_up, W_down; no layers detach it. The
-    model keeps references to the tensors."""
+    Wv, Wo, g_attn, g_mlp, W_gate, W_up, W_down (and W_router with experts:
+    then W_gate/W_up are [X, F, d], W_down [X, d, F], and top_k > 0); no
+    layers detach it. The model keeps references to the tensors."""
     if not layers:
         _check(load_library().dg_set_stack(model.handle, 0, 0, None, None))
         model._stack = None
@@ -258,8 +261,14 @@ def dg_set_stack(model, layers=None, g_final=None):
     names = [f[0] for f in dg_layer_weights._fields_]
     arr = (dg_layer_weights * len(layers))(
         *[dg_layer_weights(*[lw[n].data_ptr() for n in names]) for lw in layers])
-    _check(load_library().dg_set_stack(model.handle, len(layers), int(layers[0]["W_gate"].shape[0]), arr,
-                                       _ptr(g_final)))
+    if layers[0].get("W_router") is not None:
+        X, F = int(layers[0]["W_router"].shape[0]), int(layers[0]["W_gate"].shape[1])
+        routers = (ctypes.c_void_p * len(layers))(*[lw["W_router"].data_ptr() for lw in layers])
+        _check(load_library().dg_set_stack_moe(model.handle, len(layers), F, X, int(top_k), arr, routers,
+                                               _ptr(g_final)))
+    else:
+        _check(load_library().dg_set_stack(model.handle, len(layers), int(layers[0]["W_gate"].shape[0]),
+                                           arr, _ptr(g_final)))
     model._stack = (layers, g_final)
 
 

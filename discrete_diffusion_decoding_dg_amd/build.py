@@ -18,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["dg_api.cpp", "k_elementwise.hip", "k_gemm.hip", "k_attention.hip", "k_lmhead.hip",
-           "k_combine.hip", "k_fp32.hip", "k_select.hip"]
+           "k_combine.hip", "k_fp32.hip", "k_select.hip", "k_moe.hip"]
 
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -195,6 +195,11 @@ struct dg_model {
   char *st_mem = nullptr;   // owned: packed gate/up rows (bf16), a, h_attn, two h [R, d], hid [R, F]
   void *st_gu = nullptr, *st_a = nullptr, *st_ha = nullptr, *st_hb = nullptr, *st_hc = nullptr,
        *st_hid = nullptr;
+  // mixture of experts in the stack's MLPs (st_X == 0: dense)
+  int st_X = 0, st_k = 0;
+  std::vector<const void *> st_wr;   // routers [X, d] per layer
+  int32_t *st_sel = nullptr, *st_list = nullptr, *st_offs = nullptr, *st_toff = nullptr;
+  float *st_wts = nullptr, *st_y = nullptr;
   // profiling: event pairs recorded around stage launches while enabled
   int prof_mask = 0;
   struct Mark {
@@ -335,7 +340,30 @@ dg_status run_stack(dg_model *m, const void *h0, const void *Kp, const void *Vp,
     StageTimer tm(m, 9, st);
     DG_HIP(dg::launch_rmsnorm(bf16, m->st_ha, lw.g_mlp, R, d, kRmsEps, m->st_a, st), "norm launch");
     void *hn = hb[l & 1];
-    if (bf16) {
+    if (m->st_X) {
+      // mixture of experts: route, group, expert GEMMs, weighted combine
+      const int X = m->st_X, K = m->st_k;
+      DG_HIP(dg::launch_moe_route(bf16, m->st_a, m->st_wr[l], R, d, X, K, m->st_sel, m->st_wts,
+                                  bf16 ? m->st_list : nullptr, m->st_offs, m->st_toff, st),
+             "router launch");
+      if (bf16) {
+        using u16 = uint16_t;
+        const u16 *gu = static_cast<const u16 *>(m->st_gu) + static_cast<size_t>(l) * X * 2 * F * d;
+        DG_HIP(dg::launch_moe_experts_bf16(static_cast<const u16 *>(m->st_a), gu,
+                                           static_cast<const u16 *>(lw.W_down), m->st_list, m->st_offs,
+                                           m->st_toff, R, K, X, d, F, static_cast<u16 *>(m->st_hid),
+                                           m->st_y, st),
+               "expert GEMM launch");
+      } else {
+        DG_HIP(dg::launch_moe_experts_f32(static_cast<const float *>(m->st_a), m->st_sel,
+                                          static_cast<const float *>(lw.W_gate),
+                                          static_cast<const float *>(lw.W_up),
+                                          static_cast<const float *>(lw.W_down), R * K, K, d, F,
+                                          static_cast<float *>(m->st_hid), m->st_y, st),
+               "expert launch");
+      }
+      DG_HIP(dg::launch_moe_combine(bf16, m->st_ha, m->st_y, m->st_wts, R, d, K, hn, st), "combine launch");
+    } else if (bf16) {
       using u16 = uint16_t;
       const u16 *gu = static_cast<const u16 *>(m->st_gu) + static_cast<size_t>(l) * 2 * F * d;
       DG_HIP(dg::launch_ffw_gate_up_bf16(static_cast<const u16 *>(m->st_a), gu, R, d, F,
@@ -797,10 +825,30 @@ dg_status dg_set_ffw(dg_model *m, int32_t hidden, const void *W_gate, const void
 
 dg_status dg_set_stack(dg_model *m, int32_t n_layers, int32_t mlp_hidden,
                        const dg_layer_weights *layers, const void *g_final) {
+  return dg_set_stack_moe(m, n_layers, mlp_hidden, 0, 0, layers, nullptr, g_final);
+}
+
+dg_status dg_set_stack_moe(dg_model *m, int32_t n_layers, int32_t mlp_hidden, int32_t n_experts,
+                           int32_t top_k, const dg_layer_weights *layers,
+                           const void *const *W_router, const void *g_final) {
   g_err.clear();
   if (dg_status s = check_model(m)) return s;
   const dg::Shape &s = m->s;
   const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  if (n_experts < 0 || n_experts > dg::kMoeMaxExperts)
+    return fail(DG_ERR_INVALID_ARG, "n_experts must be in [0, %d] (got %d)", dg::kMoeMaxExperts, n_experts);
+  if (n_experts > 0 && (top_k < 1 || top_k > n_experts))
+    return fail(DG_ERR_INVALID_ARG, "top_k must be in [1, n_experts] (got %d)", top_k);
+  if (n_layers > 0 && n_experts > 0) {
+    if (!W_router) return fail(DG_ERR_INVALID_ARG, "W_router is NULL");
+    for (int l = 0; l < n_layers; ++l)
+      if (!W_router[l] || !aligned16(W_router[l]))
+        return fail(DG_ERR_INVALID_ARG, "router of layer %d is NULL or not 16-byte aligned", l);
+    if (bf16 && (mlp_hidden % 128 != 0 || s.d % 128 != 0))
+      return fail(DG_ERR_UNSUPPORTED, "the bf16 expert kernels need mlp_hidden %% 128 == 0 (got %d)", mlp_hidden);
+    if (static_cast<int64_t>(s.R()) * top_k * (mlp_hidden > s.d ? mlp_hidden : s.d) >= (int64_t(1) << 31))
+      return fail(DG_ERR_INVALID_ARG, "B*C*top_k*max(mlp_hidden, d) must be < 2^31");
+  }
   if (n_layers < 0 || n_layers > kMaxLayers)
     return fail(DG_ERR_INVALID_ARG, "n_layers must be in [0, %d] (got %d)", kMaxLayers, n_layers);
   if (n_layers > 0) {
@@ -827,28 +875,39 @@ dg_status dg_set_stack(dg_model *m, int32_t n_layers, int32_t mlp_hidden,
     DG_HIP(hipFree(m->st_mem), "hipFree");
     m->st_mem = nullptr;
   }
-  m->st_L = m->st_F = 0;
+  m->st_L = m->st_F = m->st_X = m->st_k = 0;
   m->st_w.clear();
+  m->st_wr.clear();
   m->st_gfinal = nullptr;
   m->st_gu = m->st_a = m->st_ha = m->st_hb = m->st_hc = m->st_hid = nullptr;
+  m->st_sel = m->st_list = m->st_offs = m->st_toff = nullptr;
+  m->st_wts = m->st_y = nullptr;
   if (n_layers == 0) return DG_OK;
 
   const size_t es = bf16 ? 2 : 4;
   const size_t R = static_cast<size_t>(s.R()), F = static_cast<size_t>(mlp_hidden), d = static_cast<size_t>(s.d);
-  const size_t n_gu = bf16 ? align_up(static_cast<size_t>(n_layers) * 2 * F * d * es) : 0;
-  const size_t n_act = align_up(R * d * es), n_hid = align_up(R * F * es);
+  const size_t X = static_cast<size_t>(n_experts), NX = n_experts ? X : 1;   // MLPs per layer
+  const size_t Q = n_experts ? R * static_cast<size_t>(top_k) : R;            // rows of the hidden activations
+  const size_t n_gu = bf16 ? align_up(static_cast<size_t>(n_layers) * NX * 2 * F * d * es) : 0;
+  const size_t n_act = align_up(R * d * es), n_hid = align_up(Q * F * es);
+  const size_t n_moe = n_experts ? align_up(Q * 4) * 3 + align_up((X + 1) * 4) * 2 + align_up(Q * d * 4) : 0;
+  const size_t total = n_gu + 4 * n_act + n_hid + n_moe;
   char *mem = nullptr;
-  hipError_t e = hipMalloc(&mem, n_gu + 4 * n_act + n_hid);
+  hipError_t e = hipMalloc(&mem, total);
   if (e != hipSuccess)
-    return fail(DG_ERR_OOM, "decoder stack buffers of %zu bytes: %s", n_gu + 4 * n_act + n_hid, hipGetErrorString(e));
+    return fail(DG_ERR_OOM, "decoder stack buffers of %zu bytes: %s", total, hipGetErrorString(e));
   if (bf16) {
-    // per layer, gate/up rows interleaved in groups of 32 (the GEGLU GEMM's layout)
-    const size_t grp = 32 * d * es;
-    for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
-      char *dst = mem + static_cast<size_t>(l) * 2 * F * d * es;
-      e = hipMemcpy2D(dst, 2 * grp, layers[l].W_gate, grp, grp, F / 32, hipMemcpyDeviceToDevice);
-      if (e == hipSuccess) e = hipMemcpy2D(dst + grp, 2 * grp, layers[l].W_up, grp, grp, F / 32, hipMemcpyDeviceToDevice);
-    }
+    // per layer and expert, gate/up rows interleaved in groups of 32 (the
+    // GEGLU GEMM's layout); experts' matrices follow each other
+    const size_t grp = 32 * d * es, mat = F * d * es;
+    for (int l = 0; l < n_layers && e == hipSuccess; ++l)
+      for (size_t x = 0; x < NX && e == hipSuccess; ++x) {
+        char *dst = mem + (static_cast<size_t>(l) * NX + x) * 2 * mat;
+        const char *wg = static_cast<const char *>(layers[l].W_gate) + x * mat;
+        const char *wu = static_cast<const char *>(layers[l].W_up) + x * mat;
+        e = hipMemcpy2D(dst, 2 * grp, wg, grp, grp, F / 32, hipMemcpyDeviceToDevice);
+        if (e == hipSuccess) e = hipMemcpy2D(dst + grp, 2 * grp, wu, grp, grp, F / 32, hipMemcpyDeviceToDevice);
+      }
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
       (void)hipFree(mem);
@@ -866,6 +925,18 @@ dg_status dg_set_stack(dg_model *m, int32_t n_layers, int32_t mlp_hidden,
   m->st_hb = mem + n_gu + 2 * n_act;
   m->st_hc = mem + n_gu + 3 * n_act;
   m->st_hid = mem + n_gu + 4 * n_act;
+  if (n_experts) {
+    char *p = mem + n_gu + 4 * n_act + n_hid;
+    m->st_sel = reinterpret_cast<int32_t *>(p); p += align_up(Q * 4);
+    m->st_list = reinterpret_cast<int32_t *>(p); p += align_up(Q * 4);
+    m->st_wts = reinterpret_cast<float *>(p); p += align_up(Q * 4);
+    m->st_offs = reinterpret_cast<int32_t *>(p); p += align_up((X + 1) * 4);
+    m->st_toff = reinterpret_cast<int32_t *>(p); p += align_up((X + 1) * 4);
+    m->st_y = reinterpret_cast<float *>(p);
+    m->st_X = n_experts;
+    m->st_k = top_k;
+    m->st_wr.assign(W_router, W_router + n_layers);
+  }
   return DG_OK;
 }
 

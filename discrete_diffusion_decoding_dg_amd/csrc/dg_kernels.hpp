@@ -99,6 +99,32 @@ hipError_t launch_kv_encode_bf16(const uint16_t *h, const uint16_t *Wk, const ui
                                  const Shape &s, int n, int pos, int Pst, uint16_t *K, uint16_t *V,
                                  hipStream_t st);
 
+// ---- mixture-of-experts MLP (k_moe.hip; expert GEMMs in k_gemm.hip) ----
+constexpr int kMoeMaxExperts = 64;
+constexpr int kMoeTile = 64;   // rows per expert tile of the grouped GEMMs
+// Router logits of m [R, d] against Wr [X, d], top_k experts per token (ties
+// to the lower expert) with softmax weights: sel, wts [R * top_k]. With list
+// non-null, also the entries q = token * top_k + slot grouped by expert
+// (list [R * top_k]), entry offsets offs [X + 1] and kMoeTile-row tile
+// offsets toff [X + 1].
+hipError_t launch_moe_route(bool bf16, const void *m, const void *Wr, int R, int d, int X, int top_k,
+                            int32_t *sel, float *wts, int32_t *list, int32_t *offs, int32_t *toff,
+                            hipStream_t st);
+// Expert GEMMs over the grouped entries: hid [R * top_k, F] = round(gelu(.) *
+// (.)) from the packed gate/up rows of each expert (Wgu [X, 2F, d]), and
+// y [R * top_k, d] = hid Wd_e^T in fp32 (Wd [X, d, F]). d, F % 128 == 0.
+hipError_t launch_moe_experts_bf16(const uint16_t *m, const uint16_t *Wgu, const uint16_t *Wd,
+                                   const int32_t *list, const int32_t *offs, const int32_t *toff,
+                                   int R, int top_k, int X, int d, int F, uint16_t *hid, float *y,
+                                   hipStream_t st);
+// fp32 experts directly from sel (no grouping): hid [n, F], y [n, d].
+hipError_t launch_moe_experts_f32(const float *m, const int32_t *sel, const float *Wg, const float *Wu,
+                                  const float *Wd, int n, int top_k, int d, int F, float *hid, float *y,
+                                  hipStream_t st);
+// out [R, d] = round(h + sum_j wts[r, j] y[r * top_k + j]).
+hipError_t launch_moe_combine(bool bf16, const void *h, const float *y, const float *wts, int R, int d,
+                              int top_k, void *out, hipStream_t st);
+
 // ---- k_attention.hip (bf16 MFMA) ----
 int attention_splits(const Shape &s);
 size_t attention_workspace_bytes(const Shape &s);

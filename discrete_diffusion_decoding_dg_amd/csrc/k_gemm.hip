@@ -92,6 +92,16 @@ struct KvCacheEpi {
   }
 };
 
+// Plain fp32 store of C = A B^T [M, N] (expert down projections).
+struct F32StoreEpi {
+  static constexpr bool kPair = false;
+  const uint16_t *W;
+  float *out;
+  int N;
+  __device__ const uint16_t *brow(int n, int K) const { return W + static_cast<int64_t>(n) * K; }
+  __device__ void store(int m, int n, float acc) const { out[static_cast<int64_t>(m) * N + n] = acc; }
+};
+
 // Gate and up projections of the self-conditioning block in one GEMM over
 // the packed matrix W [2F, K]: rows 64 j + [0, 32) are gate rows 32 j + [0, 32)
 // and rows 64 j + 32 + [0, 32) the up rows of the same hidden units, so a
@@ -547,9 +557,49 @@ struct Cfg {
   static constexpr int DMA = (BM + BN) / 32;                  // direct loads per wave and slab
 };
 
-template <class Epi, int BN>
-__global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__restrict__ A, int M,
-                                                          int N, int K, Epi epi) {
+// Row sources of a block's 64-row tile: begin(tm) sets up row tile tm (false:
+// the block has no rows), a_row(r) is the A row of tile row r (always a valid
+// row: padding rows repeat a valid one), out(r) the output row (-1: padding),
+// and b_off the element offset of the B matrix.
+struct DenseRows {   // rows m0 .. m0 + 63 of an [M, K] matrix
+  int M;
+  int m0 = 0;
+  int64_t b_off = 0;
+  __device__ bool begin(int tm) {
+    m0 = tm * BM;
+    return true;
+  }
+  __device__ int a_row(int r) const { return m0 + r < M ? m0 + r : M - 1; }
+  __device__ int out(int r) const { return m0 + r < M ? m0 + r : -1; }
+};
+
+// Mixture of experts: the (token, slot) entries routed to each expert are
+// listed expert by expert (list, with offsets offs[X + 1]); expert e owns
+// row tiles toff[e] .. toff[e + 1] - 1 and its B matrix sits bstride elements
+// after expert e - 1's. The A row of entry q is q / adiv (the token for the
+// gate/up GEMM, the entry itself for the down GEMM); outputs go to row q.
+struct GroupRows {
+  const int32_t *list, *offs, *toff;
+  int X, adiv;
+  int64_t bstride;
+  int base = 0, cnt = 0;
+  int64_t b_off = 0;
+  __device__ bool begin(int tm) {
+    if (tm >= toff[X]) return false;
+    int e = 0;
+    while (toff[e + 1] <= tm) ++e;
+    base = offs[e] + BM * (tm - toff[e]);
+    cnt = offs[e + 1] - base < BM ? offs[e + 1] - base : BM;
+    b_off = e * bstride;
+    return true;
+  }
+  __device__ int a_row(int r) const { return list[base + (r < cnt ? r : cnt - 1)] / adiv; }
+  __device__ int out(int r) const { return r < cnt ? list[base + r] : -1; }
+};
+
+template <class Epi, int BN, class Rows>
+__global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__restrict__ A, Rows rows,
+                                                          int mt, int N, int K, Epi epi) {
   using G = Cfg<BN>;
   constexpr int NR = BN / 32;                       // 32-column blocks per tile
   constexpr int NS = G::NS, PITCH = G::PITCH;
@@ -562,14 +612,14 @@ __global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__rest
   int bid = blockIdx.x;
   const int nblk = gridDim.x;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int mt = (M + BM - 1) / BM;
   const int tn = bid / mt, tm = bid - tn * mt;
-  const int m0 = tm * BM, n0 = tn * BN;
+  if (!rows.begin(tm)) return;                      // uniform over the block, before any barrier
+  const int n0 = tn * BN;
 
   // loads: one direct load fills 4 slab rows (1 KB); the slab's A rows and
   // then its B rows are dealt to the waves, G::DMA loads each. Lane i fills
-  // row 4 g + i / 16 at physical piece i % 16. Rows past M (N) re-read the
-  // last valid row; their results are never stored.
+  // row 4 g + i / 16 at physical piece i % 16. Padding rows (past the tile's
+  // rows or past N) re-read a valid row; their results are never stored.
   const uint16_t *src[G::DMA];
   int dst[G::DMA];
 #pragma unroll
@@ -578,11 +628,10 @@ __global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__rest
     const int r = 4 * g + (lane >> 4);              // slab row, A rows first
     const int lp = (lane & 15) ^ (r & 15);          // logical piece this lane fetches
     if (r < BM) {
-      const int m = (m0 + r < M) ? m0 + r : M - 1;
-      src[j] = A + static_cast<int64_t>(m) * K + 8 * lp;
+      src[j] = A + static_cast<int64_t>(rows.a_row(r)) * K + 8 * lp;
     } else {
       const int n = (n0 + r - BM < N) ? n0 + r - BM : N - 1;
-      src[j] = epi.brow(n, K) + 8 * lp;
+      src[j] = epi.brow(n, K) + rows.b_off + 8 * lp;
     }
     dst[j] = 4 * g * BK;                            // element offset of the load within a stage
   }
@@ -647,31 +696,38 @@ __global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__rest
     static_assert(BN == 64, "gate/up pairs need 64-column tiles");
     for (int e = tid; e < BM * 32; e += 512) {
       const int r = e >> 5, col = e & 31;
-      const int m = m0 + r, n = n0 + col;
-      if (m < M && n < N) epi.store_pair(m, n, sum8(r, col), sum8(r, col + 32));
+      const int m = rows.out(r), n = n0 + col;
+      if (m >= 0 && n < N) epi.store_pair(m, n, sum8(r, col), sum8(r, col + 32));
     }
   } else {
     for (int e = tid; e < BM * BN; e += 512) {
       const int r = e / BN, col = e - r * BN;
-      const int m = m0 + r, n = n0 + col;
-      if (m < M && n < N) epi.store(m, n, sum8(r, col));
+      const int m = rows.out(r), n = n0 + col;
+      if (m >= 0 && n < N) epi.store(m, n, sum8(r, col));
     }
   }
 }
 
 // 64-column tiles (fewest operand bytes per output) once they cover most of
 // the 256 CUs, 32-column ones below that (twice the tiles). K % 128 == 0.
-template <class Epi>
-hipError_t launch(const uint16_t *A, int M, int N, int K, const Epi &epi, hipStream_t st) {
-  const int mt = (M + BM - 1) / BM;
+template <class Epi, class Rows>
+hipError_t launch_rows(const uint16_t *A, const Rows &rows, int mt, int N, int K, const Epi &epi,
+                       hipStream_t st) {
   if (Epi::kPair || static_cast<int64_t>(mt) * ((N + 63) / 64) >= 160) {
     const int blocks = mt * ((N + 63) / 64);
-    hipLaunchKernelGGL((gemm_skinny_kernel<Epi, 64>), dim3(blocks), dim3(512), 0, st, A, M, N, K, epi);
+    hipLaunchKernelGGL((gemm_skinny_kernel<Epi, 64, Rows>), dim3(blocks), dim3(512), 0, st, A, rows, mt,
+                       N, K, epi);
   } else if constexpr (!Epi::kPair) {
     const int blocks = mt * ((N + 31) / 32);
-    hipLaunchKernelGGL((gemm_skinny_kernel<Epi, 32>), dim3(blocks), dim3(512), 0, st, A, M, N, K, epi);
+    hipLaunchKernelGGL((gemm_skinny_kernel<Epi, 32, Rows>), dim3(blocks), dim3(512), 0, st, A, rows, mt,
+                       N, K, epi);
   }
   return hipGetLastError();
+}
+
+template <class Epi>
+hipError_t launch(const uint16_t *A, int M, int N, int K, const Epi &epi, hipStream_t st) {
+  return launch_rows(A, DenseRows{M}, (M + BM - 1) / BM, N, K, epi, st);
 }
 }  // namespace skinny
 
@@ -716,6 +772,23 @@ hipError_t launch_kv_encode_bf16(const uint16_t *h, const uint16_t *Wk, const ui
     hipLaunchKernelGGL(gemm_tn_bf16_kernel<KvCacheEpi>, dim3((N + BN - 1) / BN, (M + BM - 1) / BM),
                        dim3(256), 0, st, h, M, N, s.d, epi);
   return hipGetLastError();
+}
+
+hipError_t launch_moe_experts_bf16(const uint16_t *m, const uint16_t *Wgu, const uint16_t *Wd,
+                                   const int32_t *list, const int32_t *offs, const int32_t *toff,
+                                   int R, int top_k, int X, int d, int F, uint16_t *hid, float *y,
+                                   hipStream_t st) {
+  static_assert(skinny::BM == kMoeTile, "expert tiles are the few-row kernel's row tiles");
+  const int n = R * top_k;
+  if (n == 0) return hipSuccess;
+  if (d % skinny::BK != 0 || F % skinny::BK != 0) return hipErrorInvalidValue;
+  // every expert's last tile may be partial: at most n / 64 + X row tiles
+  const int mt = (n + kMoeTile - 1) / kMoeTile + X;
+  skinny::GroupRows gu{list, offs, toff, X, top_k, static_cast<int64_t>(2) * F * d};
+  hipError_t e = skinny::launch_rows(m, gu, mt, 2 * F, d, GegluEpi{Wgu, hid, F}, st);
+  if (e != hipSuccess) return e;
+  skinny::GroupRows dn{list, offs, toff, X, 1, static_cast<int64_t>(d) * F};
+  return skinny::launch_rows(hid, dn, mt, d, F, F32StoreEpi{Wd, y, d}, st);
 }
 
 hipError_t launch_ffw_gate_up_bf16(const uint16_t *u, const uint16_t *Wgu, int M, int d, int F,

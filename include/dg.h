@@ -281,6 +281,22 @@ typedef struct dg_layer_weights {
 dg_status dg_set_stack(dg_model *m, int32_t n_layers, int32_t mlp_hidden,
                        const dg_layer_weights *layers, const void *g_final);
 
+/* dg_set_stack with a mixture of experts in every layer's MLP (the TR
+ * summary's model is a sparse mixture of experts that activates a few of
+ * many experts per token; the routing rule is a reading): router logits
+ * r = a W_router^T in fp32, the top_k experts by logit (ties to the lower
+ * expert), weights = softmax over the selected logits, and the MLP output
+ * sum_j w_j W_down_e (gelu(W_gate_e a) * (W_up_e a)) (each expert's hidden
+ * activations rounded to act, the weighted sum rounded once into h).
+ *   layers[l].W_gate, W_up: [n_experts, mlp_hidden, d], W_down:
+ *   [n_experts, d, mlp_hidden] (expert-major); W_router: host array
+ *   [n_layers] of device pointers [n_experts, d]. 1 <= top_k <= n_experts
+ *   <= 64. bf16 needs mlp_hidden % 128 == 0 and d % 128 == 0
+ *   (DG_ERR_UNSUPPORTED). n_experts = 0 is dg_set_stack. */
+dg_status dg_set_stack_moe(dg_model *m, int32_t n_layers, int32_t mlp_hidden, int32_t n_experts,
+                           int32_t top_k, const dg_layer_weights *layers,
+                           const void *const *W_router, const void *g_final);
+
 /* z_out [B,C,d] act = FFW(u) for u [B,C,d] act through the attached block
  * (DG_ERR_INVALID_ARG if none); z_out must not overlap u. */
 dg_status dg_ffw(dg_model *m, const void *u, void *z_out, void *stream);

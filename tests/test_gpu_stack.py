@@ -161,3 +161,96 @@ def test_detach_restores_the_single_block_and_unsupported_calls():
     m.close()
     del keep
     assert np.array_equal(a["x_out"], b["x_out"]) and np.array_equal(a["z_out"], b["z_out"])
+
+
+MOE = {
+    # fp32: one and two layers, 4 experts, top 2
+    "c1-moe-L1": dict(base="c1", n_layers=1, mlp_hidden=48, n_experts=4, top_k=2),
+    "c1-moe-L2": dict(base="c1", n_layers=2, mlp_hidden=48, n_experts=4, top_k=2),
+    # bf16, 8 experts, top 2, ragged rows
+    "bf16-moe-L1": dict(base="c2", B=2, C=40, P=100, d=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                        V=4096, n_layers=1, mlp_hidden=256, n_experts=8, top_k=2),
+    # bf16, two layers with every expert selected (no routing decision to drift)
+    "bf16-moe-L2-all": dict(base="c2", B=2, C=40, P=100, d=256, n_q_heads=4, n_kv_heads=2,
+                            head_dim=64, V=4096, n_layers=2, mlp_hidden=128, n_experts=4, top_k=4),
+    # 2250 tokens routed over 4 experts: many expert tiles, partial last tiles;
+    # with zero output projections the experts see the embedding itself, so
+    # the GPU's routing input equals the oracle's up to one norm's rounding
+    "bf16-moe-rows2250-wo0": dict(base="c5", B=9, C=250, P=70, d=256, n_q_heads=4, n_kv_heads=4,
+                                  head_dim=64, V=4096, n_layers=1, mlp_hidden=256, n_experts=4, top_k=2,
+                                  zero_wo=True),
+    "bf16-moe-rows2250": dict(base="c5", B=9, C=250, P=70, d=256, n_q_heads=4, n_kv_heads=4,
+                              head_dim=64, V=4096, n_layers=1, mlp_hidden=256, n_experts=4, top_k=2),
+    # width 2816, top 1
+    "bf16-moe-hd176": dict(base="c4", B=1, C=24, P=40, d=2816, n_q_heads=16, n_kv_heads=8,
+                           head_dim=176, V=1024, n_layers=1, mlp_hidden=128, n_experts=4, top_k=1),
+}
+
+
+@pytest.mark.parametrize("name", list(MOE))
+def test_moe_stack_step_matches_oracle(name):
+    import torch
+    import discrete_diffusion_decoding_dg_amd as dg
+    from oracle.stack import route
+    spec = dict(MOE[name])
+    zero_wo = spec.pop("zero_wo", False)
+    cfg = get_config(spec.pop("base"), **spec)
+    inp = make_inputs(cfg)
+    if zero_wo:
+        inp["S_Wo"] = np.zeros_like(inp["S_Wo"])
+        if "S_Wo_bits" in inp:
+            inp["S_Wo_bits"] = np.zeros_like(inp["S_Wo_bits"])
+    m = GpuModel(cfg, inp)
+    layers = _layers_dev(cfg, inp)
+    wr = to_dev(inp, "S_W_router", cfg)
+    for l, lw in enumerate(layers):
+        lw["W_router"] = wr[l].contiguous()
+    gf = to_dev(inp, "S_g_final", cfg)
+    dg.dg_set_stack(m.model, layers, gf, top_k=cfg.top_k)
+    Kp, Vp = to_dev(inp, "S_K_pre", cfg), to_dev(inp, "S_V_pre", cfg)
+    z = to_dev(inp, "z", cfg)
+    x = torch.from_numpy(inp["x"]).cuda()
+    t = np.full(cfg.B, 0.5, np.float32)
+    dt = np.float32(1.0 / cfg.steps)
+    B, C = cfg.B, cfg.C
+    h1 = act_tensor((B, C, cfg.d), cfg)
+    lse = torch.empty((B, C), dtype=torch.float32, device="cuda")
+    x_out = torch.empty((B, C), dtype=torch.int32, device="cuda")
+    z_out = act_tensor((B, C, cfg.d), cfg)
+    print(f"[gpu] moe stack step {name} L={cfg.n_layers} X={cfg.n_experts} k={cfg.top_k} R={cfg.R}", flush=True)
+    dg.dg_denoise_step_taps(m.model, x, z, Kp, Vp, t, dt, 17, x_out, z_out, {"h1": h1, "lse": lse})
+    torch.cuda.synchronize()
+    m.close()
+    del layers, wr, gf
+    sw = {n: [inp["S_" + n][l] for l in range(cfg.n_layers)] for n in LAYER_NAMES}
+    sw["W_router"] = [inp["S_W_router"][l] for l in range(cfg.n_layers)]
+    sw["g_final"], sw["top_k"] = inp["S_g_final"], cfg.top_k
+    o = stack_step(cfg, {"E": inp["E"]}, sw, inp["x"], inp["z"], inp["S_K_pre"], inp["S_V_pre"], t,
+                   float(dt), 17)
+    # rows whose routing is within the stream's rounding of a tie may pick
+    # another expert on the GPU; they are left out (all of them with one
+    # layer; with more layers only when every expert is selected)
+    keep = np.ones(cfg.R, bool)
+    if cfg.top_k < cfg.n_experts:
+        for l in range(cfg.n_layers):
+            _, _, r = route(o["layers"][l]["m"].reshape(cfg.R, cfg.d), sw["W_router"][l], cfg.top_k)
+            srt = -np.sort(-r.astype(np.float64), axis=1)
+            margin = srt[:, cfg.top_k - 1] - srt[:, cfg.top_k]
+            # the routing input m drifts by about the stream's tolerance (one
+            # norm's rounding only when the attention output is zero)
+            drift = 1e-4 if cfg.dtype == "f32" else (5e-3 if zero_wo else 2 * RTOL_BF16)
+            tol = drift * np.sqrt((r.astype(np.float64) ** 2).mean())
+            keep &= margin > tol
+        assert cfg.n_layers == 1 or cfg.dtype == "f32" or keep.all()
+    print(f"[gpu] rows compared: {int(keep.sum())} of {cfg.R}", flush=True)
+    assert keep.mean() > 0.9
+    rt = (RTOL_F32 if cfg.dtype == "f32" else RTOL_BF16) * cfg.n_layers
+    hf = to_host(h1).reshape(cfg.R, cfg.d)
+    assert_close("final norm", hf[keep], o["h_final"].reshape(cfg.R, cfg.d)[keep], rt)
+    head = lm_head(hf.reshape(B, C, cfg.d).astype(np.float64), inp["E"], o["inv_tau"], cfg.dtype)
+    smp = step_select(inp["x"], head["s"], o["lam"], 17, np.arange(cfg.B))
+    r1 = RTOL_F32 if cfg.dtype == "f32" else RTOL_BF16
+    assert_close("lse", lse.cpu().numpy().ravel()[keep], head["lse"][keep],
+                 RTOL_F32 if cfg.dtype == "f32" else LSE_RTOL)
+    assert_close("z", to_host(z_out).reshape(cfg.R, cfg.d)[keep], head["z"].reshape(cfg.R, cfg.d)[keep], r1)
+    token_gate(x_out.cpu().numpy(), smp)
