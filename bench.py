@@ -358,7 +358,32 @@ def main():
         stack_res = {"layers": L, "mlp_hidden": 4 * cfg.d, "ms_per_step": sms,
                      "step_tflops": sfl["total"] / (sms * 1e-3) / 1e12,
                      "stage_ms_per_step": {k: v[0] / 10 for k, v in sp.items() if v[1]}}
-        del layers, sdev, Ks, Vs
+        del layers, sdev
+        # the same stack with a mixture of 8 experts of width d per layer, top 2
+        X, TK = 8, 2
+        cm = cfg.with_(n_layers=L, mlp_hidden=cfg.d, n_experts=X, top_k=TK)
+        mnames = ["S_Wq", "S_Wk", "S_Wv", "S_Wo", "S_g_attn", "S_g_mlp", "S_g_final", "S_W_gate",
+                  "S_W_up", "S_W_down", "S_W_router"]
+        min_ = make_inputs(cm, mnames)
+        mdev = {n: to_dev(min_, n, cm) for n in mnames}
+        mlayers = [{n: mdev["S_" + n][l].contiguous() for n in
+                    ["Wq", "Wk", "Wv", "Wo", "g_attn", "g_mlp", "W_gate", "W_up", "W_down", "W_router"]}
+                   for l in range(L)]
+        dg.dg_set_stack(model, mlayers, mdev["S_g_final"], top_k=TK)
+        for k in range(args.warmup):
+            sstep(k)
+        torch.cuda.synchronize()
+        s0.record()
+        for k in range(nsteps):
+            sstep(k)
+        s1.record()
+        torch.cuda.synchronize()
+        dg.dg_set_stack(model)
+        mms = s0.elapsed_time(s1) / nsteps
+        mfl = cm.flops_per_step()
+        stack_res["moe"] = {"experts": X, "top_k": TK, "expert_hidden": cfg.d, "ms_per_step": mms,
+                            "step_tflops_activated": mfl["total"] / (mms * 1e-3) / 1e12}
+        del mlayers, mdev, Ks, Vs
 
     fl = cfg.flops_per_step()
     lm_ms, lm_n = prof["lmhead"]
