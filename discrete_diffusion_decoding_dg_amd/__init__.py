@@ -8,7 +8,7 @@ from ._lib import (DG_DTYPE_BF16, DG_DTYPE_F32, DG_SCHEDULE_COSINE, DG_SCHEDULE_
                    DgError, Model, dg_corrupt, dg_corrupt_batch, dg_create, dg_denoise_step,
                    dg_denoise_step_taps, dg_denoise_step_entropy, dg_destroy, dg_generate_canvas,
                    dg_generate_canvas_entropy, dg_last_error, dg_set_ffw, dg_ffw,
-                   dg_encode_kv, dg_generate_blocks, dg_set_stack,
+                   dg_encode_kv, dg_generate_blocks, dg_generate_blocks_entropy, dg_set_stack,
                    dg_profile_enable, dg_profile_read,
                    dg_status_string, dg_workspace_bytes, library_path, load_library)
 
@@ -16,6 +16,6 @@ __all__ = ["DG_DTYPE_BF16", "DG_DTYPE_F32", "DG_SCHEDULE_COSINE", "DG_SCHEDULE_L
            "Model", "dg_corrupt", "dg_corrupt_batch", "dg_create", "dg_denoise_step",
            "dg_denoise_step_taps", "dg_denoise_step_entropy", "dg_destroy", "dg_generate_canvas",
            "dg_generate_canvas_entropy", "dg_last_error", "dg_set_ffw", "dg_ffw",
-           "dg_encode_kv", "dg_generate_blocks", "dg_set_stack",
+           "dg_encode_kv", "dg_generate_blocks", "dg_generate_blocks_entropy", "dg_set_stack",
            "dg_profile_enable", "dg_profile_read",
            "dg_status_string", "dg_workspace_bytes", "library_path", "load_library"]

@@ -50,7 +50,8 @@ class dg_profile(ctypes.Structure):
 EXPORTS = ["dg_create", "dg_destroy", "dg_workspace_bytes", "dg_corrupt", "dg_corrupt_batch",
            "dg_denoise_step", "dg_denoise_step_taps", "dg_generate_canvas",
            "dg_denoise_step_entropy", "dg_generate_canvas_entropy", "dg_set_ffw", "dg_ffw",
-           "dg_encode_kv", "dg_generate_blocks", "dg_set_stack", "dg_set_stack_moe",
+           "dg_encode_kv", "dg_generate_blocks", "dg_generate_blocks_entropy", "dg_set_stack",
+           "dg_set_stack_moe",
            "dg_profile_enable",
            "dg_profile_read", "dg_status_string", "dg_last_error"]
 
@@ -87,6 +88,7 @@ def load_library():
     lib.dg_generate_canvas_entropy.argtypes = [vp, vp, vp, i32, u64, f32, f32, vp, vp, vp, vp]
     lib.dg_encode_kv.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     lib.dg_generate_blocks.argtypes = [vp, vp, vp, i32, i32, i32, u64, vp, vp]
+    lib.dg_generate_blocks_entropy.argtypes = [vp, vp, vp, i32, i32, i32, u64, f32, f32, vp, vp, vp]
     lib.dg_set_ffw.argtypes = [vp, i32, vp, vp, vp]
     lib.dg_set_stack.argtypes = [vp, i32, i32, ctypes.POINTER(dg_layer_weights), vp]
     lib.dg_set_stack_moe.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(dg_layer_weights),
@@ -247,6 +249,14 @@ def dg_generate_blocks(model, K_cache, V_cache, P0, n_canvases, steps, seed, x_o
     _check(load_library().dg_generate_blocks(model.handle, _ptr(K_cache), _ptr(V_cache), int(P0),
                                              int(n_canvases), int(steps), int(seed), _ptr(x_out),
                                              _stream(stream)))
+
+
+def dg_generate_blocks_entropy(model, K_cache, V_cache, P0, n_canvases, max_steps, seed, eps_accept,
+                               eps_stop, x_out, steps_out, stream=None):
+    _check(load_library().dg_generate_blocks_entropy(model.handle, _ptr(K_cache), _ptr(V_cache), int(P0),
+                                                     int(n_canvases), int(max_steps), int(seed),
+                                                     float(eps_accept), float(eps_stop), _ptr(x_out),
+                                                     _ptr(steps_out), _stream(stream)))
 
 
 def dg_set_stack(model, layers=None, g_final=None, top_k=0):

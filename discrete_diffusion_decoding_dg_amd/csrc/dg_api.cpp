@@ -58,7 +58,7 @@ dg::Shape shape_of(const dg_config &c) {
 
 // Workspace layout, in carve order.
 struct Layout {
-  size_t h0, q, k, v, o, h1, attn, lm, prm, kappa, genx, genz, ent, gendet, flags, blkx, total;
+  size_t h0, q, k, v, o, h1, attn, lm, prm, kappa, genx, genz, ent, gendet, flags, blkx, blksteps, total;
 };
 
 Layout layout_of(const dg_config &c) {
@@ -97,8 +97,9 @@ Layout layout_of(const dg_config &c) {
   L.gendet = align_up(2 * R * sizeof(int32_t));     // generation: argmax predictions, ping-pong
   L.flags = align_up(2 * static_cast<size_t>(s.B) * sizeof(int32_t));   // stopped, stop
   L.blkx = align_up(R * sizeof(int32_t));           // block generation: the canvas being committed
+  L.blksteps = align_up(static_cast<size_t>(s.B) * sizeof(int32_t));
   L.total = L.h0 + L.q + L.k + L.v + L.o + L.h1 + L.attn + L.lm + L.prm + L.kappa + L.genx + L.genz +
-            L.ent + L.gendet + L.flags + L.blkx;
+            L.ent + L.gendet + L.flags + L.blkx + L.blksteps;
   return L;
 }
 
@@ -182,6 +183,7 @@ struct dg_model {
   int32_t *gendet;          // [2][R] argmax predictions during generation
   int32_t *stopped, *stopbuf;   // [B] each
   int32_t *blkx;                // [B, C] canvas being committed (block generation)
+  int32_t *blksteps;            // [B] its step counts (adaptive block generation)
   int32_t *host_stopped = nullptr;   // pinned [B], allocated on first use
   // gated self-conditioning block (dg_set_ffw); ffw_F == 0 is the identity
   int ffw_F = 0;
@@ -543,6 +545,70 @@ dg_status generate_steps(dg_model *m, const void *K_pre, const void *V_pre, int 
   return DG_OK;
 }
 
+// Adaptive generation with the entropy-bounded step (see
+// dg_generate_canvas_entropy), attending to the first P_cur cache rows (-1:
+// all P).
+dg_status generate_entropy(dg_model *m, const void *K_pre, const void *V_pre, int P_cur, int max_steps,
+                           uint64_t seed, float eps_accept, float eps_stop, int32_t *x_out, void *z_out,
+                           int32_t *steps_out, hipStream_t st) {
+  const dg::Shape &s = m->s;
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  if (!m->host_stopped) {
+    void *h = nullptr;
+    DG_HIP(hipHostMalloc(&h, static_cast<size_t>(s.B) * sizeof(int32_t), hipHostMallocDefault),
+           "hipHostMalloc");
+    m->host_stopped = static_cast<int32_t *>(h);
+  }
+  const size_t es = bf16 ? 2 : 4;
+  const size_t R = static_cast<size_t>(s.R());
+  const size_t nz = R * s.d * es;
+
+  // temperatures of the whole grid t_k = 1 - k / max_steps, uploaded once
+  std::vector<dg::StepParams> prm(static_cast<size_t>(max_steps) * s.B);
+  for (int k = 0; k < max_steps; ++k) {
+    const float tk = static_cast<float>(1.0 - static_cast<double>(k) / max_steps);
+    const dg::StepParams p = step_params(tk, 1.0, m->cfg.schedule);
+    for (int b = 0; b < s.B; ++b) prm[static_cast<size_t>(k) * s.B + b] = p;
+  }
+  if (dg_status e = upload_params(m, m->prm, prm, st)) return e;
+
+  int32_t *xb[2] = {m->genx, m->genx + R};
+  char *zb[2] = {m->genz, m->genz + nz};
+  int32_t *db[2] = {m->gendet, m->gendet + R};
+  DG_HIP(dg::launch_fill_zero(m->kappa, align_up(s.B * sizeof(float)), st), "fill");
+  DG_HIP(dg::launch_fill_zero(xb[0], R * sizeof(int32_t), st), "fill");
+  DG_HIP(dg::launch_corrupt(xb[0], m->kappa, s.B, s.C, s.V, seed, xb[0], st), "corrupt launch");
+  DG_HIP(dg::launch_fill_zero(zb[0], nz, st), "fill");
+  DG_HIP(dg::launch_fill_zero(m->stopped, static_cast<size_t>(s.B) * sizeof(int32_t), st), "fill");
+  DG_HIP(dg::launch_fill_i32(steps_out, static_cast<size_t>(s.B), max_steps, st), "fill");
+  int cur = 0;
+  for (int k = 0; k < max_steps; ++k) {
+    const int nxt = cur ^ 1;
+    if (dg_status e = run_step(m, xb[cur], zb[cur], K_pre, V_pre, m->prm + static_cast<size_t>(k) * s.B,
+                               nullptr, 0, seed + static_cast<uint64_t>(k), xb[nxt], zb[nxt], nullptr,
+                               nullptr, nullptr, st, &m->ent, m->stopped, P_cur))
+      return e;
+    DG_HIP(dg::launch_entropy_select(m->ent, xb[cur], k ? db[cur] : nullptr, s.B, s.C, s.V,
+                                     eps_accept, eps_stop, seed + static_cast<uint64_t>(k), k,
+                                     xb[nxt], db[nxt], nullptr, m->stopbuf, m->stopped, steps_out, st),
+           "select launch");
+    cur = nxt;
+    // every kPoll steps, end early once every canvas has stopped
+    if ((k + 1) % kPoll == 0 && k + 1 < max_steps) {
+      DG_HIP(hipMemcpyAsync(m->host_stopped, m->stopped, static_cast<size_t>(s.B) * sizeof(int32_t),
+                            hipMemcpyDeviceToHost, st), "stop flags copy");
+      DG_HIP(hipStreamSynchronize(st), "stop flags sync");
+      bool all = true;
+      for (int b = 0; b < s.B && all; ++b) all = m->host_stopped[b] != 0;
+      if (all) break;
+    }
+  }
+  DG_HIP(hipMemcpyAsync(x_out, xb[cur], R * sizeof(int32_t), hipMemcpyDeviceToDevice, st), "x copy");
+  if (z_out) DG_HIP(hipMemcpyAsync(z_out, zb[cur], nz, hipMemcpyDeviceToDevice, st), "z copy");
+  return DG_OK;
+}
+
+
 // Encoder cache entries of tokens [B, ld] (columns [0, n)) into cache rows
 // [pos, pos + n): key and value projections of the token embeddings.
 dg_status encode_kv(dg_model *m, const int32_t *tokens, int n, int ld, int pos, void *K, void *V,
@@ -643,6 +709,7 @@ dg_status dg_create(const dg_config *cfg, const dg_weights *w, dg_model **out) {
   m->stopbuf = m->stopped + m->s.B;
   p += L.flags;
   m->blkx = reinterpret_cast<int32_t *>(p); p += L.blkx;
+  m->blksteps = reinterpret_cast<int32_t *>(p); p += L.blksteps;
   *out = m;
   return DG_OK;
 }
@@ -1098,59 +1165,51 @@ dg_status dg_generate_canvas_entropy(dg_model *m, const void *K_pre, const void 
   if (bf16 && ((K_pre && !aligned16(K_pre)) || (V_pre && !aligned16(V_pre)) ||
                (z_out && !aligned16(z_out))))
     return fail(DG_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
-  if (!m->host_stopped) {
-    void *h = nullptr;
-    DG_HIP(hipHostMalloc(&h, static_cast<size_t>(s.B) * sizeof(int32_t), hipHostMallocDefault),
-           "hipHostMalloc");
-    m->host_stopped = static_cast<int32_t *>(h);
-  }
-  const size_t es = bf16 ? 2 : 4;
-  const size_t R = static_cast<size_t>(s.R());
-  const size_t nz = R * s.d * es;
+  return generate_entropy(m, K_pre, V_pre, -1, max_steps, seed, eps_accept, eps_stop, x_out, z_out,
+                          steps_out, static_cast<hipStream_t>(stream));
+}
+
+dg_status dg_generate_blocks_entropy(dg_model *m, void *K_cache, void *V_cache, int32_t P0,
+                                     int32_t n_canvases, int32_t max_steps, uint64_t seed,
+                                     float eps_accept, float eps_stop, int32_t *x_out,
+                                     int32_t *steps_out, void *stream) {
+  g_err.clear();
+  if (dg_status s = check_model(m)) return s;
+  const dg::Shape &s = m->s;
+  if (!x_out || !steps_out) return fail(DG_ERR_INVALID_ARG, "x_out and steps_out must be non-NULL");
+  if (n_canvases < 1 || P0 < 0 || static_cast<int64_t>(P0) + static_cast<int64_t>(n_canvases) * s.C > s.P)
+    return fail(DG_ERR_INVALID_ARG, "need n_canvases >= 1, P0 >= 0 and P0 + n_canvases * C <= P "
+                "(P0=%d n_canvases=%d C=%d P=%d)", P0, n_canvases, s.C, s.P);
+  if (!K_cache || !V_cache) return fail(DG_ERR_INVALID_ARG, "K_cache and V_cache must be non-NULL");
+  if (m->st_L)
+    return fail(DG_ERR_UNSUPPORTED, "block generation with a multi-layer stack needs its causal encoder pass (not built)");
+  if (max_steps < 1 || max_steps > kMaxSteps)
+    return fail(DG_ERR_INVALID_ARG, "max_steps must be in [1, %d] (got %d)", kMaxSteps, max_steps);
+  if (s.C > dg::kSelectMaxC)
+    return fail(DG_ERR_UNSUPPORTED, "the entropy-bounded step supports C <= %d (got %d)", dg::kSelectMaxC, s.C);
+  if (!std::isfinite(eps_accept) || !std::isfinite(eps_stop))
+    return fail(DG_ERR_INVALID_ARG, "eps_accept and eps_stop must be finite");
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  if (bf16 && (!aligned16(K_cache) || !aligned16(V_cache)))
+    return fail(DG_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
-
-  // temperatures of the whole grid t_k = 1 - k / max_steps, uploaded once
-  std::vector<dg::StepParams> prm(static_cast<size_t>(max_steps) * s.B);
-  for (int k = 0; k < max_steps; ++k) {
-    const float tk = static_cast<float>(1.0 - static_cast<double>(k) / max_steps);
-    const dg::StepParams p = step_params(tk, 1.0, m->cfg.schedule);
-    for (int b = 0; b < s.B; ++b) prm[static_cast<size_t>(k) * s.B + b] = p;
-  }
-  if (dg_status e = upload_params(m, m->prm, prm, st)) return e;
-
-  int32_t *xb[2] = {m->genx, m->genx + R};
-  char *zb[2] = {m->genz, m->genz + nz};
-  int32_t *db[2] = {m->gendet, m->gendet + R};
-  DG_HIP(dg::launch_fill_zero(m->kappa, align_up(s.B * sizeof(float)), st), "fill");
-  DG_HIP(dg::launch_fill_zero(xb[0], R * sizeof(int32_t), st), "fill");
-  DG_HIP(dg::launch_corrupt(xb[0], m->kappa, s.B, s.C, s.V, seed, xb[0], st), "corrupt launch");
-  DG_HIP(dg::launch_fill_zero(zb[0], nz, st), "fill");
-  DG_HIP(dg::launch_fill_zero(m->stopped, static_cast<size_t>(s.B) * sizeof(int32_t), st), "fill");
-  DG_HIP(dg::launch_fill_i32(steps_out, static_cast<size_t>(s.B), max_steps, st), "fill");
-  int cur = 0;
-  for (int k = 0; k < max_steps; ++k) {
-    const int nxt = cur ^ 1;
-    if (dg_status e = run_step(m, xb[cur], zb[cur], K_pre, V_pre, m->prm + static_cast<size_t>(k) * s.B,
-                               nullptr, 0, seed + static_cast<uint64_t>(k), xb[nxt], zb[nxt], nullptr,
-                               nullptr, nullptr, st, &m->ent, m->stopped))
+  const size_t row = static_cast<size_t>(s.C) * sizeof(int32_t);
+  for (int j = 0; j < n_canvases; ++j) {
+    const int Pj = P0 + j * s.C;
+    // canvas j: adaptive generation against the first Pj cache rows; its step
+    // count goes to column j of steps_out [B, n_canvases]
+    if (dg_status e = generate_entropy(m, K_cache, V_cache, Pj, max_steps,
+                                       seed + static_cast<uint64_t>(j) * static_cast<uint64_t>(max_steps),
+                                       eps_accept, eps_stop, m->blkx, nullptr, m->blksteps, st))
       return e;
-    DG_HIP(dg::launch_entropy_select(m->ent, xb[cur], k ? db[cur] : nullptr, s.B, s.C, s.V,
-                                     eps_accept, eps_stop, seed + static_cast<uint64_t>(k), k,
-                                     xb[nxt], db[nxt], nullptr, m->stopbuf, m->stopped, steps_out, st),
-           "select launch");
-    cur = nxt;
-    // every kPoll steps, end early once every canvas has stopped
-    if ((k + 1) % kPoll == 0 && k + 1 < max_steps) {
-      DG_HIP(hipMemcpyAsync(m->host_stopped, m->stopped, static_cast<size_t>(s.B) * sizeof(int32_t),
-                            hipMemcpyDeviceToHost, st), "stop flags copy");
-      DG_HIP(hipStreamSynchronize(st), "stop flags sync");
-      bool all = true;
-      for (int b = 0; b < s.B && all; ++b) all = m->host_stopped[b] != 0;
-      if (all) break;
-    }
+    if (dg_status e = encode_kv(m, m->blkx, s.C, s.C, Pj, K_cache, V_cache, st)) return e;
+    DG_HIP(hipMemcpy2DAsync(x_out + static_cast<size_t>(j) * s.C, row * n_canvases, m->blkx, row, row,
+                            s.B, hipMemcpyDeviceToDevice, st),
+           "canvas copy");
+    DG_HIP(hipMemcpy2DAsync(steps_out + j, sizeof(int32_t) * n_canvases, m->blksteps, sizeof(int32_t),
+                            sizeof(int32_t), s.B, hipMemcpyDeviceToDevice, st),
+           "step count copy");
   }
-  DG_HIP(hipMemcpyAsync(x_out, xb[cur], R * sizeof(int32_t), hipMemcpyDeviceToDevice, st), "x copy");
-  if (z_out) DG_HIP(hipMemcpyAsync(z_out, zb[cur], nz, hipMemcpyDeviceToDevice, st), "z copy");
   return DG_OK;
 }
 

@@ -230,6 +230,17 @@ dg_status dg_generate_blocks(dg_model *m, void *K_cache, void *V_cache, int32_t 
                              int32_t n_canvases, int32_t steps, uint64_t seed, int32_t *x_out,
                              void *stream);
 
+/* dg_generate_blocks with the recommended sampler: canvas j is generated
+ * exactly as dg_generate_canvas_entropy with at most max_steps steps and seed
+ * seed + j * max_steps, against cache rows [0, P0 + j C), then committed.
+ *   x_out [B, n_canvases, C] int32; steps_out [B, n_canvases] int32 (device):
+ *   the steps each canvas took. Synchronises the stream every 4 steps (the
+ *   early-stop poll of adaptive generation). */
+dg_status dg_generate_blocks_entropy(dg_model *m, void *K_cache, void *V_cache, int32_t P0,
+                                     int32_t n_canvases, int32_t max_steps, uint64_t seed,
+                                     float eps_accept, float eps_stop, int32_t *x_out,
+                                     int32_t *steps_out, void *stream);
+
 /* Gated feed-forward self-conditioning block (TR summary, Method, three-line
  * update: z = FFW(p0 E) with a standard feed-forward network; the pages give
  * no structure, the reading here is the Gemma family's gated form):

@@ -96,6 +96,8 @@ def test_calls_reject_null_model_and_pointers():
     assert lib.dg_set_stack(None, 1, 64, None, None) == _lib.DG_ERR_INVALID_ARG
     assert lib.dg_set_stack_moe(None, 1, 128, 4, 2, None, None, None) == _lib.DG_ERR_INVALID_ARG
     assert lib.dg_generate_blocks(None, 32, 32, 0, 1, 4, 0, 16, None) == _lib.DG_ERR_INVALID_ARG
+    assert lib.dg_generate_blocks_entropy(None, 32, 32, 0, 1, 4, 0, ctypes.c_float(1.0),
+                                          ctypes.c_float(1.0), 16, 16, None) == _lib.DG_ERR_INVALID_ARG
     assert lib.dg_ffw(None, 16, 32, None) == _lib.DG_ERR_INVALID_ARG
     assert lib.dg_profile_enable(None, 1) == _lib.DG_ERR_INVALID_ARG
     assert lib.dg_profile_read(None, None) == _lib.DG_ERR_INVALID_ARG

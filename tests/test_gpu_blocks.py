@@ -159,3 +159,46 @@ def test_generate_blocks_argument_checks():
     with pytest.raises(dg.DgError, match="INVALID_ARG"):
         dg.dg_encode_kv(m.model, tok, cfg.P - 5, K, V)              # rows past P
     m.close()
+
+
+@pytest.mark.parametrize("name,eps_a,eps_s,sharpen", [("c1", 9.0, 4.3, 1.0), ("c1", 1e9, 1e9, 8.0),
+                                                      ("bf16-small", 60.0, 9.0, 1.0)])
+def test_generate_blocks_entropy(name, eps_a, eps_s, sharpen):
+    import torch
+    import discrete_diffusion_decoding_dg_amd as dg
+    cfg, ex = _split(BLOCKS[name])
+    P0, nb = ex["P0"], ex["n_canvases"]
+    max_steps, seed = 8, 5
+    inp = make_inputs(cfg)
+    if sharpen != 1.0:
+        inp["E"] = (inp["E"] * np.float32(sharpen)).astype(np.float32)   # fp32 workload only
+    w = {k: inp[k] for k in ["E", "Wq", "Wk", "Wv", "Wo"]}
+    m = GpuModel(cfg, inp)
+    K, V = to_dev(inp, "K_pre", cfg), to_dev(inp, "V_pre", cfg)
+    K[:, :, P0:] = 100.0
+    V[:, :, P0:] = -100.0
+    x = torch.empty((cfg.B, nb, cfg.C), dtype=torch.int32, device="cuda")
+    steps = torch.empty((cfg.B, nb), dtype=torch.int32, device="cuda")
+    print(f"[gpu] adaptive block generation {name} eps=({eps_a}, {eps_s}) sharpen={sharpen}", flush=True)
+    dg.dg_generate_blocks_entropy(m.model, K, V, P0, nb, max_steps, seed, eps_a, eps_s, x, steps)
+    torch.cuda.synchronize()
+    m.close()
+    xh, sh, Kh, Vh = x.cpu().numpy(), steps.cpu().numpy(), to_host(K), to_host(V)
+    print(f"[gpu] steps taken: {sh.tolist()}", flush=True)
+    rt = RTOL_F32 if cfg.dtype == "f32" else RTOL_BF16
+    for j in range(nb):
+        Pj = P0 + j * cfg.C
+        mj = GpuModel(cfg.with_(P=Pj), inp)
+        xj = torch.empty((cfg.B, cfg.C), dtype=torch.int32, device="cuda")
+        sj = torch.empty((cfg.B,), dtype=torch.int32, device="cuda")
+        dg.dg_generate_canvas_entropy(mj.model, K[:, :, :Pj].contiguous(), V[:, :, :Pj].contiguous(),
+                                      max_steps, seed + j * max_steps, eps_a, eps_s, xj, sj)
+        torch.cuda.synchronize()
+        mj.close()
+        assert np.array_equal(xh[:, j], xj.cpu().numpy()), f"canvas {j} differs from adaptive generation"
+        assert np.array_equal(sh[:, j], sj.cpu().numpy())
+        k, v = encode_kv(cfg, w, xh[:, j])
+        assert_close(f"k rows of canvas {j}", Kh[:, :, Pj:Pj + cfg.C], k, rt)
+        assert_close(f"v rows of canvas {j}", Vh[:, :, Pj:Pj + cfg.C], v, rt)
+    if sharpen != 1.0:
+        assert (sh < max_steps).all(), "sharp predictions should stop every canvas early"
