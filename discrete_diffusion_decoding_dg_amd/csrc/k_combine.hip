@@ -13,9 +13,14 @@
 // logits in log2 units, M the merged reference), and the plain argmax; the
 // select kernel then decides which draws to keep.
 //
-// Grid: (row, strip of 1024 columns). The first wave of each block merges
-// the row's split statistics (one split per lane, wave-wide max / sum /
-// argmax); then every thread streams 4 consecutive columns of all splits.
+// Grid: (row, strip of columns). Every wave merges the row's split
+// statistics itself (one split per lane: wave-wide max / sum); the first wave
+// of the first strip also takes the argmax and writes the per-row results.
+// Every thread then streams 8 consecutive columns (16 bytes of bf16) of a
+// group of splits, with the split weights read back from the owning lane.
+// With many splits the block's 256 threads form four groups (splits q, q + 4,
+// ...) over a strip of 512 columns, whose sums meet in LDS; with few, one
+// group over 2048 columns.
 // z partials are bf16 from the MFMA LM head and fp32 from the fp32 path.
 #include "dg_device.hpp"
 #include "dg_kernels.hpp"
@@ -24,15 +29,38 @@ namespace dg {
 namespace {
 
 constexpr int kMaxSplits = 64;
+constexpr int kCols = 8;   // columns per thread
 
-__device__ __forceinline__ float4 load4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
-__device__ __forceinline__ float4 load4(const uint16_t *p) {
-  const uint2 v = *reinterpret_cast<const uint2 *>(p);
-  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
-                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+__device__ __forceinline__ void load8(const uint16_t *p, float (&v)[kCols]) {
+  const uint4 q = *reinterpret_cast<const uint4 *>(p);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float *p, float (&v)[kCols]) {
+  const float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(uint16_t *p, const float (&v)[kCols]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+  *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ void store8(float *p, const float (&v)[kCols]) {
+  reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 __device__ __forceinline__ float load1(const float *p) { return *p; }
 __device__ __forceinline__ float load1(const uint16_t *p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ float lane_value(float v, int s) {   // s wave-uniform
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), s));
+}
 
 template <typename T, typename ZP>
 __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restrict__ part,
@@ -45,33 +73,34 @@ __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restri
                                                       float *__restrict__ lse,
                                                       int32_t *__restrict__ best, EntropyRows ent,
                                                       const int32_t *__restrict__ frozen,
-                                                      const T *__restrict__ z_t) {
-  __shared__ float wsh[kMaxSplits];
-  __shared__ float inv_l;
+                                                      const T *__restrict__ z_t, int groups) {
+  __shared__ __attribute__((aligned(16))) float gsum[3 * 64 * kCols];
   const int r = blockIdx.x;
+  const int s = threadIdx.x & 63;
+  const int tpg = 256 / groups;                    // threads per split group
+  const int q = threadIdx.x / tpg, t = threadIdx.x - q * tpg;
+  const int c0 = (blockIdx.y * tpg + t) * kCols;
+  const int64_t rowoff = static_cast<int64_t>(r) * d;
   if (frozen && frozen[r / C]) {
     // a stopped canvas keeps its self-conditioning signal
-    const int c0 = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
-    for (int c = c0; c < c0 + 4 && c < d; ++c)
-      z_out[static_cast<int64_t>(r) * d + c] = z_t[static_cast<int64_t>(r) * d + c];
+    if (q == 0)
+      for (int c = c0; c < c0 + kCols && c < d; ++c) z_out[rowoff + c] = z_t[rowoff + c];
     return;
   }
-  if (threadIdx.x < 64) {
-    const int s = threadIdx.x;
-    RowPartial p;
-    p.m = -INFINITY;
-    p.l = 0.f;
-    p.best = -INFINITY;
-    p.arg = -1;
-    p.s1 = 0.f;
-    p.dbest = -INFINITY;
-    p.darg = -1;
-    p.pad = 0;
-    if (s < splits) p = part[static_cast<int64_t>(s) * R + r];
-    const float M = wave_max(p.m);
-    const float w = (s < splits) ? exp2f(p.m - M) : 0.f;
-    const float L = wave_sum(w * p.l);
-    wsh[s] = w;
+  RowPartial p;
+  p.m = -INFINITY;
+  p.l = 0.f;
+  p.best = -INFINITY;
+  p.arg = -1;
+  p.s1 = 0.f;
+  p.dbest = -INFINITY;
+  p.darg = -1;
+  p.pad = 0;
+  if (s < splits) p = part[static_cast<int64_t>(s) * R + r];
+  const float M = wave_max(p.m);
+  const float w = (s < splits) ? exp2f(p.m - M) : 0.f;
+  const float L = wave_sum(w * p.l);
+  if (blockIdx.y == 0 && threadIdx.x < 64) {
     // argmax of the best draw over splits; an exact tie goes to the lower split
     float bv = p.arg >= 0 ? p.best : -INFINITY;
     int bs = p.arg >= 0 ? s : kMaxSplits;
@@ -95,56 +124,66 @@ __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restri
       }
       const int di = __shfl(p.darg, ds < kMaxSplits ? ds : 0, 64);
       if (s == 0) {
-        inv_l = 1.f / L;
-        if (blockIdx.y == 0) {
-          ent.H[r] = 0.6931471805599453f * (log2f(L) - S1 / L);
-          ent.y[r] = bs < kMaxSplits ? bi : -1;
-          ent.det[r] = ds < kMaxSplits ? di : -1;
-          if (lse) lse[r] = (M + log2f(L)) * 0.6931471805599453f;
-          if (best) best[r] = bs < kMaxSplits ? bi : -1;
-        }
+        ent.H[r] = 0.6931471805599453f * (log2f(L) - S1 / L);
+        ent.y[r] = bs < kMaxSplits ? bi : -1;
+        ent.det[r] = ds < kMaxSplits ? di : -1;
+        if (lse) lse[r] = (M + log2f(L)) * 0.6931471805599453f;
+        if (best) best[r] = bs < kMaxSplits ? bi : -1;
       }
     } else if (s == 0) {
-      inv_l = 1.f / L;
-      if (blockIdx.y == 0) {
-        const int b = r / C, i = r - b * C;
-        const u32x4 u = philox4x32_10(0u, static_cast<uint32_t>(i), static_cast<uint32_t>(b),
-                                      kStreamBernoulli, k0, k1);
-        const bool rs = u01(u.x) < prm[b].lam;
-        const int y = bs < kMaxSplits ? bi : -1;
-        x_out[r] = rs ? y : x_t[r];
-        if (lse) lse[r] = (M + log2f(L)) * 0.6931471805599453f;
-        if (best) best[r] = rs ? y : -1;
-      }
+      const int b = r / C, i = r - b * C;
+      const u32x4 u = philox4x32_10(0u, static_cast<uint32_t>(i), static_cast<uint32_t>(b),
+                                    kStreamBernoulli, k0, k1);
+      const bool rs = u01(u.x) < prm[b].lam;
+      const int y = bs < kMaxSplits ? bi : -1;
+      x_out[r] = rs ? y : x_t[r];
+      if (lse) lse[r] = (M + log2f(L)) * 0.6931471805599453f;
+      if (best) best[r] = rs ? y : -1;
     }
   }
-  __syncthreads();
-  const float il = inv_l;
-  const int c0 = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
-  if (c0 >= d) return;
-  const int64_t rowoff = static_cast<int64_t>(r) * d;
-  if (c0 + 4 <= d && (d & 3) == 0) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    const ZP *zp = zpart + rowoff + c0;
-    const int64_t sstride = static_cast<int64_t>(R) * d;
+  const float il = 1.f / L;
+  const int64_t sstride = static_cast<int64_t>(R) * d;
+  if ((d % kCols) == 0) {
+    // group q sums splits q, q + groups, ...; the groups meet in LDS
+    const bool active = c0 + kCols <= d;
+    float acc[kCols];
+#pragma unroll
+    for (int i = 0; i < kCols; ++i) acc[i] = 0.f;
+    if (active) {
+      const ZP *zp = zpart + rowoff + c0;
 #pragma unroll 8
-    for (int s = 0; s < splits; ++s) {
-      const float4 v = load4(zp + s * sstride);
-      const float w = wsh[s];
-      acc.x += w * v.x;
-      acc.y += w * v.y;
-      acc.z += w * v.z;
-      acc.w += w * v.w;
+      for (int sp = q; sp < splits; sp += groups) {
+        float v[kCols];
+        load8(zp + sp * sstride, v);
+        const float ws = lane_value(w, sp);
+#pragma unroll
+        for (int i = 0; i < kCols; ++i) acc[i] += ws * v[i];
+      }
     }
-    Act<T>::store(z_out, rowoff + c0, acc.x * il);
-    Act<T>::store(z_out, rowoff + c0 + 1, acc.y * il);
-    Act<T>::store(z_out, rowoff + c0 + 2, acc.z * il);
-    Act<T>::store(z_out, rowoff + c0 + 3, acc.w * il);
+    if (groups > 1) {
+      if (q > 0)
+#pragma unroll
+        for (int i = 0; i < kCols; ++i) gsum[((q - 1) * tpg + t) * kCols + i] = acc[i];
+      __syncthreads();
+      if (q > 0) return;
+      for (int g = 0; g < groups - 1; ++g)
+#pragma unroll
+        for (int i = 0; i < kCols; ++i) acc[i] += gsum[(g * tpg + t) * kCols + i];
+    }
+    if (!active) return;
+#pragma unroll
+    for (int i = 0; i < kCols; ++i) acc[i] *= il;
+    if ((reinterpret_cast<uintptr_t>(z_out) & 15) == 0) {
+      store8(z_out + rowoff + c0, acc);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kCols; ++i) Act<T>::store(z_out, rowoff + c0 + i, acc[i]);
+    }
   } else {
-    for (int c = c0; c < d && c < c0 + 4; ++c) {
+    if (q > 0) return;
+    for (int c = c0; c < d && c < c0 + kCols; ++c) {
       float acc = 0.f;
-      for (int s = 0; s < splits; ++s)
-        acc += wsh[s] * load1(zpart + (static_cast<int64_t>(s) * R + r) * d + c);
+      for (int sp = 0; sp < splits; ++sp) acc += lane_value(w, sp) * load1(zpart + sp * sstride + rowoff + c);
       Act<T>::store(z_out, rowoff + c, acc * il);
     }
   }
@@ -162,19 +201,22 @@ hipError_t launch_combine(bool bf16, const void *work, int splits, const int32_t
   const RowPartial *part = static_cast<const RowPartial *>(work);
   const char *zbase = static_cast<const char *>(work) + static_cast<size_t>(splits) * R * sizeof(RowPartial);
   const uint32_t k0 = static_cast<uint32_t>(seed), k1 = static_cast<uint32_t>(seed >> 32);
-  const dim3 grid(R, (s.d + 1023) / 1024);
+  // four split groups when there are many splits and d fills the strips
+  const int groups = (splits >= 8 && s.d % kCols == 0) ? 4 : 1;
+  const int strip = 256 / groups * kCols;
+  const dim3 grid(R, (s.d + strip - 1) / strip);
   const EntropyRows er = ent ? *ent : EntropyRows{nullptr, nullptr, nullptr};
   if (frozen && !z_t) return hipErrorInvalidValue;
   if (bf16)
     hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st, part,
                        reinterpret_cast<const uint16_t *>(zbase), splits,
                        x_t, prm, R, s.C, s.d, k0, k1, x_out, static_cast<uint16_t *>(z_out), lse,
-                       best, er, frozen, static_cast<const uint16_t *>(z_t));
+                       best, er, frozen, static_cast<const uint16_t *>(z_t), groups);
   else
     hipLaunchKernelGGL((combine_kernel<float, float>), grid, dim3(256), 0, st, part,
                        reinterpret_cast<const float *>(zbase), splits, x_t,
                        prm, R, s.C, s.d, k0, k1, x_out, static_cast<float *>(z_out), lse, best,
-                       er, frozen, static_cast<const float *>(z_t));
+                       er, frozen, static_cast<const float *>(z_t), groups);
   return hipGetLastError();
 }
 

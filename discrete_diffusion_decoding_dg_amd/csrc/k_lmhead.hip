@@ -24,10 +24,10 @@
 //      (16x16x16 for 16-row blocks), E read transposed from LDS by
 //      ds_read_b64_tr_b16.
 // E tiles reach LDS by direct global->LDS loads (no register staging). With
-// two tile buffers (d <= 2048) the next tile is requested in small batches
-// spread over the current tile, so its transfer overlaps a whole tile of work
-// without ever filling the load queue; a single buffer (d = 2816) refills
-// chunk by chunk behind the z contraction.
+// two tile buffers (d <= 2048) the next tile is requested in two halves
+// between the contractions (after the scores and after the epilogue), where
+// its LDS writes do not compete with the contractions' LDS reads; a single
+// buffer (d = 2816) refills chunk by chunk behind the z contraction.
 //
 // Gumbel noise: the Philox block of lane (row, position j) for the aligned
 // group of four tiles g holds the noise of ids 64 g + j + {0, 16, 32, 48}, one
@@ -274,13 +274,13 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
     const int v0 = tile * VT;
     const bool more = tile + 1 < t_end;
     if (a.p0) wait_vmcnt<0>();   // checking mode: p0 stores share the counter
-    // With two buffers the next tile streams into the other buffer in small
-    // batches spread over this tile (after the scores, after the epilogue and
-    // through the z contraction): the per-CU direct-load path moves about one
-    // tile per tile period, and a burst would stall the issuing waves.
+    // With two buffers the next tile streams into the other buffer in two
+    // halves, one after the scores and one after the epilogue. Measured on the
+    // 32-row blocks: issuing loads before or during either contraction (whose
+    // LDS reads they compete with) costs 2-15 %, a single burst up to 35 %.
     // Each batch goes into the buffer of the previous tile, whose reads by
     // this wave's own z contraction have all returned (they fed its MFMAs).
-    constexpr int kB1 = NKS / 4, kB2 = NKS / 2;   // chunk ranges [0,kB1) [kB1,kB2) [kB2,NKS)
+    constexpr int kB1 = NKS / 2;   // chunk ranges [0,kB1) and [kB1,NKS)
     const uint8_t *eb = ebuf(tile);
 
     // ---- S^T partial over this wave's slice (two accumulator sets break the
@@ -364,7 +364,7 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
     if constexpr (NBUF == 2) {
       if (more) {
 #pragma unroll
-        for (int c = kB1; c < kB2; ++c) dma_chunk(tile + 1, c);
+        for (int c = kB1; c < NKS; ++c) dma_chunk(tile + 1, c);
       }
     }
     __syncthreads();
@@ -407,8 +407,6 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
             wait_lgkm0();
             dma_chunk(tile + 1, c);
           }
-        } else {
-          if (c >= kB2 && more) dma_chunk(tile + 1, c);
         }
       }
     } else {
@@ -426,8 +424,6 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
             wait_lgkm0();
             dma_chunk(tile + 1, n >> 1);
           }
-        } else {
-          if ((n & 1) && (n >> 1) >= kB2 && more) dma_chunk(tile + 1, n >> 1);
         }
       }
     }
