@@ -6,9 +6,11 @@
 // here as one joint, unmasked softmax over [prefix ; canvas] keys, scale
 // 1/sqrt(hd), query head h using kv head h / G.
 //
-// One block = 256 query rows of one kv head (the G query heads of a kv head
-// share its K/V, so their rows are stacked: row qr = (h - g G) C + i), 8 waves
-// of 32 rows. Keys stream through LDS in tiles of 64 by direct global->LDS
+// One block = 32 NWA query rows of one kv head (the G query heads of a kv
+// head share its K/V, so their rows are stacked: row qr = (h - g G) C + i),
+// NWA waves of 32 rows: 8 waves, or 4 where 8-wave blocks would leave half
+// the CUs idle (short caches at batch 1), which doubles the blocks. Keys
+// stream through LDS in tiles of 64 by direct global->LDS
 // loads, NS tiles in flight. Per tile and wave:
 //   S^T[key, query] = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as the
 //   A operand, the wave's Q rows held in registers as B). A lane then holds 16
@@ -33,8 +35,6 @@
 namespace dg {
 namespace {
 
-constexpr int NWA = 8;              // waves per block
-constexpr int BQ = NWA * 32;        // query rows per block
 constexpr int BK = 64;              // keys per tile
 constexpr int kLdsBudget = 160 * 1024;
 constexpr float kSlack = 8.0f;      // log2 units
@@ -55,7 +55,7 @@ struct Geo {
 struct AttnArgs {
   const uint16_t *q, *k, *v, *Kp, *Vp;
   uint16_t *o;
-  float *opart;   // [splits][R][Hq][hd] unnormalised, when splits > 1
+  uint16_t *opart;   // [splits][R][Hq][hd] unnormalised bf16, when splits > 1
   float2 *ml;     // [splits][R][Hq] (m, l), log2 units
   int B, C, P, Pst, Hq, Hkv, G, splits, tiles_per_split;   // Pst: cache rows per (b, g)
   float scale_log2;   // log2(e) / sqrt(hd)
@@ -85,14 +85,14 @@ __device__ __forceinline__ void wait_vmcnt_steps(int k) {
 }
 
 // Direct global -> LDS load of 16 bytes per lane from a per-lane 64-bit
-// address; lane i's bytes land at lds + 16 i (lds wave-uniform). Inline asm
+// address; lane i's bytes land at LDS byte address lds + 16 i (lds
+// wave-uniform). Inline asm
 // keeps the compiler from adding waits before unrelated LDS reads; reads of
 // the loaded data follow an explicit vmcnt wait and a barrier. The
 // instruction has no register result: its address registers are read at
 // issue.
-__device__ __forceinline__ void lds_dma16_va(const void *src, void *lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds)));
+__device__ __forceinline__ void lds_dma16_va(const void *src, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
   const uint64_t addr = reinterpret_cast<uint64_t>(src);
   uint32_t saved;
   // M0 is reserved by the compiler: keep its value across the block
@@ -109,9 +109,8 @@ __device__ __forceinline__ void lds_dma16_va(const void *src, void *lds) {
 
 // The same load with a wave-uniform 64-bit base (scalar registers) and a
 // 32-bit per-lane byte offset: cheaper to form than a per-lane address.
-__device__ __forceinline__ void lds_dma16_sa(const void *base, uint32_t voff, void *lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds)));
+__device__ __forceinline__ void lds_dma16_sa(const void *base, uint32_t voff, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
   // readfirstlane returns a signed int: go through uint32_t so that the low
   // half is zero-extended
   const uint64_t b = reinterpret_cast<uint64_t>(base);
@@ -130,13 +129,17 @@ __device__ __forceinline__ void lds_dma16_sa(const void *base, uint32_t voff, vo
       : "memory");
 }
 
-template <int HD>
-__global__ void __launch_bounds__(512) attn_fwd_kernel(AttnArgs a) {
+template <int HD, int NWA>
+__global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
+  constexpr int BQ = NWA * 32;                   // query rows per block
   using G_ = Geo<HD>;
   constexpr int HDP = G_::HDP, NPC = G_::NPC, NPR = G_::NPR, KS = G_::KS, NB = G_::NB;
   constexpr int TILE_B = G_::TILE_B, NS = G_::NS, NDMA = G_::NDMA;
   constexpr int MAXL = (NDMA + NWA - 1) / NWA;   // loads per wave and tile, at most
   __shared__ __attribute__((aligned(16))) uint8_t stage_mem[NS * 2 * TILE_B];
+  // LDS byte address of the stage (the M0 operand of the direct loads)
+  const uint32_t stage_lds = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)stage_mem));
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -149,7 +152,7 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(AttnArgs a) {
   // padding pieces (head dims that are not a multiple of 32) are read by the
   // contractions against zero Q / into discarded O columns and must be finite
   if constexpr (NPC > NPR) {
-    for (int c = tid; c < NS * 2 * (NPC - NPR) * BK; c += 512) {
+    for (int c = tid; c < NS * 2 * (NPC - NPR) * BK; c += NWA * 64) {
       const int key = c % BK, rest = c / BK;
       const int p = NPR + rest % (NPC - NPR), tens = rest / (NPC - NPR);
       *reinterpret_cast<uint4 *>(stage_mem + tens * TILE_B + p * BK * 16 + key * 16) = make_uint4(0, 0, 0, 0);
@@ -188,7 +191,7 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) koff[q] = static_cast<uint32_t>((lane ^ (4 * q)) * HD * 2);
   auto issue_tile = [&](int tile) {
-    uint8_t *st = stage_mem + (tile % NS) * 2 * TILE_B;
+    const uint32_t st = stage_lds + (tile % NS) * 2 * TILE_B;
     const int j0 = tile * BK;
     if (j0 + BK <= a.P || (j0 >= a.P && j0 + BK <= Lk)) {
       // the whole tile lies in the prefix or in the canvas: one uniform base
@@ -369,11 +372,13 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(AttnArgs a) {
       }
     } else {
       const int64_t R = static_cast<int64_t>(a.B) * a.C;
-      float *prow = a.opart + ((split * R + r) * a.Hq + h) * HD;
+      // partials travel in bf16: the merge rescales and sums them in fp32
+      // and rounds the result to bf16 anyway; half the bytes of fp32
+      uint16_t *prow = a.opart + ((split * R + r) * a.Hq + h) * HD;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int col = 32 * nb + (lane & 31);
-        if (HDP == HD || col < HD) prow[col] = oacc[nb][e];
+        if (HDP == HD || col < HD) prow[col] = f32_to_bf16(oacc[nb][e]);
       }
       if ((lane & 31) == 0) a.ml[(split * R + r) * a.Hq + h] = make_float2(mr, lr);
     }
@@ -382,8 +387,8 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(AttnArgs a) {
 
 // o[r, h, e] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s. One thread
 // per four consecutive columns of a row (hd % 4 == 0): the split weights are
-// computed once per thread and the partials stream as 16-byte loads.
-__global__ void __launch_bounds__(256) attn_combine_kernel(const float *__restrict__ opart,
+// computed once per thread and the bf16 partials stream as 8-byte loads.
+__global__ void __launch_bounds__(256) attn_combine_kernel(const uint16_t *__restrict__ opart,
                                                            const float2 *__restrict__ ml,
                                                            int splits, int64_t rows, int hd,
                                                            uint16_t *__restrict__ o) {
@@ -401,7 +406,9 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float *__restri
     for (int s = 0; s < splits; ++s) {
       const float2 v = ml[s * rows + row];
       const float w = exp2f(v.x - M);
-      const float4 x = *reinterpret_cast<const float4 *>(opart + s * total + idx);
+      const uint2 xb = *reinterpret_cast<const uint2 *>(opart + s * total + idx);
+      const float4 x = make_float4(__uint_as_float(xb.x << 16), __uint_as_float(xb.x & 0xFFFF0000u),
+                                   __uint_as_float(xb.y << 16), __uint_as_float(xb.y & 0xFFFF0000u));
       num.x += w * x.x;
       num.y += w * x.y;
       num.z += w * x.z;
@@ -416,9 +423,10 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float *__restri
   }
 }
 
-void plan(const Shape &s, int &splits, int &tps) {
+void plan_waves(const Shape &s, int nwa, int &splits, int &tps) {
+  const int bq = nwa * 32;
   const int tiles = (s.P + s.C + BK - 1) / BK;
-  const int base = ((s.G() * s.C + BQ - 1) / BQ) * s.Hkv * s.B;
+  const int base = ((s.G() * s.C + bq - 1) / bq) * s.Hkv * s.B;
   int want = (256 + base - 1) / base;   // one block per CU fills the chip
   if (want < 1) want = 1;
   if (want > tiles) want = tiles;
@@ -428,11 +436,22 @@ void plan(const Shape &s, int &splits, int &tps) {
   splits = (tiles + tps - 1) / tps;
 }
 
+// 8-wave blocks unless they leave half the CUs idle; then 4-wave blocks
+void plan(const Shape &s, int &nwa, int &splits, int &tps) {
+  nwa = 8;
+  plan_waves(s, 8, splits, tps);
+  const int blocks = ((s.G() * s.C + 255) / 256) * s.Hkv * s.B * splits;
+  if (blocks <= 128) {
+    nwa = 4;
+    plan_waves(s, 4, splits, tps);
+  }
+}
+
 }  // namespace
 
 int attention_splits(const Shape &s) {
-  int sp, tps;
-  plan(s, sp, tps);
+  int nwa, sp, tps;
+  plan(s, nwa, sp, tps);
   return sp;
 }
 
@@ -440,7 +459,7 @@ size_t attention_workspace_bytes(const Shape &s) {
   const int sp = attention_splits(s);
   if (sp <= 1) return 0;
   const size_t rows = static_cast<size_t>(s.R()) * s.Hq;
-  return sp * rows * (s.hd * sizeof(float) + sizeof(float2));
+  return sp * rows * (s.hd * sizeof(uint16_t) + sizeof(float2));
 }
 
 hipError_t launch_attention_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -450,19 +469,27 @@ hipError_t launch_attention_bf16(const uint16_t *q, const uint16_t *k, const uin
   AttnArgs a;
   a.q = q; a.k = k; a.v = v; a.Kp = Kp; a.Vp = Vp; a.o = o;
   a.B = s.B; a.C = s.C; a.P = s.P; a.Pst = s.pstride(); a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G();
-  plan(s, a.splits, a.tiles_per_split);
+  int nwa = 8;
+  plan(s, nwa, a.splits, a.tiles_per_split);
   const size_t rows = static_cast<size_t>(s.R()) * s.Hq;
-  a.opart = static_cast<float *>(work);
+  a.opart = static_cast<uint16_t *>(work);
   a.ml = reinterpret_cast<float2 *>(static_cast<char *>(work) +
-                                    static_cast<size_t>(a.splits) * rows * s.hd * sizeof(float));
+                                    static_cast<size_t>(a.splits) * rows * s.hd * sizeof(uint16_t));
   a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(s.hd)));
-  dim3 grid((s.G() * s.C + BQ - 1) / BQ, s.Hkv, s.B * a.splits);
+  const int bq = nwa * 32;
+  dim3 grid((s.G() * s.C + bq - 1) / bq, s.Hkv, s.B * a.splits);
+#define DG_ATT(HD_)                                                                       \
+  case HD_:                                                                               \
+    if (nwa == 8)                                                                         \
+      hipLaunchKernelGGL((attn_fwd_kernel<HD_, 8>), grid, dim3(512), 0, st, a);           \
+    else                                                                                  \
+      hipLaunchKernelGGL((attn_fwd_kernel<HD_, 4>), grid, dim3(256), 0, st, a);           \
+    break;
   switch (s.hd) {
-    case 64: hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(512), 0, st, a); break;
-    case 128: hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(512), 0, st, a); break;
-    case 176: hipLaunchKernelGGL(attn_fwd_kernel<176>, grid, dim3(512), 0, st, a); break;
+    DG_ATT(64) DG_ATT(128) DG_ATT(176)
     default: return hipErrorInvalidValue;
   }
+#undef DG_ATT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   const int64_t total4 = static_cast<int64_t>(rows) * (s.hd / 4);
