@@ -392,6 +392,12 @@ def main():
     traffic = _traffic(args.workload)
     kernels = {k: {"avg_ms": (v[0] / v[1]) if v[1] else None, "launches": v[1]}
                for k, v in stages.items() if v[1]}
+    # algorithmic rate of the contraction stages (stage time includes each
+    # stage's own merge kernel, and event pairs add queue time)
+    for k, f in (("qkv", fl["qkv"]), ("attention", fl["attn"]), ("oproj", fl["oproj"]), ("lmhead", fl["lm"])):
+        if k in kernels and kernels[k]["avg_ms"]:
+            tf = f / (kernels[k]["avg_ms"] * 1e-3) / 1e12
+            kernels[k].update({"algorithmic_flop": f, "tflops": tf, "frac_mfma_bf16": tf / PEAK_BF16_TFLOPS})
     steps_per_s = 1000.0 / ms_per_step
     result = {
         "metric": METRIC,
