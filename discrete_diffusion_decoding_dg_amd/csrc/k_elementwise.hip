@@ -124,27 +124,88 @@ __global__ void __launch_bounds__(256) embed_bf16_vec_kernel(const uint16_t *__r
 }
 
 // RMSNorm of the decoder stack: y = round(x / sqrt(mean(x^2) + eps) * g), one
-// block per row, fp32 sums.
+// block per row, fp32 sums. Rows of up to 512 16-byte pieces stay in
+// registers between the sum of squares and the scaling (16-byte loads and
+// stores); longer rows or unaligned pointers take the scalar loop.
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4 &q, float (&v)[16 / sizeof(T)]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
+    v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
+  }
+}
+template <typename T>
+__device__ __forceinline__ uint4 pack16(const float (&v)[16 / sizeof(T)]) {
+  if constexpr (sizeof(T) == 2) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+  }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const T *__restrict__ x,
                                                       const T *__restrict__ g, int d, float eps,
                                                       T *__restrict__ y) {
+  constexpr int VW = 16 / sizeof(T);               // elements per 16-byte piece
+  constexpr int PPT = 2;                           // pieces per thread, at most
   __shared__ float red[4];
   const int r = blockIdx.x;
   const T *xr = x + static_cast<int64_t>(r) * d;
+  T *yr = y + static_cast<int64_t>(r) * d;
+  const bool vec = (d % VW) == 0 && d / VW <= PPT * 256 &&
+                   ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(g) |
+                     reinterpret_cast<uintptr_t>(y)) & 15) == 0;
+  float v[PPT][VW];
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    const float v = Act<T>::load(xr, c);
-    ss = fmaf(v, v, ss);
+  if (vec) {
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int c = threadIdx.x + 256 * k;         // this thread's pieces
+      if (c < d / VW) {
+        unpack16<T>(*reinterpret_cast<const uint4 *>(xr + c * VW), v[k]);
+#pragma unroll
+        for (int i = 0; i < VW; ++i) ss = fmaf(v[k][i], v[k][i], ss);
+      }
+    }
+  } else {
+    for (int k = threadIdx.x; k < d; k += blockDim.x) {
+      const float t = Act<T>::load(xr, k);
+      ss = fmaf(t, t, ss);
+    }
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float tot = (red[0] + red[1]) + (red[2] + red[3]);
   const float inv = 1.f / sqrtf(tot / static_cast<float>(d) + eps);
-  T *yr = y + static_cast<int64_t>(r) * d;
-  for (int c = threadIdx.x; c < d; c += blockDim.x)
-    Act<T>::store(yr, c, Act<T>::load(xr, c) * inv * Act<T>::load(g, c));
+  if (vec) {
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int c = threadIdx.x + 256 * k;
+      if (c < d / VW) {
+        float gv[VW];
+        unpack16<T>(*reinterpret_cast<const uint4 *>(g + c * VW), gv);
+#pragma unroll
+        for (int i = 0; i < VW; ++i) v[k][i] = v[k][i] * inv * gv[i];
+        *reinterpret_cast<uint4 *>(yr + c * VW) = pack16<T>(v[k]);
+      }
+    }
+  } else {
+    for (int k = threadIdx.x; k < d; k += blockDim.x)
+      Act<T>::store(yr, k, Act<T>::load(xr, k) * inv * Act<T>::load(g, k));
+  }
 }
 
 hipError_t launch_rmsnorm(bool bf16, const void *x, const void *g, int R, int d, float eps, void *y,

@@ -15,31 +15,66 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// One block per token row: each thread accumulates its columns' share of the
-// X logits, the waves combine them in LDS, and thread 0 picks the top_k.
+// One block per token row. Each thread holds 16-byte pieces of the row and
+// accumulates every expert's logit over them (XM >= X accumulators, one load
+// of the row and independent loads of the router rows); the waves combine
+// the logits in LDS and thread 0 picks the top_k.
 template <typename T>
+__device__ __forceinline__ void load_piece(const T *p, float (&v)[16 / sizeof(T)]) {
+  const uint4 q = *reinterpret_cast<const uint4 *>(p);
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
+    v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
+  }
+}
+
+template <typename T, int XM>
 __global__ void __launch_bounds__(256) router_topk_kernel(const T *__restrict__ m,
                                                           const T *__restrict__ Wr, int d, int X,
                                                           int top_k, int32_t *__restrict__ sel,
                                                           float *__restrict__ wts) {
-  __shared__ float part[4][kMoeMaxExperts];
+  constexpr int VW = 16 / sizeof(T);               // elements per piece
+  __shared__ float part[4][XM];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const T *mr = m + static_cast<int64_t>(r) * d;
-  for (int e = 0; e < X; ++e) {
-    const T *we = Wr + static_cast<int64_t>(e) * d;
-    float acc = 0.f;
-    for (int c = tid; c < d; c += blockDim.x) acc = fmaf(Act<T>::load(mr, c), Act<T>::load(we, c), acc);
-    acc = wave_sum(acc);
-    if (lane == 0) part[wave][e] = acc;
+  float acc[XM];
+#pragma unroll
+  for (int e = 0; e < XM; ++e) acc[e] = 0.f;
+  for (int c = tid; c < d / VW; c += blockDim.x) {
+    float mv[VW];
+    load_piece<T>(mr + c * VW, mv);
+#pragma unroll
+    for (int e = 0; e < XM; ++e) {
+      if (e < X) {
+        float wv[VW];
+        load_piece<T>(Wr + static_cast<int64_t>(e) * d + c * VW, wv);
+#pragma unroll
+        for (int i = 0; i < VW; ++i) acc[e] = fmaf(mv[i], wv[i], acc[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < XM; ++e) {
+    if (e < X) {
+      const float t = wave_sum(acc[e]);
+      if (lane == 0) part[wave][e] = t;
+    }
   }
   __syncthreads();
   if (tid != 0) return;
-  float lg[kMoeMaxExperts];
+  float lg[XM];
   for (int e = 0; e < X; ++e) lg[e] = (part[0][e] + part[1][e]) + (part[2][e] + part[3][e]);
   // selection by repeated maximum: strict comparison keeps the lower expert on ties
   uint64_t taken = 0;
-  float top[kMoeMaxExperts];
-  int idx[kMoeMaxExperts];
+  float top[XM];
+  int idx[XM];
   for (int j = 0; j < top_k; ++j) {
     int best = -1;
     for (int e = 0; e < X; ++e)
@@ -178,13 +213,21 @@ hipError_t launch_moe_route(bool bf16, const void *m, const void *Wr, int R, int
                             hipStream_t st) {
   if (R == 0) return hipSuccess;
   if (X < 1 || X > kMoeMaxExperts || top_k < 1 || top_k > X) return hipErrorInvalidValue;
-  if (bf16)
-    hipLaunchKernelGGL(router_topk_kernel<uint16_t>, dim3(R), dim3(256), 0, st,
-                       static_cast<const uint16_t *>(m), static_cast<const uint16_t *>(Wr), d, X, top_k,
-                       sel, wts);
-  else
-    hipLaunchKernelGGL(router_topk_kernel<float>, dim3(R), dim3(256), 0, st, static_cast<const float *>(m),
-                       static_cast<const float *>(Wr), d, X, top_k, sel, wts);
+  // the row is read in 16-byte pieces
+  if (d % (bf16 ? 8 : 4) != 0) return hipErrorInvalidValue;
+#define DG_ROUTE(T_, XM_)                                                                          \
+  hipLaunchKernelGGL((router_topk_kernel<T_, XM_>), dim3(R), dim3(256), 0, st, static_cast<const T_ *>(m), \
+                     static_cast<const T_ *>(Wr), d, X, top_k, sel, wts)
+  if (bf16) {
+    if (X <= 8) DG_ROUTE(uint16_t, 8);
+    else if (X <= 16) DG_ROUTE(uint16_t, 16);
+    else DG_ROUTE(uint16_t, kMoeMaxExperts);
+  } else {
+    if (X <= 8) DG_ROUTE(float, 8);
+    else if (X <= 16) DG_ROUTE(float, 16);
+    else DG_ROUTE(float, kMoeMaxExperts);
+  }
+#undef DG_ROUTE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !list) return e;
   hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(1024), 0, st, sel, R * top_k, X, list, offs, toff);
