@@ -144,7 +144,74 @@ __global__ void __launch_bounds__(1024) moe_group_kernel(const int32_t *__restri
   }
 }
 
-// out[r] = round(h[r] + sum_j wts[r, j] y[r * top_k + j]).
+// The same grouping in one pass, for up to kGroupCells chunk x expert cells:
+// entries are taken in chunks of 64 (a wave's lanes); per chunk and expert a
+// ballot gives the count and each entry's rank among the chunk's entries of
+// that expert; one exclusive scan over the (expert, chunk) counts in expert-
+// major order gives every chunk's first position in the list.
+constexpr int kGroupCells = 8192;
+__global__ void __launch_bounds__(1024) moe_group_ballot_kernel(const int32_t *__restrict__ sel, int n,
+                                                                int X, int32_t *__restrict__ list,
+                                                                int32_t *__restrict__ offs,
+                                                                int32_t *__restrict__ toff) {
+  __shared__ int cell[kGroupCells];               // [X][chunks] counts, then exclusive prefixes
+  __shared__ int tsum[1024];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = (n + 63) / 64, cells = X * nch;
+  for (int c = wave; c < nch; c += 16) {
+    const int q = c * 64 + lane;
+    const int e_q = q < n ? sel[q] : -1;
+    for (int e = 0; e < X; ++e) {
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(e_q == e);
+      if (lane == 0) cell[e * nch + c] = __popcll(bal);
+    }
+  }
+  __syncthreads();
+  // exclusive scan of cell[0, cells): thread t owns a contiguous run
+  const int per = (cells + 1023) / 1024;
+  const int c0 = tid * per;
+  int run = 0;
+  for (int i = 0; i < per; ++i)
+    if (c0 + i < cells) run += cell[c0 + i];
+  tsum[tid] = run;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {             // inclusive scan of the run sums
+    const int v = tid >= o ? tsum[tid - o] : 0;
+    __syncthreads();
+    tsum[tid] += v;
+    __syncthreads();
+  }
+  int acc = tsum[tid] - run;
+  for (int i = 0; i < per; ++i)
+    if (c0 + i < cells) {
+      const int v = cell[c0 + i];
+      cell[c0 + i] = acc;
+      acc += v;
+    }
+  __syncthreads();
+  for (int c = wave; c < nch; c += 16) {
+    const int q = c * 64 + lane;
+    const int e_q = q < n ? sel[q] : -1;
+    for (int e = 0; e < X; ++e) {
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(e_q == e);
+      if (e_q == e) list[cell[e * nch + c] + __popcll(bal & ((uint64_t(1) << lane) - 1))] = q;
+    }
+  }
+  if (tid == 0) {
+    int tiles = 0;
+    for (int e = 0; e < X; ++e) {
+      const int b = cell[e * nch], end = (e + 1 < X) ? cell[(e + 1) * nch] : n;
+      offs[e] = b;
+      toff[e] = tiles;
+      tiles += (end - b + kMoeTile - 1) / kMoeTile;
+    }
+    offs[X] = n;
+    toff[X] = tiles;
+  }
+}
+
+// out[r] = round(h[r] + sum_j wts[r, j] y[r * top_k + j]). Four columns per
+// thread (16-byte loads of y) when d % 4 == 0.
 template <typename T>
 __global__ void __launch_bounds__(256) moe_combine_kernel(const T *__restrict__ h,
                                                           const float *__restrict__ y,
@@ -152,6 +219,22 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(const T *__restrict__ 
                                                           int top_k, T *__restrict__ out) {
   const int r = blockIdx.x;
   const int64_t row = static_cast<int64_t>(r) * d;
+  if ((d & 3) == 0) {
+    for (int c = 4 * threadIdx.x; c < d; c += 4 * blockDim.x) {
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < top_k; ++j) {
+        const float w = wts[static_cast<int64_t>(r) * top_k + j];
+        const float4 v = *reinterpret_cast<const float4 *>(y + (static_cast<int64_t>(r) * top_k + j) * d + c);
+        acc[0] = fmaf(w, v.x, acc[0]);
+        acc[1] = fmaf(w, v.y, acc[1]);
+        acc[2] = fmaf(w, v.z, acc[2]);
+        acc[3] = fmaf(w, v.w, acc[3]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Act<T>::store(out, row + c + i, Act<T>::load(h, row + c + i) + acc[i]);
+    }
+    return;
+  }
   for (int c = threadIdx.x; c < d; c += blockDim.x) {
     float acc = 0.f;
     for (int j = 0; j < top_k; ++j)
@@ -230,7 +313,11 @@ hipError_t launch_moe_route(bool bf16, const void *m, const void *Wr, int R, int
 #undef DG_ROUTE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !list) return e;
-  hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(1024), 0, st, sel, R * top_k, X, list, offs, toff);
+  const int n = R * top_k;
+  if (static_cast<int64_t>(X) * ((n + 63) / 64) <= kGroupCells)
+    hipLaunchKernelGGL(moe_group_ballot_kernel, dim3(1), dim3(1024), 0, st, sel, n, X, list, offs, toff);
+  else
+    hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(1024), 0, st, sel, n, X, list, offs, toff);
   return hipGetLastError();
 }
 
