@@ -184,6 +184,12 @@ MOE = {
     # width 2816, top 1
     "bf16-moe-hd176": dict(base="c4", B=1, C=24, P=40, d=2816, n_q_heads=16, n_kv_heads=8,
                            head_dim=176, V=1024, n_layers=1, mlp_hidden=128, n_experts=4, top_k=1),
+    # 66,000 routed entries over 8 experts: more (expert, 64-entry chunk)
+    # cells than the one-pass grouping holds, so the per-expert grouping
+    # runs; canvases are independent, so the oracle checks the first four
+    "bf16-moe-long-list": dict(base="c5", B=132, C=250, P=70, d=256, n_q_heads=4, n_kv_heads=4,
+                               head_dim=64, V=1024, n_layers=1, mlp_hidden=128, n_experts=8, top_k=2,
+                               zero_wo=True, oracle_canvases=4),
 }
 
 
@@ -194,6 +200,7 @@ def test_moe_stack_step_matches_oracle(name):
     from oracle.stack import route
     spec = dict(MOE[name])
     zero_wo = spec.pop("zero_wo", False)
+    nb = spec.pop("oracle_canvases", None)
     cfg = get_config(spec.pop("base"), **spec)
     inp = make_inputs(cfg)
     if zero_wo:
@@ -222,6 +229,15 @@ def test_moe_stack_step_matches_oracle(name):
     torch.cuda.synchronize()
     m.close()
     del layers, wr, gf
+    # the oracle runs the first nb canvases (each canvas is independent of
+    # the others: its own cache, its own Philox streams)
+    nb = nb or B
+    h1, lse, x_out, z_out = h1[:nb], lse[:nb], x_out[:nb], z_out[:nb]
+    cfg = cfg.with_(B=nb)
+    B = nb
+    inp = dict(inp, x=inp["x"][:nb], z=inp["z"][:nb], S_K_pre=inp["S_K_pre"][:, :nb],
+               S_V_pre=inp["S_V_pre"][:, :nb])
+    t = t[:nb]
     sw = {n: [inp["S_" + n][l] for l in range(cfg.n_layers)] for n in LAYER_NAMES}
     sw["W_router"] = [inp["S_W_router"][l] for l in range(cfg.n_layers)]
     sw["g_final"], sw["top_k"] = inp["S_g_final"], cfg.top_k
