@@ -547,26 +547,29 @@ constexpr int PITCH64 = 72, PITCH32 = 40;   // LDS row pitch (floats) of a wave'
 // k-step on 16 distinct pieces (all 64 banks)
 __device__ __forceinline__ int sk_off(int r, int p) { return r * BK + ((p ^ (r & 15)) << 3); }
 
-template <int BN>
+// BMT rows per tile: 64, or 128 (row halves of 64, see the kernel)
+template <int BN, int BMT = BM>
 struct Cfg {
-  static constexpr int NS = BN == 64 ? 4 : 5;                 // slab stages
-  static constexpr int STAGE = (BM + BN) * BK;                // elements per stage
+  static constexpr int NS = BMT == 128 ? 3 : (BN == 64 ? 4 : 5);   // slab stages
+  static constexpr int STAGE = (BMT + BN) * BK;               // elements per stage
   static constexpr int PITCH = BN == 64 ? PITCH64 : PITCH32;
-  static constexpr int RED = 8 * BM * PITCH * 4;              // bytes of the partial-tile buffer
+  static constexpr int RED = 8 * BM * PITCH * 4;              // bytes of the 8 partial 64-row tiles
   static constexpr int LDS = (NS * STAGE * 2 > RED) ? NS * STAGE * 2 : RED;
-  static constexpr int DMA = (BM + BN) / 32;                  // direct loads per wave and slab
+  static constexpr int DMA = (BMT + BN) / 32;                 // direct loads per wave and slab
+  static_assert(LDS <= 160 * 1024, "LDS");
 };
 
 // Row sources of a block's 64-row tile: begin(tm) sets up row tile tm (false:
 // the block has no rows), a_row(r) is the A row of tile row r (always a valid
 // row: padding rows repeat a valid one), out(r) the output row (-1: padding),
 // and b_off the element offset of the B matrix.
-struct DenseRows {   // rows m0 .. m0 + 63 of an [M, K] matrix
+struct DenseRows {   // rows m0 .. m0 + bm - 1 of an [M, K] matrix
   int M;
+  int bm = BM;
   int m0 = 0;
   int64_t b_off = 0;
   __device__ bool begin(int tm) {
-    m0 = tm * BM;
+    m0 = tm * bm;
     return true;
   }
   __device__ int a_row(int r) const { return m0 + r < M ? m0 + r : M - 1; }
@@ -597,10 +600,13 @@ struct GroupRows {
   __device__ int out(int r) const { return r < cnt ? list[base + r] : -1; }
 };
 
-template <class Epi, int BN, class Rows>
+// BMT = 128: wave w computes row half w / 4 of the tile over k-steps w % 4
+// and w % 4 + 4 of every slab; the four partials of each half meet in LDS.
+template <class Epi, int BN, class Rows, int BMT = BM>
 __global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__restrict__ A, Rows rows,
                                                           int mt, int N, int K, Epi epi) {
-  using G = Cfg<BN>;
+  static_assert(BMT == BM || BMT == 2 * BM, "row tile");
+  using G = Cfg<BN, BMT>;
   constexpr int NR = BN / 32;                       // 32-column blocks per tile
   constexpr int NS = G::NS, PITCH = G::PITCH;
   __shared__ __attribute__((aligned(16))) uint16_t smem[G::LDS / 2];
@@ -627,10 +633,10 @@ __global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__rest
     const int g = wave * G::DMA + j;                // load index within the slab
     const int r = 4 * g + (lane >> 4);              // slab row, A rows first
     const int lp = (lane & 15) ^ (r & 15);          // logical piece this lane fetches
-    if (r < BM) {
+    if (r < BMT) {
       src[j] = A + static_cast<int64_t>(rows.a_row(r)) * K + 8 * lp;
     } else {
-      const int n = (n0 + r - BM < N) ? n0 + r - BM : N - 1;
+      const int n = (n0 + r - BMT < N) ? n0 + r - BMT : N - 1;
       src[j] = epi.brow(n, K) + rows.b_off + 8 * lp;
     }
     dst[j] = 4 * g * BK;                            // element offset of the load within a stage
@@ -649,6 +655,7 @@ __global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__rest
 #pragma unroll
     for (int j = 0; j < NR; ++j) acc[i][j] = f32x16{};
   const int p = 2 * wave + (lane >> 5);             // logical piece of this lane's k-step half
+  const int rg = wave >> 2, kg = wave & 3;          // BMT = 128: row half and k-step group
   for (int it = 0; it < nk; ++it) {
     int younger = nk - 1 - it;                      // slabs issued after this one
     if (younger > NS - 2) younger = NS - 2;
@@ -656,17 +663,35 @@ __global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__rest
     __syncthreads();                                // every wave's part of slab `it` landed
     if (it + NS - 1 < nk) issue(it + NS - 1);       // refill the stage every wave finished reading
     const uint16_t *as = smem + (it % NS) * G::STAGE;
-    const uint16_t *bs = as + BM * BK;
-    bf16x8 a[2], b[NR];
+    const uint16_t *bs = as + BMT * BK;
+    if constexpr (BMT == BM) {
+      bf16x8 a[2], b[NR];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(as + sk_off(32 * i + (lane & 31), p));
+      for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(as + sk_off(32 * i + (lane & 31), p));
 #pragma unroll
-    for (int j = 0; j < NR; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(bs + sk_off(32 * j + (lane & 31), p));
+      for (int j = 0; j < NR; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(bs + sk_off(32 * j + (lane & 31), p));
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < NR; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NR; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int pk = 2 * (kg + 4 * kk) + (lane >> 5);
+        bf16x8 a[2], b[NR];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          a[i] = *reinterpret_cast<const bf16x8 *>(as + sk_off(64 * rg + 32 * i + (lane & 31), pk));
+#pragma unroll
+        for (int j = 0; j < NR; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(bs + sk_off(32 * j + (lane & 31), pk));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < NR; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    }
   }
 
   // the eight partial tiles meet in LDS (the stages are free once everyone is
@@ -685,22 +710,30 @@ __global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__rest
         for (int e = 0; e < 4; ++e)
           mine[(32 * i + 8 * q + 4 * (lane >> 5) + e) * PITCH + 32 * j + (lane & 31)] = acc[i][j][4 * q + e];
   __syncthreads();
+  // tile row r: the sum of the eight K-split partials (BMT = 64), or of the
+  // four partials of its row half (BMT = 128)
   auto sum8 = [&](int r, int col) {
     float s = 0.f;
+    if constexpr (BMT == BM) {
 #pragma unroll
-    for (int w = 0; w < 8; ++w) s += red[w * BM * PITCH + r * PITCH + col];
+      for (int w = 0; w < 8; ++w) s += red[w * BM * PITCH + r * PITCH + col];
+    } else {
+      const float *h = red + (r >> 6) * 4 * BM * PITCH + (r & 63) * PITCH + col;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) s += h[w * BM * PITCH];
+    }
     return s;
   };
   if constexpr (Epi::kPair) {
     // columns [0, 32) of the tile are gate values, [32, 64) the up values of the same units
     static_assert(BN == 64, "gate/up pairs need 64-column tiles");
-    for (int e = tid; e < BM * 32; e += 512) {
+    for (int e = tid; e < BMT * 32; e += 512) {
       const int r = e >> 5, col = e & 31;
       const int m = rows.out(r), n = n0 + col;
       if (m >= 0 && n < N) epi.store_pair(m, n, sum8(r, col), sum8(r, col + 32));
     }
   } else {
-    for (int e = tid; e < BM * BN; e += 512) {
+    for (int e = tid; e < BMT * BN; e += 512) {
       const int r = e / BN, col = e - r * BN;
       const int m = rows.out(r), n = n0 + col;
       if (m >= 0 && n < N) epi.store(m, n, sum8(r, col));
@@ -725,9 +758,23 @@ hipError_t launch_rows(const uint16_t *A, const Rows &rows, int mt, int N, int K
   return hipGetLastError();
 }
 
+// Dense rows: 128-row tiles where 64-row ones would give at least two blocks
+// per CU of 64-column tiles (wide outputs, e.g. the gate/up GEMM of a wide
+// MLP): each B tile then serves twice the rows, and each CU moves 3/4 of
+// the operand bytes.
 template <class Epi>
 hipError_t launch(const uint16_t *A, int M, int N, int K, const Epi &epi, hipStream_t st) {
-  return launch_rows(A, DenseRows{M}, (M + BM - 1) / BM, N, K, epi, st);
+  const int mt = (M + BM - 1) / BM;
+  if (M > BM && static_cast<int64_t>(mt) * ((N + 63) / 64) >= 512) {
+    DenseRows rows{M};
+    rows.bm = 2 * BM;
+    const int mt2 = (M + 2 * BM - 1) / (2 * BM);
+    const int blocks = mt2 * ((N + 63) / 64);
+    hipLaunchKernelGGL((gemm_skinny_kernel<Epi, 64, DenseRows, 2 * BM>), dim3(blocks), dim3(512), 0, st, A,
+                       rows, mt2, N, K, epi);
+    return hipGetLastError();
+  }
+  return launch_rows(A, DenseRows{M}, mt, N, K, epi, st);
 }
 }  // namespace skinny
 

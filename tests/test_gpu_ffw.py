@@ -26,6 +26,10 @@ CASES = {
     # 2250 rows: 256 x 256 tiles for both GEMMs, ragged last row tile
     "bf16-rows2250-F256": dict(base="c5", B=9, C=250, P=70, d=256, n_q_heads=4, n_kv_heads=4,
                                head_dim=64, V=4096, ffw_hidden=256),
+    # 200 rows, 2F = 8192: the gate/up GEMM takes 128-row tiles (ragged
+    # second tile); the down GEMM 64-row ones
+    "bf16-rows200-F4096": dict(base="c2", B=1, C=200, P=100, d=256, n_q_heads=4, n_kv_heads=2,
+                               head_dim=64, V=4096, ffw_hidden=4096),
     # 2250 rows with 2F = 384 (not a multiple of 256): gate/up on 64 x 64 tiles
     "bf16-rows2250-F192": dict(base="c5", B=9, C=250, P=70, d=256, n_q_heads=4, n_kv_heads=4,
                                head_dim=64, V=4096, ffw_hidden=192),
