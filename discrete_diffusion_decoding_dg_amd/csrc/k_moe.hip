@@ -15,10 +15,9 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// One block per token row. Each thread holds 16-byte pieces of the row and
-// accumulates every expert's logit over them (XM >= X accumulators, one load
-// of the row and independent loads of the router rows); the waves combine
-// the logits in LDS and thread 0 picks the top_k.
+// One block per token row; 256 / XM threads per expert (XM >= X) take the
+// row and the expert's router row in 16-byte pieces, reduce their partial
+// dot products within the group, and thread 0 picks the top_k.
 template <typename T>
 __device__ __forceinline__ void load_piece(const T *p, float (&v)[16 / sizeof(T)]) {
   const uint4 q = *reinterpret_cast<const uint4 *>(p);
@@ -41,44 +40,38 @@ __global__ void __launch_bounds__(256) router_topk_kernel(const T *__restrict__ 
                                                           int top_k, int32_t *__restrict__ sel,
                                                           float *__restrict__ wts) {
   constexpr int VW = 16 / sizeof(T);               // elements per piece
-  __shared__ float part[4][XM];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int TE = 256 / XM;                     // threads per expert (one wave or less)
+  static_assert(TE >= 1 && TE <= 64 && 64 % TE == 0, "expert groups");
+  __shared__ float logit[XM];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int e = tid / TE, sub = tid - e * TE;      // expert and position in its group
   const T *mr = m + static_cast<int64_t>(r) * d;
-  float acc[XM];
+  float acc = 0.f;
+  if (e < X) {
+    const T *we = Wr + static_cast<int64_t>(e) * d;
+    for (int c = sub; c < d / VW; c += TE) {
+      float mv[VW], wv[VW];
+      load_piece<T>(mr + c * VW, mv);
+      load_piece<T>(we + c * VW, wv);
 #pragma unroll
-  for (int e = 0; e < XM; ++e) acc[e] = 0.f;
-  for (int c = tid; c < d / VW; c += blockDim.x) {
-    float mv[VW];
-    load_piece<T>(mr + c * VW, mv);
-#pragma unroll
-    for (int e = 0; e < XM; ++e) {
-      if (e < X) {
-        float wv[VW];
-        load_piece<T>(Wr + static_cast<int64_t>(e) * d + c * VW, wv);
-#pragma unroll
-        for (int i = 0; i < VW; ++i) acc[e] = fmaf(mv[i], wv[i], acc[e]);
-      }
+      for (int i = 0; i < VW; ++i) acc = fmaf(mv[i], wv[i], acc);
     }
   }
 #pragma unroll
-  for (int e = 0; e < XM; ++e) {
-    if (e < X) {
-      const float t = wave_sum(acc[e]);
-      if (lane == 0) part[wave][e] = t;
-    }
-  }
+  for (int o = 1; o < TE; o <<= 1) acc += __shfl_xor(acc, o, 64);
+  if (sub == 0 && e < X) logit[e] = acc;
   __syncthreads();
   if (tid != 0) return;
   float lg[XM];
-  for (int e = 0; e < X; ++e) lg[e] = (part[0][e] + part[1][e]) + (part[2][e] + part[3][e]);
+  for (int k = 0; k < X; ++k) lg[k] = logit[k];
   // selection by repeated maximum: strict comparison keeps the lower expert on ties
   uint64_t taken = 0;
   float top[XM];
   int idx[XM];
   for (int j = 0; j < top_k; ++j) {
     int best = -1;
-    for (int e = 0; e < X; ++e)
-      if (!((taken >> e) & 1) && (best < 0 || lg[e] > lg[best])) best = e;
+    for (int x = 0; x < X; ++x)
+      if (!((taken >> x) & 1) && (best < 0 || lg[x] > lg[best])) best = x;
     taken |= uint64_t(1) << best;
     idx[j] = best;
     top[j] = lg[best];
