@@ -184,7 +184,7 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
   if (tile_end > total_tiles) tile_end = total_tiles;
 
   // direct loads of one tile: load u in [0, NDMA) fills piece u % NPR of K
-  // (u < NPR) or of V; wave w issues loads w, w + 8, ...
+  // (u < NPR) or of V; wave w issues loads w, w + NWA, ...
   constexpr int MINL = NDMA / NWA;               // loads per wave and tile, at least
   // byte offset of this lane's key row inside a tile, for each piece phase
   uint32_t koff[4];

@@ -8,7 +8,8 @@
 //   - rows >= 2048 (batched canvases): 256 x 256 tiles, K in 32-wide slabs
 //     through four LDS stages (big::);
 //   - fewer rows with K % 128 == 0: 64 x 64 or 64 x 32 tiles, K in 128-wide
-//     slabs, the eight waves splitting K (skinny::);
+//     slabs, the eight waves splitting K (skinny::), or 128 x 64 tiles for
+//     wide outputs (two row halves of four waves splitting K);
 //   - K % 64 == 0 otherwise: 64 x 64 tiles, 64-wide slabs, nine stages;
 //   - anything else: 64 x 64 tiles, register double buffering.
 // Operand slabs reach LDS through direct global->LDS loads except in the
@@ -536,7 +537,8 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(const uint16_t *__restric
 // 256-byte row segments), and the eight waves split each slab by K instead
 // of splitting the tile: wave w multiplies k-step w (16 wide) of every slab
 // for the whole 64 x BN tile, so each element staged in LDS is read exactly
-// once. The eight partial tiles meet once, through LDS, at the end.
+// once. The eight partial tiles meet once, through LDS, at the end. Wide
+// outputs take 128 x 64 tiles instead (see the kernel).
 namespace skinny {
 constexpr int BM = 64, BK = 128;
 constexpr int PITCH64 = 72, PITCH32 = 40;   // LDS row pitch (floats) of a wave's partial tile:
