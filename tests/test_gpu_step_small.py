@@ -24,6 +24,10 @@ SMALL = {
                        head_dim=176, V=1024),
     "bf16-linear-b3": dict(base="c5", B=3, C=33, P=64, d=1024, n_q_heads=8, n_kv_heads=4,
                            head_dim=128, V=1024),
+    # V = 1040 = 65 tiles of 16 ids: the last split holds one tile, a partial
+    # group of four Gumbel tiles; zero prefix (P = 0: canvas keys only)
+    "bf16-vocab-1040-p0": dict(base="c2", B=2, C=40, P=0, d=256, n_q_heads=4, n_kv_heads=2,
+                               head_dim=64, V=1040),
     # enough rows (2250 = 8 x 256 + 202) for the 256 x 256-tile projections,
     # with a ragged last row tile
     "bf16-many-rows": dict(base="c5", B=9, C=250, P=70, d=256, n_q_heads=4, n_kv_heads=4,
