@@ -13,6 +13,10 @@ CASES = {
     "c1": dict(base="c1"),
     "bf16-small": dict(base="c2", B=2, C=40, P=100, d=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
                        V=512),
+    # one step under the linear schedule: lambda = dt / t = 1 at t = 1, so
+    # every row draws from the first prediction
+    "bf16-one-step": dict(base="c2", B=2, C=40, P=100, d=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                          V=512, steps=1, schedule="linear"),
 }
 
 
