@@ -9,8 +9,9 @@
 // eps_stop and its argmax predictions repeat those of the previous step.
 //
 // One block per canvas, one thread per position (padded to a power of two):
-// a bitonic sort of (entropy, position) in LDS, an inclusive scan of the
-// sorted entropies, then every thread settles the position of its rank.
+// a bitonic sort of (entropy, position) in registers (cross-lane shuffles
+// within a wave, LDS between waves), an inclusive scan of the sorted
+// entropies, then every thread settles the position of its rank.
 #include "dg_device.hpp"
 #include "dg_kernels.hpp"
 
@@ -44,44 +45,57 @@ __global__ void __launch_bounds__(1024) entropy_select_kernel(
     return;
   }
   const bool in = t < C;
-  key[t] = in ? ent.H[base + t] : INFINITY;
-  pos[t] = in ? t : 0x7fffffff;
+  float kv = in ? ent.H[base + t] : INFINITY;
+  int pv = in ? t : 0x7fffffff;
   if (in) {
     det_out[base + t] = ent.det[base + t];
     if (entropy_out) entropy_out[base + t] = ent.H[base + t];
   }
-  __syncthreads();
-  // bitonic sort, ascending by (entropy, position)
+  // bitonic sort, ascending by (entropy, position): thread t ends holding
+  // rank t. Partners less than 64 apart are in the same wave and trade
+  // through cross-lane shuffles; farther ones through LDS (one barrier pair).
   for (int k = 2; k <= n; k <<= 1)
     for (int j = k >> 1; j > 0; j >>= 1) {
-      const int p = t ^ j;
-      if (p > t) {
-        const bool up = (t & k) == 0;
-        const bool swap = up ? key_less(key[p], pos[p], key[t], pos[t])
-                             : key_less(key[t], pos[t], key[p], pos[p]);
-        if (swap) {
-          const float kt = key[t];
-          key[t] = key[p];
-          key[p] = kt;
-          const int pt = pos[t];
-          pos[t] = pos[p];
-          pos[p] = pt;
-        }
+      float kp;
+      int pp;
+      if (j >= 64) {
+        key[t] = kv;
+        pos[t] = pv;
+        __syncthreads();
+        kp = key[t ^ j];
+        pp = pos[t ^ j];
+        __syncthreads();
+      } else {
+        kp = __shfl_xor(kv, j, 64);
+        pp = __shfl_xor(pv, j, 64);
       }
-      __syncthreads();
+      // ascending runs (t & k == 0): the lower index of a pair keeps the
+      // smaller key; descending runs the larger (keys are distinct)
+      const bool up = (t & k) == 0, lower = (t & j) == 0;
+      const bool p_less = key_less(kp, pp, kv, pv);
+      if ((up == lower) ? p_less : !p_less) {
+        kv = kp;
+        pv = pp;
+      }
     }
-  // inclusive scan of the sorted entropies (padding sorts last)
-  scan[t] = in ? key[t] : 0.f;
-  __syncthreads();
-  for (int off = 1; off < n; off <<= 1) {
-    const float add = (t >= off) ? scan[t - off] : 0.f;
-    __syncthreads();
-    scan[t] += add;
-    __syncthreads();
+  // inclusive scan of the sorted entropies (padding sorts last): within each
+  // wave by shuffles, then the totals of the earlier waves
+  const int lane = t & 63, wv = t >> 6;
+  float run = in ? kv : 0.f;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float add = __shfl_up(run, off, 64);
+    if (lane >= off) run += add;
   }
+  if (lane == 63) scan[wv] = run;
+  __syncthreads();
+  for (int w = 0; w < wv; ++w) run += scan[w];
+  __syncthreads();
+  scan[t] = run;   // the scan by rank, for the mean below
+  __syncthreads();
   if (in) {
-    const int i = pos[t];
-    const bool accept = (t == 0) || (scan[t] < eps_accept);
+    const int i = pv;
+    const bool accept = (t == 0) || (run < eps_accept);
     int32_t tok;
     if (accept) {
       tok = ent.y[base + i];
