@@ -58,7 +58,7 @@ dg::Shape shape_of(const dg_config &c) {
 
 // Workspace layout, in carve order.
 struct Layout {
-  size_t h0, q, k, v, o, h1, attn, lm, prm, kappa, genx, genz, ent, gendet, flags, blkx, blksteps, total;
+  size_t h0, q, k, v, o, h1, attn, lm, etm, prm, kappa, genx, genz, ent, gendet, flags, blkx, blksteps, total;
 };
 
 Layout layout_of(const dg_config &c) {
@@ -85,9 +85,11 @@ Layout layout_of(const dg_config &c) {
     }
     L.attn = align_up(attn);
     L.lm = align_up(dg::lmhead_workspace_bytes(s));
+    L.etm = align_up(dg::lmhead_copy_bytes(s));      // the LM head's tile-major copy of E
   } else {
     L.attn = 0;
     L.lm = align_up(dg::lmhead_f32_workspace_bytes(s));
+    L.etm = 0;
   }
   L.prm = align_up(static_cast<size_t>(kMaxSteps) * s.B * sizeof(dg::StepParams));
   L.kappa = align_up(static_cast<size_t>(s.B) * sizeof(float));
@@ -98,8 +100,8 @@ Layout layout_of(const dg_config &c) {
   L.flags = align_up(2 * static_cast<size_t>(s.B) * sizeof(int32_t));   // stopped, stop
   L.blkx = align_up(R * sizeof(int32_t));           // block generation: the canvas being committed
   L.blksteps = align_up(static_cast<size_t>(s.B) * sizeof(int32_t));
-  L.total = L.h0 + L.q + L.k + L.v + L.o + L.h1 + L.attn + L.lm + L.prm + L.kappa + L.genx + L.genz +
-            L.ent + L.gendet + L.flags + L.blkx + L.blksteps;
+  L.total = L.h0 + L.q + L.k + L.v + L.o + L.h1 + L.attn + L.lm + L.etm + L.prm + L.kappa + L.genx +
+            L.genz + L.ent + L.gendet + L.flags + L.blkx + L.blksteps;
   return L;
 }
 
@@ -174,7 +176,7 @@ struct dg_model {
   int device;
   Layout L;
   char *ws;
-  void *h0, *q, *k, *v, *o, *h1, *attn, *lm;
+  void *h0, *q, *k, *v, *o, *h1, *attn, *lm, *etm;
   dg::StepParams *prm;
   float *kappa;
   int32_t *genx;
@@ -448,7 +450,7 @@ dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void 
     using u16 = uint16_t;
     {
       StageTimer tm(m, 4, st);
-      DG_HIP(dg::launch_lmhead_bf16(static_cast<const u16 *>(h1), static_cast<const u16 *>(m->w.E),
+      DG_HIP(dg::launch_lmhead_bf16(static_cast<const u16 *>(h1), static_cast<const u16 *>(m->etm),
                                   x_t, prm, s, seed, m->lm, p0, ent != nullptr, st),
            "LM head launch");
     }
@@ -693,6 +695,7 @@ dg_status dg_create(const dg_config *cfg, const dg_weights *w, dg_model **out) {
   m->h1 = p; p += L.h1;
   m->attn = p; p += L.attn;
   m->lm = p; p += L.lm;
+  m->etm = p; p += L.etm;
   m->prm = reinterpret_cast<dg::StepParams *>(p); p += L.prm;
   m->kappa = reinterpret_cast<float *>(p); p += L.kappa;
   m->genx = reinterpret_cast<int32_t *>(p); p += L.genx;
@@ -710,6 +713,18 @@ dg_status dg_create(const dg_config *cfg, const dg_weights *w, dg_model **out) {
   p += L.flags;
   m->blkx = reinterpret_cast<int32_t *>(p); p += L.blkx;
   m->blksteps = reinterpret_cast<int32_t *>(p); p += L.blksteps;
+  if (cfg->dtype == DG_DTYPE_BF16) {
+    // the LM head's tile-major copy of E, made once (E must not change while
+    // the model lives)
+    hipError_t re = dg::launch_lmhead_relayout(static_cast<const uint16_t *>(w->E), m->s,
+                                               static_cast<uint16_t *>(m->etm), nullptr);
+    if (re == hipSuccess) re = hipDeviceSynchronize();
+    if (re != hipSuccess) {
+      (void)hipFree(ws);
+      delete m;
+      return hip_fail(re, "copy of E for the LM head");
+    }
+  }
   *out = m;
   return DG_OK;
 }

@@ -136,10 +136,14 @@ hipError_t launch_attention_bf16(const uint16_t *q, const uint16_t *k, const uin
 bool lmhead_supported(const Shape &s);
 int lmhead_splits(const Shape &s);
 size_t lmhead_workspace_bytes(const Shape &s);
-// Fused LM head over V splits; writes RowPartial [splits, R] and z partials
-// [splits, R, d] bf16 into `work`, and raw scaled logits into p0 when non-null.
-// With `entropy` every row draws (no Bernoulli) and the entropy statistics
-// of RowPartial are filled in.
+// The LM head reads E from a tile-major copy (lmhead_copy_bytes, filled once
+// by launch_lmhead_relayout from the row-major [V, d] matrix).
+size_t lmhead_copy_bytes(const Shape &s);
+hipError_t launch_lmhead_relayout(const uint16_t *E, const Shape &s, uint16_t *Et, hipStream_t st);
+// Fused LM head over V splits (E: the tile-major copy); writes RowPartial
+// [splits, R] and z partials [splits, R, d] bf16 into `work`, and raw scaled
+// logits into p0 when non-null. With `entropy` every row draws (no
+// Bernoulli) and the entropy statistics of RowPartial are filled in.
 hipError_t launch_lmhead_bf16(const uint16_t *h1, const uint16_t *E, const int32_t *x_t,
                               const StepParams *prm, const Shape &s, uint64_t seed, void *work,
                               float *p0, bool entropy, hipStream_t st);

@@ -23,7 +23,10 @@
 //   3. z[m, slice] += P[m, tile] E[tile, slice] with v_mfma_f32_32x32x16_bf16
 //      (16x16x16 for 16-row blocks), E read transposed from LDS by
 //      ds_read_b64_tr_b16.
-// E tiles reach LDS by direct global->LDS loads (no register staging). With
+// E tiles reach LDS by direct global->LDS loads (no register staging) from a
+// tile-major copy of E made when the model is created: each 16-id x 32-column
+// chunk is 1 KB contiguous, already in the chunk's LDS order, so one direct
+// load reads whole cache lines. With
 // two tile buffers (d <= 2048) the next tile is requested in two halves
 // between the contractions (after the scores and after the epilogue), where
 // its LDS writes do not compete with the contractions' LDS reads; a single
@@ -193,13 +196,12 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
   auto ebuf = [&](int tile) -> uint8_t * {
     return Es + ((NBUF == 2 ? (tile & 1) : 0) * NW + wave) * SLICE_B;
   };
-  // one direct load fills a chunk: lane i writes LDS bytes [16 i, 16 i + 16),
-  // i.e. row i / 4, physical piece i % 4, which holds logical piece
-  // (i % 4) ^ eswz(i / 4) (the swizzle is an XOR, so its own inverse)
-  const uint32_t dma_off =
-      static_cast<uint32_t>(((lane >> 2) * a.d + (((lane & 3) ^ eswz(lane >> 2)) << 3)) * 2);
+  // one direct load fills a chunk: lane i copies bytes [16 i, 16 i + 16) of
+  // the chunk's 1 KB in the tile-major copy (see relayout_kernel) to the
+  // same bytes of the chunk in LDS
+  const uint32_t dma_off = static_cast<uint32_t>(lane * 16);
   auto dma_chunk = [&](int tile, int c) {
-    const uint16_t *tb = a.E + static_cast<int64_t>(tile * VT) * a.d + dcol0 + c * 32;
+    const uint16_t *tb = a.E + (static_cast<int64_t>(tile) * (a.d / 32) + dcol0 / 32 + c) * (VT * 32);
     lds_dma16(tb, dma_off, ebuf(tile) + c * CHUNK_B);
   };
   if (t_begin < t_end)
@@ -499,6 +501,24 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
   }
 }
 
+// Tile-major copy of E for the LM head: chunk q = tile * (d / 32) + c (ids
+// 16 tile + [0, 16), columns 32 c + [0, 32)) is 1 KB at Et + 512 q, and its
+// 16-byte piece i holds row i / 4, logical piece (i % 4) ^ eswz(i / 4), the
+// LDS order of the chunk (the swizzle is an XOR, so its own inverse). One
+// wave per chunk.
+__global__ void __launch_bounds__(256) relayout_kernel(const uint16_t *__restrict__ E, int d,
+                                                       int64_t chunks, uint16_t *__restrict__ Et) {
+  const int lane = threadIdx.x & 63;
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (q >= chunks) return;
+  const int cpr = d / 32;                          // chunks per 16-id tile
+  const int64_t tile = q / cpr;
+  const int c = static_cast<int>(q - tile * cpr);
+  const int row = lane >> 2, lp = (lane & 3) ^ eswz(row);
+  const uint4 v = *reinterpret_cast<const uint4 *>(E + (tile * VT + row) * d + 32 * c + 8 * lp);
+  *reinterpret_cast<uint4 *>(Et + q * (VT * 32) + 8 * lane) = v;
+}
+
 struct Plan {
   int MT, DW, NBUF, splits, tps;
 };
@@ -544,6 +564,21 @@ size_t lmhead_workspace_bytes(const Shape &s) {
   if (!plan(s, p)) return 0;
   const size_t R = static_cast<size_t>(s.R());
   return p.splits * R * (sizeof(RowPartial) + static_cast<size_t>(s.d) * sizeof(uint16_t));
+}
+
+size_t lmhead_copy_bytes(const Shape &s) {
+  return static_cast<size_t>(s.V) * s.d * sizeof(uint16_t);
+}
+
+hipError_t launch_lmhead_relayout(const uint16_t *E, const Shape &s, uint16_t *Et, hipStream_t st) {
+  Plan p;
+  if (!plan(s, p)) return hipErrorInvalidValue;
+  const int64_t chunks = static_cast<int64_t>(s.V / VT) * (s.d / 32);
+  const int64_t blocks = (chunks + 3) / 4;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(relayout_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, E, s.d,
+                     chunks, Et);
+  return hipGetLastError();
 }
 
 hipError_t launch_lmhead_bf16(const uint16_t *h1, const uint16_t *E, const int32_t *x_t,

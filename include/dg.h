@@ -110,10 +110,12 @@ typedef struct dg_model dg_model;
 
 /* Create a model over caller-owned weights. Allocates the library's own
  * device workspace (activations, split partials, per-step constants,
- * generation buffers); per-call host arrays reach the device as kernel
- * arguments, so no host memory outlives a call. Binds to the HIP device that
- * is current at the time of the call; later calls must run with that device
- * current. Weight pointers must be 16-byte aligned. *out is set only on DG_OK. */
+ * generation buffers and, for bf16, a tile-major copy of E that the LM head
+ * reads: E must keep its values while the model lives); per-call host arrays
+ * reach the device as kernel arguments, so no host memory outlives a call.
+ * Binds to the HIP device that is current at the time of the call; later
+ * calls must run with that device current. Weight pointers must be 16-byte
+ * aligned. Waits for the copy of E to finish. *out is set only on DG_OK. */
 dg_status dg_create(const dg_config *cfg, const dg_weights *w, dg_model **out);
 
 /* Frees the workspace; waits for the device to finish work already queued
