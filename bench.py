@@ -32,12 +32,17 @@ WORKLOADS = {
     "c5": "batched: B=32 C=256 P=4096 d=2048 16q/8kv heads x 128 V=131072 bf16, linear, per-canvas t",
 }
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "lmhead_counters.txt")
-LMHEAD_SRC = os.path.join(ROOT, "discrete_diffusion_decoding_dg_amd", "csrc", "k_lmhead.hip")
+# the LM-head kernel's source: its file and the device helpers it inlines
+LMHEAD_SRCS = [os.path.join(ROOT, "discrete_diffusion_decoding_dg_amd", "csrc", n)
+               for n in ("k_lmhead.hip", "dg_device.hpp")]
 
 
-def _sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def _sha(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic(workload):
@@ -50,7 +55,7 @@ def _traffic(workload):
         rec = rec.get(workload, rec if rec.get("workload") == workload else {})
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_source_sha") != _sha(LMHEAD_SRC):
+    if not rec or rec.get("kernel_source_sha") != _sha(LMHEAD_SRCS):
         return None
     return (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"]) * 1024.0
 

@@ -9,11 +9,11 @@ namespace dg {
 // Method, forward path equation): each token keeps x0 with probability kappa_b
 // and is otherwise a uniform token over [0, V). One Philox block serves the
 // token pair (2j, 2j+1) of a canvas: words 0/1 for the even token, 2/3 for the
-// odd one (keep draw, replacement word).
-__global__ void __launch_bounds__(256) corrupt_kernel(const int32_t *__restrict__ x0,
+// odd one (keep draw, replacement word). x0 and out may be the same array.
+__global__ void __launch_bounds__(256) corrupt_kernel(const int32_t *x0,
                                                       const float *__restrict__ kappa, int B,
                                                       int C, uint32_t V, uint32_t k0, uint32_t k1,
-                                                      int32_t *__restrict__ out, bool vec2) {
+                                                      int32_t *out, bool vec2) {
   const uint32_t pairs = (static_cast<uint32_t>(C) + 1u) >> 1;
   const uint64_t total = static_cast<uint64_t>(B) * pairs;
   const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
@@ -41,8 +41,70 @@ __global__ void __launch_bounds__(256) corrupt_kernel(const int32_t *__restrict_
   }
 }
 
+// The same draws for C % 4 == 0, 16-byte aligned arrays and fewer than 2^32
+// quads. A quad is four tokens (two pairs) of one canvas: one 16-byte load and
+// store. A thread takes quads base + 256 u, u < kQuadU, per iteration and
+// issues all their loads before the Philox work, so each wave keeps kQuadU
+// streaming loads in flight. The loads and stores are nontemporal: x0 is read
+// once and x_t written once. Measured with plain copies of 1 GiB: one 8-byte
+// load per thread and iteration copies at about 4.8 TB/s, four 16-byte
+// nontemporal loads per thread at about 6 TB/s; this kernel, Philox included,
+// at 5.6-5.7 TB/s with up to 64 blocks per CU.
+constexpr int kQuadU = 4;
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+
+// x0 and out may be the same array (no __restrict__): every quad is loaded
+// before it is stored, by the same thread.
+__global__ void __launch_bounds__(256) corrupt_quad_kernel(const int32_t *x0,
+                                                           const float *__restrict__ kappa,
+                                                           uint32_t qpc, uint64_t nquads, uint32_t V,
+                                                           uint32_t k0, uint32_t k1, int32_t *out) {
+  const i32x4v *src = reinterpret_cast<const i32x4v *>(x0);
+  i32x4v *dst = reinterpret_cast<i32x4v *>(out);
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * 256 * kQuadU;
+  for (uint64_t base = static_cast<uint64_t>(blockIdx.x) * 256 * kQuadU + threadIdx.x; base < nquads;
+       base += stride) {
+    i32x4v xv[kQuadU];
+#pragma unroll
+    for (int u = 0; u < kQuadU; ++u) {
+      const uint64_t q = base + 256u * u;
+      xv[u] = (q < nquads) ? __builtin_nontemporal_load(src + q) : i32x4v{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kQuadU; ++u) {
+      const uint64_t q = base + 256u * u;
+      if (q >= nquads) break;
+      const uint32_t q32 = static_cast<uint32_t>(q);   // nquads < 2^32
+      const uint32_t b = q32 / qpc;
+      const uint32_t j = 2u * (q32 - b * qpc);
+      const float kap = kappa[b];
+      const u32x4 w0 = philox4x32_10(j, 0u, b, kStreamCorrupt, k0, k1);
+      const u32x4 w1 = philox4x32_10(j + 1u, 0u, b, kStreamCorrupt, k0, k1);
+      i32x4v r;
+      r.x = (u01(w0.x) < kap) ? xv[u].x : static_cast<int32_t>(__umulhi(w0.y, V));
+      r.y = (u01(w0.z) < kap) ? xv[u].y : static_cast<int32_t>(__umulhi(w0.w, V));
+      r.z = (u01(w1.x) < kap) ? xv[u].z : static_cast<int32_t>(__umulhi(w1.y, V));
+      r.w = (u01(w1.z) < kap) ? xv[u].w : static_cast<int32_t>(__umulhi(w1.w, V));
+      __builtin_nontemporal_store(r, dst + q);
+    }
+  }
+}
+
 hipError_t launch_corrupt(const int32_t *x0, const float *kappa, int B, int C, int V,
                           uint64_t seed, int32_t *out, hipStream_t st) {
+  const uint64_t nquads = static_cast<uint64_t>(B) * (C / 4);
+  const bool quad = (C % 4 == 0) && nquads < (uint64_t{1} << 32) &&
+                    (reinterpret_cast<uintptr_t>(x0) % 16 == 0) &&
+                    (reinterpret_cast<uintptr_t>(out) % 16 == 0);
+  if (quad) {
+    if (nquads == 0) return hipSuccess;
+    uint64_t blocks = (nquads + 256 * kQuadU - 1) / (256 * kQuadU);
+    if (blocks > 256 * 64) blocks = 256 * 64;  // grid-stride beyond 64 blocks per CU
+    hipLaunchKernelGGL(corrupt_quad_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, x0,
+                       kappa, static_cast<uint32_t>(C / 4), nquads, static_cast<uint32_t>(V),
+                       static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), out);
+    return hipGetLastError();
+  }
   const uint64_t pairs = static_cast<uint64_t>(B) * ((C + 1) / 2);
   const bool vec2 = (C % 2 == 0) && (reinterpret_cast<uintptr_t>(x0) % 8 == 0) &&
                     (reinterpret_cast<uintptr_t>(out) % 8 == 0);

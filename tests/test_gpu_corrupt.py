@@ -28,11 +28,14 @@ def test_corrupt_bit_exact_with_model(name):
     m.close()
 
 
-@pytest.mark.parametrize("C", [1, 33, 256])
-def test_corrupt_batch_ragged_and_in_place(C):
+# C % 4 == 0 takes the 16-byte quad kernel (4, 36, 260, and 1001 x 12 = 3003
+# quads: three blocks of 1024, the last one partial); odd C and C % 4 == 2 the
+# pair kernel
+@pytest.mark.parametrize("B,C", [(5, 1), (5, 33), (5, 34), (5, 256), (5, 4), (5, 36), (5, 260), (1001, 12)])
+def test_corrupt_batch_ragged_and_in_place(B, C):
     import torch
     import discrete_diffusion_decoding_dg_amd as dg
-    B, V = 5, 1000
+    V = 1000
     rng = np.random.default_rng(C)
     x0 = rng.integers(0, V, (B, C)).astype(np.int32)
     kappa = rng.random(B).astype(np.float32)
@@ -41,6 +44,26 @@ def test_corrupt_batch_ragged_and_in_place(C):
     dg.dg_corrupt_batch(xd, kd, B, C, V, 99, xd)          # in place
     torch.cuda.synchronize()
     assert np.array_equal(xd.cpu().numpy(), corrupt(x0, kappa, 99, V))
+
+
+def test_corrupt_batch_unaligned_rows():
+    # arrays 4 bytes past a 16-byte boundary: the quad kernel does not apply
+    import torch
+    import discrete_diffusion_decoding_dg_amd as dg
+    B, C, V = 9, 20, 5000
+    rng = np.random.default_rng(7)
+    x0 = rng.integers(0, V, (B, C)).astype(np.int32)
+    kappa = rng.random(B).astype(np.float32)
+    buf = torch.zeros(B * C + 8, dtype=torch.int32, device="cuda")
+    obuf = torch.zeros(B * C + 8, dtype=torch.int32, device="cuda")
+    xd = buf[1:1 + B * C].view(B, C)
+    od = obuf[3:3 + B * C].view(B, C)
+    xd.copy_(torch.from_numpy(x0).cuda())
+    assert xd.data_ptr() % 16 != 0 and od.data_ptr() % 16 != 0
+    dg.dg_corrupt_batch(xd, torch.from_numpy(kappa).cuda(), B, C, V, 5, od)
+    torch.cuda.synchronize()
+    assert np.array_equal(od.cpu().numpy(), corrupt(x0, kappa, 5, V))
+    assert (obuf[:3] == 0).all() and (obuf[3 + B * C:] == 0).all()
 
 
 def test_corrupt_batch_at_bandwidth_size():
