@@ -46,6 +46,19 @@ def test_corrupt_batch_ragged_and_in_place(B, C):
     assert np.array_equal(xd.cpu().numpy(), corrupt(x0, kappa, 99, V))
 
 
+@pytest.mark.parametrize("B,C", [(0, 256), (4, 0)])
+def test_corrupt_batch_empty(B, C):
+    # no tokens: nothing is read or written, and the call succeeds
+    import torch
+    import discrete_diffusion_decoding_dg_amd as dg
+    x0 = torch.zeros(16, dtype=torch.int32, device="cuda")
+    out = torch.full((16,), 7, dtype=torch.int32, device="cuda")
+    kd = torch.zeros(max(B, 1), dtype=torch.float32, device="cuda")
+    dg.dg_corrupt_batch(x0, kd, B, C, 1000, 3, out)
+    torch.cuda.synchronize()
+    assert (out == 7).all()
+
+
 def test_corrupt_batch_unaligned_rows():
     # arrays 4 bytes past a 16-byte boundary: the quad kernel does not apply
     import torch

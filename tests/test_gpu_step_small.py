@@ -92,3 +92,27 @@ def test_taps_do_not_change_results():
     m.close()
     assert np.array_equal(a["x_out"], b["x_out"]) and np.array_equal(b["x_out"], c["x_out"])
     assert np.array_equal(a["z_out"], b["z_out"]) and np.array_equal(b["z_out"], c["z_out"])
+
+
+def test_out_of_range_tokens_embed_as_zero_rows():
+    # a guard, not part of the method: a token outside [0, V) contributes a
+    # zero embedding row, so h0 of that position is z itself (rounded)
+    import torch
+    from tests.dg_harness import to_host
+    cfg = _cfg("bf16-hd64")
+    inp = make_inputs(cfg)
+    m = GpuModel(cfg, inp)
+    xh = inp["x"].copy()
+    xh[0, 3], xh[1, 7], xh[1, cfg.C - 1] = -1, cfg.V, 2**31 - 1
+    x = torch.from_numpy(xh).cuda()
+    dev = {n: to_dev(inp, n, cfg) for n in ["K_pre", "V_pre"]}
+    gen = torch.Generator(device="cuda").manual_seed(4)
+    dev["z"] = (0.05 * torch.randn((cfg.B, cfg.C, cfg.d), device="cuda", generator=gen)).to(torch.bfloat16)
+    t = np.full(cfg.B, 0.5, np.float32)
+    g = m.step(x, dev["z"], dev["K_pre"], dev["V_pre"], t, 1 / 12, 9)
+    m.close()
+    zh = to_host(dev["z"])
+    for b, i in [(0, 3), (1, 7), (1, cfg.C - 1)]:
+        assert np.array_equal(g["h0"][b, i], zh[b, i])
+    ok = (xh >= 0) & (xh < cfg.V)
+    assert ((g["x_out"] >= 0) & (g["x_out"] < cfg.V) | ~ok).all()
