@@ -388,6 +388,9 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
 // o[r, h, e] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s. One thread
 // per four consecutive columns of a row (hd % 4 == 0): the split weights are
 // computed once per thread and the bf16 partials stream as 8-byte loads.
+// NP > 0 (splits <= NP): every (m, l) and partial load of the thread is issued
+// before the maximum over the splits, so that their latencies overlap.
+template <int NP>
 __global__ void __launch_bounds__(256) attn_combine_kernel(const uint16_t *__restrict__ opart,
                                                            const float2 *__restrict__ ml,
                                                            int splits, int64_t rows, int hd,
@@ -398,6 +401,38 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const uint16_t *__res
        t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int64_t row = t / q4;
     const int64_t idx = row * hd + 4 * (t - row * q4);
+    if constexpr (NP > 0) {
+      uint2 xr[NP];
+      float2 mr[NP];
+#pragma unroll
+      for (int k = 0; k < NP; ++k) {
+        const int sp = k < splits ? k : splits - 1;
+        xr[k] = *reinterpret_cast<const uint2 *>(opart + sp * total + idx);
+        mr[k] = ml[sp * rows + row];
+      }
+      float M = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < NP; ++k) M = fmaxf(M, mr[k].x);   // surplus entries repeat the last split
+      float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+      float den = 0.f;
+#pragma unroll
+      for (int k = 0; k < NP; ++k) {
+        if (k < splits) {
+          const float w = exp2f(mr[k].x - M);
+          num.x += w * __uint_as_float(xr[k].x << 16);
+          num.y += w * __uint_as_float(xr[k].x & 0xFFFF0000u);
+          num.z += w * __uint_as_float(xr[k].y << 16);
+          num.w += w * __uint_as_float(xr[k].y & 0xFFFF0000u);
+          den += w * mr[k].y;
+        }
+      }
+      const float inv = 1.f / den;
+      uint2 out;
+      out.x = pack_bf16x2(num.x * inv, num.y * inv);
+      out.y = pack_bf16x2(num.z * inv, num.w * inv);
+      *reinterpret_cast<uint2 *>(o + idx) = out;
+      continue;
+    }
     float M = -INFINITY;
     for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[s * rows + row].x);
     float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -495,8 +530,16 @@ hipError_t launch_attention_bf16(const uint16_t *q, const uint16_t *k, const uin
   const int64_t total4 = static_cast<int64_t>(rows) * (s.hd / 4);
   int64_t blocks = (total4 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st,
-                     a.opart, a.ml, a.splits, static_cast<int64_t>(rows), s.hd, o);
+  const dim3 cgrid(static_cast<uint32_t>(blocks));
+  if (a.splits <= 8)
+    hipLaunchKernelGGL(attn_combine_kernel<8>, cgrid, dim3(256), 0, st, a.opart, a.ml, a.splits,
+                       static_cast<int64_t>(rows), s.hd, o);
+  else if (a.splits <= 16)
+    hipLaunchKernelGGL(attn_combine_kernel<16>, cgrid, dim3(256), 0, st, a.opart, a.ml, a.splits,
+                       static_cast<int64_t>(rows), s.hd, o);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<0>, cgrid, dim3(256), 0, st, a.opart, a.ml, a.splits,
+                       static_cast<int64_t>(rows), s.hd, o);
   return hipGetLastError();
 }
 

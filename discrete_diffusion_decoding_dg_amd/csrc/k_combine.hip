@@ -62,7 +62,10 @@ __device__ __forceinline__ float lane_value(float v, int s) {   // s wave-unifor
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), s));
 }
 
-template <typename T, typename ZP>
+// NPRE: bf16 partial loads per thread issued before the split statistics are
+// reduced (at least ceil(splits / groups); the surplus re-read the last
+// split and are not summed), so that their latency overlaps the reductions.
+template <typename T, typename ZP, int NPRE>
 __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restrict__ part,
                                                       const ZP *__restrict__ zpart, int splits,
                                                       const int32_t *__restrict__ x_t,
@@ -86,6 +89,21 @@ __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restri
     if (q == 0)
       for (int c = c0; c < c0 + kCols && c < d; ++c) z_out[rowoff + c] = z_t[rowoff + c];
     return;
+  }
+  const int64_t sstride = static_cast<int64_t>(R) * d;
+  constexpr bool kPrefetch = NPRE > 0;
+  uint4 raw[kPrefetch ? NPRE : 1];
+  if constexpr (kPrefetch) {
+    // split q + k groups of this thread's 8 columns (clamped to valid
+    // addresses; only the splits below `splits` are summed further down)
+    const int cc = (c0 + kCols <= d) ? c0 : 0;
+    const uint16_t *zp = reinterpret_cast<const uint16_t *>(zpart) + rowoff + cc;
+#pragma unroll
+    for (int k = 0; k < NPRE; ++k) {
+      int sp = q + k * groups;
+      if (sp > splits - 1) sp = splits - 1;
+      raw[k] = *reinterpret_cast<const uint4 *>(zp + sp * sstride);
+    }
   }
   RowPartial p;
   p.m = -INFINITY;
@@ -142,14 +160,27 @@ __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restri
     }
   }
   const float il = 1.f / L;
-  const int64_t sstride = static_cast<int64_t>(R) * d;
   if ((d % kCols) == 0) {
     // group q sums splits q, q + groups, ...; the groups meet in LDS
     const bool active = c0 + kCols <= d;
     float acc[kCols];
 #pragma unroll
     for (int i = 0; i < kCols; ++i) acc[i] = 0.f;
-    if (active) {
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int k = 0; k < NPRE; ++k) {
+        const int sp = q + k * groups;   // wave-uniform
+        if (sp < splits) {
+          const float ws = lane_value(w, sp);
+          const uint32_t wd[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += ws * __uint_as_float(wd[i] << 16);
+            acc[2 * i + 1] += ws * __uint_as_float(wd[i] & 0xFFFF0000u);
+          }
+        }
+      }
+    } else if (active) {
       const ZP *zp = zpart + rowoff + c0;
 #pragma unroll 8
       for (int sp = q; sp < splits; sp += groups) {
@@ -207,16 +238,26 @@ hipError_t launch_combine(bool bf16, const void *work, int splits, const int32_t
   const dim3 grid(R, (s.d + strip - 1) / strip);
   const EntropyRows er = ent ? *ent : EntropyRows{nullptr, nullptr, nullptr};
   if (frozen && !z_t) return hipErrorInvalidValue;
-  if (bf16)
-    hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st, part,
-                       reinterpret_cast<const uint16_t *>(zbase), splits,
-                       x_t, prm, R, s.C, s.d, k0, k1, x_out, static_cast<uint16_t *>(z_out), lse,
-                       best, er, frozen, static_cast<const uint16_t *>(z_t), groups);
+  // bf16 partials with d % 8 == 0 are prefetched: 8 or 16 loads per thread
+  const int per_group = (splits + groups - 1) / groups;
+  const bool pre = bf16 && s.d % kCols == 0 && per_group <= 16;
+#define DG_COMB(NP)                                                                              \
+  hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t, NP>), grid, dim3(256), 0, st, part,     \
+                     reinterpret_cast<const uint16_t *>(zbase), splits, x_t, prm, R, s.C, s.d, k0, \
+                     k1, x_out, static_cast<uint16_t *>(z_out), lse, best, er, frozen,            \
+                     static_cast<const uint16_t *>(z_t), groups)
+  if (pre && per_group <= 8)
+    DG_COMB(8);
+  else if (pre)
+    DG_COMB(16);
+  else if (bf16)
+    DG_COMB(0);
   else
-    hipLaunchKernelGGL((combine_kernel<float, float>), grid, dim3(256), 0, st, part,
+    hipLaunchKernelGGL((combine_kernel<float, float, 0>), grid, dim3(256), 0, st, part,
                        reinterpret_cast<const float *>(zbase), splits, x_t,
                        prm, R, s.C, s.d, k0, k1, x_out, static_cast<float *>(z_out), lse, best,
                        er, frozen, static_cast<const float *>(z_t), groups);
+#undef DG_COMB
   return hipGetLastError();
 }
 
