@@ -305,14 +305,11 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
         m_ref = tmax;
       }
       l_lane *= alpha;
-      // O rows of this lane are queries 8 jj + 4 hl + i; their factors live
-      // in lanes 0..31 (one per query)
+      // every O^T element of this lane belongs to its own query
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float f = __shfl(alpha, 8 * (e >> 2) + 4 * hl + (e & 3), 64);
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) oacc[nb][e] *= f;
-      }
+        for (int e = 0; e < 16; ++e) oacc[nb][e] *= alpha;
     }
     // P in the k-slot order of the PV contraction: for the 16-key step kk
     // (block mb = kk / 2, half kk2 = kk % 2) the A operand is elements
@@ -346,41 +343,43 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4 *)(pb + kslot(16 * kk + 8 + tr_key, p) * 16));
         const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], vb, oacc[nb], 0, 0, 0);
+        // O^T = V^T P^T: the V fragment as A operand (row = head column), P
+        // as B operand (column = query); the k slots are the same as for P V
+        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, pa[kk], oacc[nb], 0, 0, 0);
       }
     }
   }
 
-  // ---- normalise, or write the split partials
-  const float l_q = l_lane + __shfl_xor(l_lane, 32, 64);   // lanes q and q + 32 hold query q
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int rq = 8 * (e >> 2) + 4 * hl + (e & 3);       // query of this O element
-    const float lr = __shfl(l_q, rq, 64);
-    const float mr = __shfl(m_ref, rq, 64);
-    const int row = qb * BQ + wave * 32 + rq;
-    if (row >= GC) continue;
-    const int h = g * a.G + row / a.C, ii = row % a.C;
-    const int64_t r = static_cast<int64_t>(b) * a.C + ii;
-    if (a.splits == 1) {
-      const float inv = 1.f / lr;
-      uint16_t *orow = a.o + r * qcols + h * HD;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int col = 32 * nb + (lane & 31);
-        if (HDP == HD || col < HD) orow[col] = f32_to_bf16(oacc[nb][e] * inv);
-      }
-    } else {
-      const int64_t R = static_cast<int64_t>(a.B) * a.C;
+  // ---- normalise, or write the split partials. oacc[nb] holds O^T: lane
+  // (hl, q) has query q = lane & 31 and, per element 4 jj + i, head column
+  // 32 nb + 8 jj + 4 hl + i, so each jj gives four consecutive columns (one
+  // 8-byte store)
+  {
+    const float l_q = l_lane + __shfl_xor(l_lane, 32, 64);   // lanes q and q + 32 hold query q
+    const int row = qb * BQ + wave * 32 + (lane & 31);
+    if (row < GC) {
+      const int h = g * a.G + row / a.C, ii = row % a.C;
+      const int64_t r = static_cast<int64_t>(b) * a.C + ii;
+      const bool whole = a.splits == 1;
+      const float sc = whole ? 1.f / l_q : 1.f;
       // partials travel in bf16: the merge rescales and sums them in fp32
       // and rounds the result to bf16 anyway; half the bytes of fp32
-      uint16_t *prow = a.opart + ((split * R + r) * a.Hq + h) * HD;
+      uint16_t *dst = whole ? a.o + r * qcols + h * HD
+                            : a.opart + ((split * (static_cast<int64_t>(a.B) * a.C) + r) * a.Hq + h) * HD;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int col = 32 * nb + (lane & 31);
-        if (HDP == HD || col < HD) prow[col] = f32_to_bf16(oacc[nb][e]);
-      }
-      if ((lane & 31) == 0) a.ml[(split * R + r) * a.Hq + h] = make_float2(mr, lr);
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int col = 32 * nb + 8 * jj + 4 * hl;
+          if (HDP == HD || col < HD) {
+            uint2 v;
+            v.x = pack_bf16x2(oacc[nb][4 * jj] * sc, oacc[nb][4 * jj + 1] * sc);
+            v.y = pack_bf16x2(oacc[nb][4 * jj + 2] * sc, oacc[nb][4 * jj + 3] * sc);
+            *reinterpret_cast<uint2 *>(dst + col) = v;
+          }
+        }
+      if (!whole && hl == 0)
+        a.ml[(split * (static_cast<int64_t>(a.B) * a.C) + r) * a.Hq + h] = make_float2(m_ref, l_q);
     }
   }
 }
