@@ -189,6 +189,18 @@ def main():
     dg.dg_profile_enable(model, [])
     prof = dg.dg_profile_read(model)
     ms_per_step_profiled = p0.elapsed_time(p1) / args.steps
+    # distribution of single-step times: an event pair around each step, in a
+    # pass of its own (the pairs add queue time, so it does not touch `value`)
+    nd = min(args.steps, 100)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nd)]
+    for k in range(nd):
+        evs[k][0].record()
+        step(args.warmup + 2 * args.steps + k)
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    one = np.sort(np.array([a.elapsed_time(b) for a, b in evs]))
+    step_dist = {"steps": nd, "p10_ms": float(np.percentile(one, 10)),
+                 "p50_ms": float(np.percentile(one, 50)), "p90_ms": float(np.percentile(one, 90))}
     # per-stage durations from one short pass with every stage bracketed
     dg.dg_profile_enable(model, None)
     for k in range(20):
@@ -426,6 +438,7 @@ def main():
         "step_frac_mfma": fl["total"] / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "generate_canvas_ms": gen_ms,
         "ms_per_step_with_lmhead_events": ms_per_step_profiled,
+        "step_ms_distribution": step_dist,
         "roofline": {"bound": "mfma", "kernel": "lmhead_kernel", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic, "avg_ms": lm_avg_ms,

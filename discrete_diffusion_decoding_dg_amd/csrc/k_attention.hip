@@ -58,6 +58,7 @@ struct AttnArgs {
   uint16_t *opart;   // [splits][R][Hq][hd] unnormalised bf16, when splits > 1
   float2 *ml;     // [splits][R][Hq] (m, l), log2 units
   int B, C, P, Pst, Hq, Hkv, G, splits, tiles_per_split;   // Pst: cache rows per (b, g)
+  int qblocks;                                              // query blocks per (b, g, split)
   float scale_log2;   // log2(e) / sqrt(hd)
 };
 
@@ -143,8 +144,17 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qb = blockIdx.x, g = blockIdx.y;
-  const int b = blockIdx.z / a.splits, split = blockIdx.z - b * a.splits;
+  // XCD-aware order: the hardware deals consecutive blocks round-robin to the
+  // 8 XCDs; the logical id gives each XCD a contiguous run, so the query
+  // blocks that share a kv head and key range (consecutive ids) share an L2
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int nqb = a.qblocks;
+  const int qb = bid % nqb;
+  const int rest = bid / nqb;
+  const int g = rest % a.Hkv, bz = rest / a.Hkv;
+  const int b = bz / a.splits, split = bz - b * a.splits;
   const int GC = a.G * a.C;
   const int Lk = a.P + a.C;
   const int qcols = a.Hq * HD;
@@ -511,7 +521,10 @@ hipError_t launch_attention_bf16(const uint16_t *q, const uint16_t *k, const uin
                                     static_cast<size_t>(a.splits) * rows * s.hd * sizeof(uint16_t));
   a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(s.hd)));
   const int bq = nwa * 32;
-  dim3 grid((s.G() * s.C + bq - 1) / bq, s.Hkv, s.B * a.splits);
+  a.qblocks = (s.G() * s.C + bq - 1) / bq;
+  const int64_t nblocks = static_cast<int64_t>(a.qblocks) * s.Hkv * s.B * a.splits;
+  if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid(static_cast<uint32_t>(nblocks));
 #define DG_ATT(HD_)                                                                       \
   case HD_:                                                                               \
     if (nwa == 8)                                                                         \
