@@ -415,6 +415,12 @@ def main():
         if k in kernels and kernels[k]["avg_ms"]:
             tf = f / (kernels[k]["avg_ms"] * 1e-3) / 1e12
             kernels[k].update({"algorithmic_flop": f, "tflops": tf, "frac_mfma_bf16": tf / PEAK_BF16_TFLOPS})
+    # the attention's K/V stream (prefix cache plus canvas keys, K and V, bf16)
+    # against the HBM peak; the stage is MFMA-bound, so this is context
+    if "attention" in kernels and kernels["attention"]["avg_ms"]:
+        kv = 2.0 * 2 * cfg.B * cfg.n_kv_heads * (cfg.P + cfg.C) * cfg.head_dim
+        gbs = kv / (kernels["attention"]["avg_ms"] * 1e-3) / 1e9
+        kernels["attention"].update({"kv_bytes": kv, "kv_GB_s": gbs, "kv_frac_hbm": gbs / PEAK_HBM_GBS})
     steps_per_s = 1000.0 / ms_per_step
     result = {
         "metric": METRIC,
