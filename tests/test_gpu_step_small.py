@@ -28,6 +28,10 @@ SMALL = {
     # group of four Gumbel tiles; zero prefix (P = 0: canvas keys only)
     "bf16-vocab-1040-p0": dict(base="c2", B=2, C=40, P=0, d=256, n_q_heads=4, n_kv_heads=2,
                                head_dim=64, V=1040),
+    # few query rows against a long prefix: 63 key tiles in 32 splits of two,
+    # more splits than the merge kernel prefetches (16)
+    "bf16-long-prefix-32-splits": dict(base="c3", B=1, C=8, P=4000, d=256, n_q_heads=4, n_kv_heads=2,
+                                       head_dim=64, V=512),
     # enough rows (2250 = 8 x 256 + 202) for the 256 x 256-tile projections,
     # with a ragged last row tile
     "bf16-many-rows": dict(base="c5", B=9, C=250, P=70, d=256, n_q_heads=4, n_kv_heads=4,
