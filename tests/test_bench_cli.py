@@ -30,3 +30,25 @@ def test_help_lists_the_contract_flags():
     assert r.returncode == 0
     for flag in ["--gpus", "--steps", "--warmup", "--workload"]:
         assert flag in r.stdout
+
+
+def test_traffic_is_dropped_once_the_lm_head_source_changes(tmp_path, monkeypatch):
+    # roofline.traffic comes from stored counters only while the hash of the
+    # LM-head source (the kernel file and the device helpers it inlines)
+    # matches the one recorded with them
+    import json
+    sys.path.insert(0, ROOT)
+    import bench
+    srcs = [tmp_path / "k.hip", tmp_path / "h.hpp"]
+    srcs[0].write_text("kernel v1\n")
+    srcs[1].write_text("helpers v1\n")
+    monkeypatch.setattr(bench, "LMHEAD_SRCS", [str(p) for p in srcs])
+    rec = {"c2": {"workload": "c2", "kernel_source_sha": bench._sha([str(p) for p in srcs]),
+                  "fetch_kib": 100.0, "fetch_factor": 2.0, "write_kib": 10.0, "write_factor": 1.0}}
+    counters = tmp_path / "counters.txt"
+    counters.write_text("# header\n" + json.dumps(rec) + "\n")
+    monkeypatch.setattr(bench, "COUNTERS_FILE", str(counters))
+    assert bench._traffic("c2") == (100.0 * 2.0 + 10.0) * 1024.0
+    assert bench._traffic("c5") is None
+    srcs[1].write_text("helpers v2\n")          # a helper changed: the counters are stale
+    assert bench._traffic("c2") is None
