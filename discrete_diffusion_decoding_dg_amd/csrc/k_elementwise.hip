@@ -77,14 +77,18 @@ __global__ void __launch_bounds__(256) corrupt_quad_kernel(const int32_t *x0,
       const uint32_t q32 = static_cast<uint32_t>(q);   // nquads < 2^32
       const uint32_t b = q32 / qpc;
       const uint32_t j = 2u * (q32 - b * qpc);
-      const float kap = kappa[b];
+      // u01(w) < kappa in integers: u01(w) = (2 (w >> 9) + 1) 2^-24 exactly,
+      // so the draw keeps x0 iff 2 (w >> 9) + 1 < T = kappa 2^24 (exact), iff
+      // (w >> 9) < ceil((T - 1) / 2); every step of that bound is exact in
+      // fp32 for T up to 2^24 (and the conversion saturates above)
+      const int kth = static_cast<int>(ceilf((kappa[b] * 16777216.f - 1.f) * 0.5f));
       const u32x4 w0 = philox4x32_10(j, 0u, b, kStreamCorrupt, k0, k1);
       const u32x4 w1 = philox4x32_10(j + 1u, 0u, b, kStreamCorrupt, k0, k1);
       i32x4v r;
-      r.x = (u01(w0.x) < kap) ? xv[u].x : static_cast<int32_t>(__umulhi(w0.y, V));
-      r.y = (u01(w0.z) < kap) ? xv[u].y : static_cast<int32_t>(__umulhi(w0.w, V));
-      r.z = (u01(w1.x) < kap) ? xv[u].z : static_cast<int32_t>(__umulhi(w1.y, V));
-      r.w = (u01(w1.z) < kap) ? xv[u].w : static_cast<int32_t>(__umulhi(w1.w, V));
+      r.x = (static_cast<int>(w0.x >> 9) < kth) ? xv[u].x : static_cast<int32_t>(__umulhi(w0.y, V));
+      r.y = (static_cast<int>(w0.z >> 9) < kth) ? xv[u].y : static_cast<int32_t>(__umulhi(w0.w, V));
+      r.z = (static_cast<int>(w1.x >> 9) < kth) ? xv[u].z : static_cast<int32_t>(__umulhi(w1.y, V));
+      r.w = (static_cast<int>(w1.z >> 9) < kth) ? xv[u].w : static_cast<int32_t>(__umulhi(w1.w, V));
       __builtin_nontemporal_store(r, dst + q);
     }
   }
