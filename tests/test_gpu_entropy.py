@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from oracle import accept_mask, entropy_step, generate_canvas_entropy
-from tests.dg_harness import (NEAR_TIE, RTOL_BF16, RTOL_F32, GpuModel, act_tensor, assert_close,
+from tests.dg_harness import (NEAR_TIE, near_ties, RTOL_BF16, RTOL_F32, GpuModel, act_tensor, assert_close,
                               to_dev, to_host)
 from workloads import get_config, make_inputs
 
@@ -71,6 +71,9 @@ def test_entropy_step_matches_oracle(name):
     htol = _htol(cfg, o["H"])
     assert np.all(np.abs(g["H"] - o["H"]) <= htol), f"entropy: max err {np.abs(g['H'] - o['H']).max():.3e}"
     assert_close("z", g["z_out"], o["z_out"], RTOL_F32 if cfg.dtype == "f32" else RTOL_BF16)
+    # the plain argmax has no Gumbel noise: its top logits are far below 1 at
+    # these weight scales, so the near-tie band is floored at NEAR_TIE
+    # absolute (the logits' own bf16 rounding is of that order)
     det_near = o["det_gap"] < NEAR_TIE * np.maximum(1.0, np.abs(o["det_top"]))
     assert not ((g["det_h"] != o["det"]) & ~det_near).any(), "argmax differs off near-ties"
     assert not g["stop"].any(), "first step must not stop"
@@ -100,7 +103,7 @@ def test_entropy_step_matches_oracle(name):
                 f"canvas {b}: acceptance differs away from the boundary"
     # accepted tokens are the draws (up to near-ties); rejected ones the re-noise tokens exactly
     both = g_acc & o["accept"] & ~amb
-    near = o["gap"] < NEAR_TIE * np.maximum(1.0, np.abs(o["top1"]))
+    near = near_ties(o["gap"], o["top1"])
     assert not ((g["x_out"] != o["y"]) & both & ~near).any(), "accepted draws differ off near-ties"
     rej = ~g_acc & ~o["accept"]
     assert np.array_equal(g["x_out"][rej], o["renoise"][rej])
@@ -185,7 +188,7 @@ def test_adaptive_generation_equals_stepwise_and_oracle(name, eps_a, eps_s):
             break
         act = rec["active"]
         htol = _htol(cfg, rec["H"])
-        near = (rec["gap"] < NEAR_TIE * np.maximum(1.0, np.abs(rec["top1"]))) & rec["accept"]
+        near = near_ties(rec["gap"], rec["top1"]) & rec["accept"]
         dnear = rec["det_gap"] < NEAR_TIE * np.maximum(1.0, np.abs(rec["det_top"]))
         border = np.zeros(len(act), dtype=bool)
         for j in range(len(act)):

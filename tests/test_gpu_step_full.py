@@ -1,6 +1,6 @@
 """GPU parity of one denoising step at the full workload sizes, in the launch
 configuration the benchmark times. The standard and long-prefix canvases are
-checked on every row; the large-vocabulary and batched workloads compute
+checked on every row (p0 included); the large-vocabulary and batched workloads compute
 every decoder stage on the oracle for all rows of the sampled canvases and
 the LM head, z and the Step draw on sampled rows (rows are independent)."""
 import numpy as np
@@ -79,9 +79,9 @@ def test_long_prefix_all_rows():
     cfg = get_config("c3")
     inp = make_inputs(cfg)
     t = np.full(cfg.B, 0.25, np.float32)
-    g = _gpu_step(cfg, inp, t, seed=22, p0=False)
+    g = _gpu_step(cfg, inp, t, seed=22, p0=True)
     rows = np.arange(cfg.C)
-    o = _oracle(cfg, inp, t, 22, np.arange(cfg.B), rows, want_p0=False)
+    o = _oracle(cfg, inp, t, 22, np.arange(cfg.B), rows, want_p0=True)
     _compare(cfg, g, o, np.arange(cfg.B), rows)
 
 
@@ -90,7 +90,9 @@ def test_large_vocabulary_sampled_rows():
     inp = make_inputs(cfg)
     t = np.full(cfg.B, 1.0 / 12, np.float32)      # lambda = 1: every row draws from p0
     g = _gpu_step(cfg, inp, t, seed=23, p0=True)
-    rows = np.array([0, 1, 15, 16, 31, 32, 100, 127, 128, 200, 254, 255])
+    # 58 rows: every fifth row, plus both sides of the 16-, 32- and 128-row
+    # block edges and the last two rows
+    rows = np.unique(np.concatenate([np.arange(0, cfg.C, 5), [15, 16, 31, 32, 127, 128, 254, 255]]))
     o = _oracle(cfg, inp, t, 23, np.arange(cfg.B), rows, want_p0=True)
     _compare(cfg, g, o, np.arange(cfg.B), rows)
 
@@ -101,8 +103,11 @@ def test_batched_sampled_canvases_and_rows():
     t = inp["t"]
     g = _gpu_step(cfg, inp, t, seed=24, p0=False)
     nz = inp["z_nonzero"]
-    canvases = np.array([int(np.argmax(nz)), int(np.argmax(~nz)), cfg.B - 1])
-    rows = np.array([0, 5, 31, 32, 77, 128, 255])
+    # three canvases with z = 0 and three with z != 0 (the last one included)
+    zc = np.flatnonzero(~nz)[:3]
+    nzc = np.flatnonzero(nz)[:3]
+    canvases = np.unique(np.concatenate([zc, nzc, [cfg.B - 1]]))
+    rows = np.array([0, 5, 17, 31, 32, 63, 64, 77, 100, 127, 128, 150, 191, 200, 223, 255])
     o = _oracle(cfg, inp, t, 24, canvases, rows, want_p0=False)
     _compare(cfg, g, o, canvases, rows)
     # every canvas's kept rows carry their input tokens

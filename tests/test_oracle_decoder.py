@@ -97,9 +97,31 @@ def test_lm_head_softmax_against_library_routines():
     assert np.allclose(r["p0"], scipy.special.softmax(s, axis=1), atol=1e-15)
     assert np.allclose(r["lse"], scipy.special.logsumexp(s, axis=1), atol=1e-13)
     assert np.all(r["p0"] >= 0) and np.allclose(r["p0"].sum(axis=1), 1.0, atol=1e-12)
-    # shift invariance: adding a constant row offset to s leaves p0 unchanged
-    r2 = lm_head(h1, E, inv_tau, "f64", want_p0=True)
-    assert np.allclose(r2["p0"], r["p0"])
+
+
+def test_lm_head_row_shift_moves_lse_not_p0():
+    """Adding a row constant c to the scaled logits leaves p0 unchanged and moves
+    lse by exactly c. The shift is made through the inputs: an extra column of
+    h1 that meets a column of ones appended to E adds h_extra * inv_tau to every
+    logit of that row."""
+    rng = np.random.default_rng(15)
+    B, C, d, V = 2, 3, 6, 11
+    h1 = rng.standard_normal((B, C, d))
+    E = rng.standard_normal((V, d))
+    inv_tau = np.array([1.25, 2.0], dtype=np.float32)
+    base = lm_head(h1, E, inv_tau, "f64", want_p0=True)
+    shift = rng.uniform(-3.0, 3.0, size=(B, C))
+    h1s = np.concatenate([h1, shift[:, :, None]], axis=2)
+    Es = np.concatenate([E, np.ones((V, 1))], axis=1)
+    r = lm_head(h1s, Es, inv_tau, "f64", want_p0=True)
+    c = (shift * inv_tau.astype(np.float64)[:, None]).reshape(-1)
+    assert np.allclose(r["s"], base["s"] + c[:, None], atol=1e-12)
+    assert np.allclose(r["p0"], base["p0"], atol=1e-14)
+    assert np.allclose(r["lse"], base["lse"] + c, atol=1e-12)
+    # a slip that dropped the max subtraction or the log would move p0 or
+    # break lse - c; a slip that applied tau per row instead of per canvas
+    # would break the per-canvas shift above
+    assert not np.allclose(r["lse"], base["lse"])
 
 
 def test_z_special_cases():
@@ -153,3 +175,94 @@ def test_bf16_rounding_matches_torch_and_ties_to_even():
     assert round_bf16(one + 3 * 2 ** -8) == one + 2 ** -6    # tie -> even (upwards)
     assert round_bf16(-(one + 2 ** -8 + 2 ** -20)) == -(one + 2 ** -7)
     assert round_bf16(0.0) == 0.0
+
+
+def test_embed_adds_self_conditioning_explicit_sum():
+    """h0[b, i, :] = E[x[b, i], :] + z[b, i, :], element by element, with z != 0
+    (TR summary, Method, decoder equation: z_t is a decoder input)."""
+    rng = np.random.default_rng(16)
+    B, C, d, V = 2, 5, 7, 9
+    E = rng.standard_normal((V, d))
+    x = rng.integers(0, V, size=(B, C))
+    z = rng.standard_normal((B, C, d))
+    h0 = embed(E, x, z, "f64")
+    for b in range(B):
+        for i in range(C):
+            for e in range(d):
+                assert h0[b, i, e] == E[x[b, i], e] + z[b, i, e]
+    # the z term matters: zeroing it changes every entry
+    assert np.all(embed(E, x, np.zeros_like(z), "f64") != h0)
+
+
+def test_embed_rounds_the_sum_once_in_bf16():
+    """bf16 workloads round E[x] + z once (not E[x] and z separately)."""
+    E = np.array([[1.0, 0.0], [0.0, 1.0]])
+    z = np.array([[[2 ** -9, 0.0], [0.0, 2 ** -9 + 2 ** -20]]])
+    h0 = embed(E, np.array([[0, 1]]), z, "bf16")
+    # 1 + 2^-9 is below the bf16 half-ulp (2^-8): rounds to 1; a value just
+    # above the tie rounds up to 1 + 2^-7 only when the sum is rounded once
+    assert h0[0, 0, 0] == 1.0
+    assert h0[0, 1, 1] == 1.0
+    z2 = np.array([[[2 ** -8 + 2 ** -20, 0.0], [0.0, 0.0]]])
+    h0b = embed(E, np.array([[0, 1]]), z2, "bf16")
+    assert h0b[0, 0, 0] == 1.0 + 2 ** -7
+
+
+def test_qkv_projection_explicit_sums_rectangular():
+    """q = h0 Wq^T with Wq [Hq*hd, d] and k, v = h0 W^T written head-major,
+    on a rectangular case (Hq*hd != d, Hkv*hd != d), so a product with W
+    instead of W^T cannot even be formed the same way."""
+    rng = np.random.default_rng(17)
+    B, C, d, Hq, Hkv, hd = 2, 3, 5, 4, 2, 3
+    h0 = rng.standard_normal((B, C, d))
+    Wq = rng.standard_normal((Hq * hd, d))
+    Wk = rng.standard_normal((Hkv * hd, d))
+    Wv = rng.standard_normal((Hkv * hd, d))
+    q, k, v = qkv_proj(h0, Wq, Wk, Wv, Hq, Hkv, hd, "f64")
+    assert q.shape == (B, C, Hq, hd) and k.shape == (B, Hkv, C, hd) and v.shape == (B, Hkv, C, hd)
+    for b in range(B):
+        for i in range(C):
+            for h in range(Hq):
+                for e in range(hd):
+                    want = sum(h0[b, i, c] * Wq[h * hd + e, c] for c in range(d))
+                    assert abs(q[b, i, h, e] - want) < 1e-12
+            for g in range(Hkv):
+                for e in range(hd):
+                    wk = sum(h0[b, i, c] * Wk[g * hd + e, c] for c in range(d))
+                    wv = sum(h0[b, i, c] * Wv[g * hd + e, c] for c in range(d))
+                    assert abs(k[b, g, i, e] - wk) < 1e-12
+                    assert abs(v[b, g, i, e] - wv) < 1e-12
+
+
+def test_out_projection_explicit_sums_rectangular():
+    """h1[b, i, c] = h0[b, i, c] + sum_j o[b, i, j] Wo[c, j], with Wo [d, Hq*hd]
+    rectangular (Hq*hd != d) and a non-zero o, so an o Wo (untransposed)
+    slip or a dropped residual fails."""
+    rng = np.random.default_rng(18)
+    B, C, d, Hq, hd = 2, 3, 5, 2, 4          # Hq*hd = 8 != d = 5
+    o = rng.standard_normal((B, C, Hq, hd))
+    Wo = rng.standard_normal((d, Hq * hd))
+    h0 = rng.standard_normal((B, C, d))
+    h1 = out_proj(o, Wo, h0, "f64")
+    assert h1.shape == (B, C, d)
+    for b in range(B):
+        for i in range(C):
+            flat = o[b, i].reshape(-1)
+            for c in range(d):
+                want = h0[b, i, c] + sum(flat[j] * Wo[c, j] for j in range(Hq * hd))
+                assert abs(h1[b, i, c] - want) < 1e-12
+
+
+def test_out_projection_square_transpose_slip_detected():
+    """The square case (d = Hq*hd, as in every configured workload): o Wo^T
+    differs from o Wo for a non-symmetric Wo, and the oracle takes the former."""
+    rng = np.random.default_rng(19)
+    B, C, Hq, hd = 1, 2, 2, 3
+    d = Hq * hd
+    o = rng.standard_normal((B, C, Hq, hd))
+    Wo = rng.standard_normal((d, d))
+    h0 = np.zeros((B, C, d))
+    h1 = out_proj(o, Wo, h0, "f64")
+    flat = o.reshape(B * C, d)
+    assert np.allclose(h1.reshape(B * C, d), np.einsum("rj,cj->rc", flat, Wo), atol=1e-13)
+    assert not np.allclose(h1.reshape(B * C, d), flat @ Wo, atol=1e-3)
