@@ -8,9 +8,14 @@ and Step select, for every canvas of the batch. Inputs are seeded synthetic
 tensors already resident in HBM; t cycles through the 12-step cosine grid,
 one Philox seed per step.
 
-Prints one JSON line. `roofline` reports the dominant kernel (the fused LM
-head) from HIP events recorded around its launches in the timed region;
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+Prints one JSON line. `value` is the standard canvas (or --workload).
+`roofline` reports the dominant kernel (the fused LM head) from HIP events
+recorded around its launches in the timed region; `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload. `workloads` repeats the
+throughput measurement for the other workloads (tiny fp32, long prefix,
+large vocabulary, batched) on seeded inputs drawn on the GPU, each with its
+per-stage algorithmic rates, its LM head's fraction of the MFMA peak and its
+own CPU-oracle sample.
 """
 import argparse
 import hashlib
@@ -25,7 +30,9 @@ sys.path.insert(0, ROOT)
 METRIC = "canvas denoise steps/s & canvas tokens/s (C=256, 1 GPU); % MFMA/HBM peak"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 vector
 WORKLOADS = {
+    "c1": "tiny fp32: B=1 C=16 P=8 d=32 2 heads x 16 (MHA) V=64 fp32, linear 8 steps",
     "c2": "standard canvas: B=1 C=256 P=512 d=2048 16q/8kv heads x 128 V=32768 bf16, cosine 12 steps",
     "c3": "long prefix: B=1 C=256 P=32768 d=2048 16q/8kv heads x 128 V=32768 bf16, cosine 12 steps",
     "c4": "large vocabulary: B=1 C=256 P=2048 d=2816 16q/8kv heads x 176 V=262144 bf16, cosine 12 steps",
@@ -60,27 +67,57 @@ def _traffic(workload):
     return (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"]) * 1024.0
 
 
-def cpu_baseline(cfg, inp, budget_s):
+def cpu_threads():
+    """Threads the oracle's BLAS may use: the process's CPU affinity, capped by
+    OMP_NUM_THREADS when set (the share of the host this job is given)."""
+    aff = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    n = min(aff, int(omp)) if omp.isdigit() and int(omp) > 0 else aff
+    return n, aff, os.cpu_count()
+
+
+def cpu_baseline(cfg, inp, budget_s, canvases=None):
+    """The CPU oracle timed on the host cores over a bounded sample of the
+    workload: whole denoising steps, or with `canvases` = k one canvas at a
+    time, cycling over canvases 0..k-1 of the batch (each with its own Philox
+    counters; the K_pre/V_pre arrays may then hold just those k canvases), the
+    rate then scaled to the whole batch of cfg.B canvases."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import denoise_step
+    n_threads, aff, ncpu = cpu_threads()
     w = {k: inp[k] for k in ["E", "Wq", "Wk", "Wv", "Wo"]}
     t = np.full(cfg.B, 0.5, np.float32) if not cfg.per_canvas_t else inp["t"]
     dt = float(np.float32(1.0 / cfg.steps))
     runs, t0 = 0, time.perf_counter()
-    while True:
-        denoise_step(cfg, w, inp["x"], inp["z"], inp["K_pre"], inp["V_pre"], t, dt, seed=runs)
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    sps = runs / el
+    with threadpool_limits(limits=n_threads, user_api="blas"):
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+        while True:
+            if canvases:
+                b = runs % canvases
+                sl = slice(b, b + 1)
+                denoise_step(cfg, w, inp["x"][sl], inp["z"][sl], inp["K_pre"][sl], inp["V_pre"][sl],
+                             t[sl], dt, seed=runs, canvas_ids=[b])
+            else:
+                denoise_step(cfg, w, inp["x"], inp["z"], inp["K_pre"], inp["V_pre"], t, dt, seed=runs)
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    if canvases:
+        sps = runs / el / cfg.B
+        what = (f"{runs} single-canvas oracle steps (cycling over canvases 0..{canvases - 1} of {cfg.B}, "
+                f"each with its own prefix cache, z and t) in {el:.1f} s, scaled to the "
+                f"{cfg.B}-canvas batch")
+    else:
+        sps = runs / el
+        what = f"{runs} full oracle denoise step(s) of the same workload in {el:.1f} s"
     return {"value": sps, "unit": "denoise steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{runs} full oracle denoise step(s) of the same workload at t=0.5 "
-                      f"({el:.1f} s wall, float64 BLAS on {threads} threads)",
-            "canvas_tokens_per_s": sps * cfg.B * cfg.C}
+            "sample": what + f" (float64 BLAS on {threads} threads)",
+            "canvas_tokens_per_s": sps * cfg.B * cfg.C,
+            "host_cpu_count": ncpu, "affinity_cpus": aff}
 
 
 def corrupt_bandwidth(reps=20):
@@ -106,14 +143,141 @@ def corrupt_bandwidth(reps=20):
             "bytes_per_token": 8}
 
 
+def stage_rates(cfg, stages):
+    """Average time per launch of each profiled stage, and for the contraction
+    stages their algorithmic TFLOP/s and fraction of the bf16 MFMA peak (a
+    stage's time includes its own merge kernel; event pairs add queue time)."""
+    fl = cfg.flops_per_step()
+    kernels = {k: {"avg_ms": (v[0] / v[1]) if v[1] else None, "launches": v[1]}
+               for k, v in stages.items() if v[1]}
+    # bf16 stages run on MFMA; the fp32 path is plain VALU (fp32 vector peak)
+    peak, key = ((PEAK_BF16_TFLOPS, "frac_mfma_bf16") if cfg.dtype == "bf16"
+                 else (PEAK_FP32_TFLOPS, "frac_fp32_vector"))
+    for k, f in (("qkv", fl["qkv"]), ("attention", fl["attn"]), ("oproj", fl["oproj"]), ("lmhead", fl["lm"])):
+        if k in kernels and kernels[k]["avg_ms"]:
+            tf = f / (kernels[k]["avg_ms"] * 1e-3) / 1e12
+            kernels[k].update({"algorithmic_flop": f, "tflops": tf, key: tf / peak})
+    # the attention's K/V stream (prefix cache plus canvas keys, K and V)
+    # against the HBM peak; the stage is MFMA-bound, so this is context
+    if "attention" in kernels and kernels["attention"]["avg_ms"]:
+        es = 2 if cfg.dtype == "bf16" else 4
+        kv = 2.0 * es * cfg.B * cfg.n_kv_heads * (cfg.P + cfg.C) * cfg.head_dim
+        gbs = kv / (kernels["attention"]["avg_ms"] * 1e-3) / 1e9
+        kernels["attention"].update({"kv_bytes": kv, "kv_GB_s": gbs, "kv_frac_hbm": gbs / PEAK_HBM_GBS})
+    return kernels
+
+
+def time_steps(dg, torch, model, cfg, x, z, Kp, Vp, tvec, steps, warmup, seed0=1000):
+    """K timed steps (nothing else on the stream), then the same K steps with
+    HIP events around every LM-head launch, then a short pass with every stage
+    bracketed. Returns (ms_per_step, LM-head ms per launch, stage profile)."""
+    import numpy as np
+    xs = [x, torch.empty_like(x)]
+    zs = [z, torch.empty_like(z)]
+    dt = float(np.float32(1.0 / cfg.steps))
+
+    def step(k):
+        a, b = k & 1, (k & 1) ^ 1
+        dg.dg_denoise_step(model, xs[a], zs[a], Kp, Vp, tvec(k), dt, seed0 + k, xs[b], zs[b])
+
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    dg.dg_profile_read(model)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for k in range(steps):
+        step(warmup + k)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    dg.dg_profile_enable(model, ["lmhead"])
+    for k in range(steps):
+        step(warmup + steps + k)
+    torch.cuda.synchronize()
+    dg.dg_profile_enable(model, [])
+    lm_ms, lm_n = dg.dg_profile_read(model)["lmhead"]
+    dg.dg_profile_enable(model, None)
+    for k in range(min(steps, 10)):
+        step(k)
+    torch.cuda.synchronize()
+    dg.dg_profile_enable(model, [])
+    stages = dg.dg_profile_read(model)
+    return ms, lm_ms / max(1, lm_n), stages
+
+
+def workload_leg(name, steps, warmup, cpu_budget, with_cpu):
+    """Throughput of one more workload on device-drawn inputs of its shape:
+    ms per step, steps/s, canvas tokens/s, per-stage algorithmic rates, the LM
+    head's fraction of the MFMA peak, and the CPU oracle on a bounded sample."""
+    import numpy as np
+    import torch
+
+    import discrete_diffusion_decoding_dg_amd as dg
+    from tests.dg_harness import config_args
+    from workloads import get_config
+    from workloads.device_inputs import make_device_inputs, to_host_f32
+
+    cfg = get_config(name)
+    t_setup = time.perf_counter()
+    d = make_device_inputs(cfg, seed=7)
+    model = dg.dg_create(config_args(cfg), d["E"], d["Wq"], d["Wk"], d["Wv"], d["Wo"])
+    grid = [np.float32(1.0 - k / cfg.steps) for k in range(cfg.steps)]
+
+    def tvec(k):
+        return d["t"] if cfg.per_canvas_t else np.full(cfg.B, grid[k % cfg.steps], np.float32)
+
+    ms, lm_ms, stages = time_steps(dg, torch, model, cfg, d["x"].clone(), d["z"].clone(), d["K_pre"],
+                                   d["V_pre"], tvec, steps, warmup)
+    model.close()
+    fl = cfg.flops_per_step()
+    sps = 1000.0 / ms
+    lm_tf = fl["lm"] / (lm_ms * 1e-3) / 1e12
+    peak, key = ((PEAK_BF16_TFLOPS, "frac_mfma_bf16") if cfg.dtype == "bf16"
+                 else (PEAK_FP32_TFLOPS, "frac_fp32_vector"))
+    res = {"workload": WORKLOADS[name], "steps": steps, "warmup": warmup, "dtype": cfg.dtype,
+           "ms_per_step": ms, "steps_per_s": sps, "canvas_tokens_per_s": sps * cfg.B * cfg.C,
+           "step_tflops": fl["total"] / (ms * 1e-3) / 1e12,
+           "step_" + key: fl["total"] / (ms * 1e-3) / 1e12 / peak,
+           "lmhead": {"avg_ms": lm_ms, "algorithmic_flop_per_launch": fl["lm"], "tflops": lm_tf,
+                      key: lm_tf / peak},
+           "kernels": stage_rates(cfg, stages),
+           "inputs": "seeded synthetic tensors of the workload's shapes and distributions, drawn on the GPU"}
+    if with_cpu:
+        # the oracle reads the same tensors, copied to the host
+        host = {k: to_host_f32(d[k]) for k in ["E", "Wq", "Wk", "Wv", "Wo", "x", "z"]}
+        host["t"] = d["t"]
+        # a batch is sampled one canvas at a time: only the first nb canvases'
+        # caches travel
+        nb = min(cfg.B, 4) if cfg.B > 1 else None
+        host["K_pre"] = to_host_f32(d["K_pre"][:nb] if nb else d["K_pre"])
+        host["V_pre"] = to_host_f32(d["V_pre"][:nb] if nb else d["V_pre"])
+        del d
+        torch.cuda.empty_cache()
+        res["cpu_baseline"] = cpu_baseline(cfg, host, cpu_budget, canvases=nb)
+        del host
+    else:
+        del d
+        torch.cuda.empty_cache()
+    res["leg_wall_s"] = time.perf_counter() - t_setup
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle time per workload")
+    ap.add_argument("--workloads", default="c1,c3,c4,c5",
+                    help="comma-separated workloads timed after the main one (device-drawn inputs), "
+                         "each with its own CPU-oracle sample; empty for none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--device-inputs", action="store_true",
+                    help="draw the main workload's inputs on the GPU (seeded, same shapes and "
+                         "distributions; for profiling runs: no CPU baseline)")
     ap.add_argument("--no-corrupt", action="store_true")
     ap.add_argument("--no-ffw", action="store_true", help="skip the feed-forward block timings")
     ap.add_argument("--no-blocks", action="store_true", help="skip the block-autoregressive timings")
@@ -136,8 +300,12 @@ def main():
     from tests.dg_harness import config_args, to_dev
 
     cfg = get_config(args.workload)
-    inp = make_inputs(cfg)
     torch.cuda.set_device(0)
+    if args.device_inputs:
+        from workloads.device_inputs import make_device_inputs
+        inp = make_device_inputs(cfg, seed=7)
+    else:
+        inp = make_inputs(cfg)
     if args.copy_mib:
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -145,10 +313,14 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    wdev = {n: to_dev(inp, n, cfg) for n in ["E", "Wq", "Wk", "Wv", "Wo"]}
+    if args.device_inputs:
+        wdev = {n: inp[n] for n in ["E", "Wq", "Wk", "Wv", "Wo"]}
+        Kp, Vp, z, x = inp["K_pre"], inp["V_pre"], inp["z"], inp["x"]
+    else:
+        wdev = {n: to_dev(inp, n, cfg) for n in ["E", "Wq", "Wk", "Wv", "Wo"]}
+        Kp, Vp, z = (to_dev(inp, n, cfg) for n in ["K_pre", "V_pre", "z"])
+        x = torch.from_numpy(inp["x"]).cuda()
     model = dg.dg_create(config_args(cfg), wdev["E"], wdev["Wq"], wdev["Wk"], wdev["Wv"], wdev["Wo"])
-    Kp, Vp, z = (to_dev(inp, n, cfg) for n in ["K_pre", "V_pre", "z"])
-    x = torch.from_numpy(inp["x"]).cuda()
     xs = [x, torch.empty_like(x)]
     zs = [z, torch.empty_like(z)]
     dt = float(np.float32(1.0 / cfg.steps))
@@ -407,20 +579,7 @@ def main():
     lm_avg_ms = lm_ms / max(1, lm_n)
     achieved = fl["lm"] / (lm_avg_ms * 1e-3) / 1e12
     traffic = _traffic(args.workload)
-    kernels = {k: {"avg_ms": (v[0] / v[1]) if v[1] else None, "launches": v[1]}
-               for k, v in stages.items() if v[1]}
-    # algorithmic rate of the contraction stages (stage time includes each
-    # stage's own merge kernel, and event pairs add queue time)
-    for k, f in (("qkv", fl["qkv"]), ("attention", fl["attn"]), ("oproj", fl["oproj"]), ("lmhead", fl["lm"])):
-        if k in kernels and kernels[k]["avg_ms"]:
-            tf = f / (kernels[k]["avg_ms"] * 1e-3) / 1e12
-            kernels[k].update({"algorithmic_flop": f, "tflops": tf, "frac_mfma_bf16": tf / PEAK_BF16_TFLOPS})
-    # the attention's K/V stream (prefix cache plus canvas keys, K and V, bf16)
-    # against the HBM peak; the stage is MFMA-bound, so this is context
-    if "attention" in kernels and kernels["attention"]["avg_ms"]:
-        kv = 2.0 * 2 * cfg.B * cfg.n_kv_heads * (cfg.P + cfg.C) * cfg.head_dim
-        gbs = kv / (kernels["attention"]["avg_ms"] * 1e-3) / 1e9
-        kernels["attention"].update({"kv_bytes": kv, "kv_GB_s": gbs, "kv_frac_hbm": gbs / PEAK_HBM_GBS})
+    kernels = stage_rates(cfg, stages)
     steps_per_s = 1000.0 / ms_per_step
     result = {
         "metric": METRIC,
@@ -461,8 +620,24 @@ def main():
     if not args.no_corrupt:
         result["corrupt"] = corrupt_bandwidth()
     model.close()
-    if not args.no_cpu_baseline:
+    del wdev, Kp, Vp, z, x, xs, zs
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline and not args.device_inputs:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
+    del inp
+    # the other workloads, one after another (each frees its tensors)
+    legs = [w for w in args.workloads.split(",") if w and w != args.workload]
+    if legs:
+        wl = {args.workload: {
+            "workload": WORKLOADS[args.workload], "ms_per_step": ms_per_step,
+            "steps_per_s": steps_per_s, "canvas_tokens_per_s": steps_per_s * cfg.B * cfg.C,
+            "lmhead": {"avg_ms": lm_avg_ms, "frac_mfma_bf16": achieved / PEAK_BF16_TFLOPS},
+            "note": "the main measurement (value, roofline, cpu_baseline above)"}}
+        for w in legs:
+            print(f"[bench] workload {w}", file=sys.stderr, flush=True)
+            wl[w] = workload_leg(w, args.steps, args.warmup, args.cpu_budget,
+                                 not args.no_cpu_baseline)
+        result["workloads"] = wl
     print(json.dumps(result), flush=True)
 
 
