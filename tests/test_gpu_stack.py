@@ -97,7 +97,10 @@ def test_stack_step_matches_oracle(name):
     for n in ["q", "k", "v", "o"]:
         assert_close(f"last layer {n}", to_host(taps[n]), last[n], rt)
     hf = to_host(taps["h1"])
-    assert_close("final norm", hf, o["h_final"], rt)
+    # entries above rms: the plain relative bound per residual sub-block, two
+    # per layer (attention and MLP, each re-rounding the stream like the
+    # single block), applied to the final norm that sees both
+    assert_close("final norm", hf, o["h_final"], rt, plain_rtol=2 * rt)
     # the head after the stack, from the GPU's own final activation (the
     # softmax amplifies the stack's drift in z; the head itself is checked at
     # the single block's tolerances)
@@ -262,7 +265,8 @@ def test_moe_stack_step_matches_oracle(name):
     assert keep.mean() > 0.9
     rt = (RTOL_F32 if cfg.dtype == "f32" else RTOL_BF16) * cfg.n_layers
     hf = to_host(h1).reshape(cfg.R, cfg.d)
-    assert_close("final norm", hf[keep], o["h_final"].reshape(cfg.R, cfg.d)[keep], rt)
+    assert_close("final norm", hf[keep], o["h_final"].reshape(cfg.R, cfg.d)[keep], rt,
+                 plain_rtol=2 * rt)
     head = lm_head(hf.reshape(B, C, cfg.d).astype(np.float64), inp["E"], o["inv_tau"], cfg.dtype)
     smp = step_select(inp["x"], head["s"], o["lam"], 17, np.arange(cfg.B))
     r1 = RTOL_F32 if cfg.dtype == "f32" else RTOL_BF16
