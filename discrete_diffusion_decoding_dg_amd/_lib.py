@@ -48,7 +48,7 @@ class dg_profile(ctypes.Structure):
 
 
 EXPORTS = ["dg_create", "dg_destroy", "dg_workspace_bytes", "dg_corrupt", "dg_corrupt_batch",
-           "dg_denoise_step", "dg_denoise_step_taps", "dg_generate_canvas",
+           "dg_denoise_step", "dg_denoise_step_taps", "dg_denoise_step_static", "dg_generate_canvas",
            "dg_denoise_step_entropy", "dg_generate_canvas_entropy", "dg_set_ffw", "dg_ffw",
            "dg_encode_kv", "dg_generate_blocks", "dg_generate_blocks_entropy", "dg_set_stack",
            "dg_set_stack_moe",
@@ -82,6 +82,8 @@ def load_library():
     lib.dg_denoise_step.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(f32), f32, u64, vp, vp, vp, vp, vp]
     lib.dg_denoise_step_taps.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(f32), f32, u64, vp, vp,
                                          ctypes.POINTER(dg_taps), vp]
+    lib.dg_denoise_step_static.argtypes = [ctypes.POINTER(dg_config), ctypes.POINTER(dg_weights), vp, vp,
+                                           vp, vp, ctypes.POINTER(f32), f32, u64, vp, vp, vp, vp, vp]
     lib.dg_generate_canvas.argtypes = [vp, vp, vp, i32, u64, vp, vp, vp]
     lib.dg_denoise_step_entropy.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(f32), u64, f32, f32,
                                             vp, vp, vp, vp, vp, vp, vp]
@@ -213,6 +215,16 @@ def dg_denoise_step_taps(model, x_t, z_t, K_pre, V_pre, t, dt, seed, x_out, z_ou
                                                _ptr(x_out), _ptr(z_out),
                                                ctypes.byref(tp) if tp is not None else None,
                                                _stream(stream)))
+
+
+def dg_denoise_step_static(cfg, E, Wq, Wk, Wv, Wo, x_t, z_t, K_pre, V_pre, t, dt, seed, x_out, z_out,
+                           lse_out=None, p0_out=None, stream=None):
+    """dg_denoise_step without a model and without allocation (static scratch)."""
+    w = dg_weights(*[t_.data_ptr() if t_ is not None else None for t_ in (E, Wq, Wk, Wv, Wo)])
+    _check(load_library().dg_denoise_step_static(ctypes.byref(cfg), ctypes.byref(w), _ptr(x_t), _ptr(z_t),
+                                                 _ptr(K_pre), _ptr(V_pre), _floats(t), float(dt),
+                                                 int(seed), _ptr(x_out), _ptr(z_out), _ptr(lse_out),
+                                                 _ptr(p0_out), _stream(stream)))
 
 
 def dg_generate_canvas(model, K_pre, V_pre, steps, seed, x_out, z_out=None, stream=None):

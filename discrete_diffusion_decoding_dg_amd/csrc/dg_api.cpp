@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -638,6 +639,92 @@ dg_status encode_kv(dg_model *m, const int32_t *tokens, int n, int ld, int pos, 
   return DG_OK;
 }
 
+// Argument checks of one denoising step of model m (after the model check).
+dg_status check_step_args(const dg_model *m, const int32_t *x_t, const void *z_t, const void *K_pre,
+                          const void *V_pre, const float *t, float dt, const int32_t *x_out,
+                          const void *z_out, const dg_taps *taps) {
+  const dg::Shape &s = m->s;
+  if (!x_t || !z_t || !x_out || !z_out) return fail(DG_ERR_INVALID_ARG, "x_t, z_t, x_out and z_out must be non-NULL");
+  if (s.P > 0 && (!K_pre || !V_pre)) return fail(DG_ERR_INVALID_ARG, "K_pre and V_pre must be non-NULL when P > 0");
+  if (dg_status e = check_times(t, s.B, dt)) return e;
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  const size_t es = bf16 ? 2 : 4;
+  const size_t nx = static_cast<size_t>(s.R()) * sizeof(int32_t);
+  const size_t nz = static_cast<size_t>(s.R()) * s.d * es;
+  if (overlap(x_out, nx, x_t, nx)) return fail(DG_ERR_INVALID_ARG, "x_out overlaps x_t");
+  if (overlap(z_out, nz, z_t, nz)) return fail(DG_ERR_INVALID_ARG, "z_out overlaps z_t");
+  if (bf16 && (!aligned16(z_t) || !aligned16(z_out) || (K_pre && !aligned16(K_pre)) ||
+               (V_pre && !aligned16(V_pre))))
+    return fail(DG_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+  if (taps && taps->p0 && !taps->lse)
+    return fail(DG_ERR_INVALID_ARG, "taps->p0 requires taps->lse");
+  if (taps && bf16) {
+    const void *tp[7] = {taps->h0, taps->q, taps->k, taps->v, taps->o, taps->h1, taps->p0E};
+    for (const void *p : tp)
+      if (p && !aligned16(p)) return fail(DG_ERR_INVALID_ARG, "bf16 taps must be 16-byte aligned");
+  }
+  return DG_OK;
+}
+
+// The launches of one checked step: step constants (host storage prm_host of
+// B entries, supplied by the caller), then the kernels.
+dg_status launch_step(dg_model *m, const int32_t *x_t, const void *z_t, const void *K_pre,
+                      const void *V_pre, const float *t, float dt, uint64_t seed, int32_t *x_out,
+                      void *z_out, const dg_taps *taps, void *stream, dg::StepParams *prm_host) {
+  const dg::Shape &s = m->s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int b = 0; b < s.B; ++b) prm_host[b] = step_params(t[b], dt, m->cfg.schedule);
+  // a few canvases: the constants ride along with the embedding launch
+  const int n_inline = s.B <= dg::kInlineParams ? s.B : 0;
+  if (!n_inline)
+    DG_HIP(dg::launch_set_params(m->prm, prm_host, s.B, st), "parameter upload");
+  return run_step(m, x_t, z_t, K_pre, V_pre, m->prm, prm_host, n_inline, seed, x_out, z_out,
+                  taps, taps ? taps->lse : nullptr, taps ? taps->p0 : nullptr, st);
+}
+
+// ---- the step without allocation (dg_denoise_step_static) ----
+// Its whole workspace lives in one file-scope device array per GPU. In host
+// code `scratch` names a host-side stand-in; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+constexpr int kStaticMaxB = 256;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Workspace of one step in carve order: activations, attention and LM-head
+// split partials, the LM head's tile-major copy of E, step constants.
+struct StaticLayout {
+  size_t h0, q, k, v, o, h1, attn, lm, etm, prm, total;
+};
+
+StaticLayout static_layout_of(const dg_config &c) {
+  const Layout L = layout_of(c);
+  StaticLayout S;
+  S.h0 = L.h0; S.q = L.q; S.k = L.k; S.v = L.v; S.o = L.o; S.h1 = L.h1;
+  S.attn = L.attn; S.lm = L.lm; S.etm = L.etm;
+  S.prm = align_up(static_cast<size_t>(c.B) * sizeof(dg::StepParams));
+  S.total = S.h0 + S.q + S.k + S.v + S.o + S.h1 + S.attn + S.lm + S.etm + S.prm;
+  return S;
+}
+
+// Device address of this device's scratch array (looked up on the device's
+// first call).
+dg_status scratch_address(int dev, char **out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(DG_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(DG_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char *>(g_scratch_ptr[dev]);
+  return DG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -815,35 +902,9 @@ dg_status dg_denoise_step_taps(dg_model *m, const int32_t *x_t, const void *z_t,
                                void *stream) {
   g_err.clear();
   if (dg_status s = check_model(m)) return s;
-  const dg::Shape &s = m->s;
-  if (!x_t || !z_t || !x_out || !z_out) return fail(DG_ERR_INVALID_ARG, "x_t, z_t, x_out and z_out must be non-NULL");
-  if (s.P > 0 && (!K_pre || !V_pre)) return fail(DG_ERR_INVALID_ARG, "K_pre and V_pre must be non-NULL when P > 0");
-  if (dg_status e = check_times(t, s.B, dt)) return e;
-  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
-  const size_t es = bf16 ? 2 : 4;
-  const size_t nx = static_cast<size_t>(s.R()) * sizeof(int32_t);
-  const size_t nz = static_cast<size_t>(s.R()) * s.d * es;
-  if (overlap(x_out, nx, x_t, nx)) return fail(DG_ERR_INVALID_ARG, "x_out overlaps x_t");
-  if (overlap(z_out, nz, z_t, nz)) return fail(DG_ERR_INVALID_ARG, "z_out overlaps z_t");
-  if (bf16 && (!aligned16(z_t) || !aligned16(z_out) || (K_pre && !aligned16(K_pre)) ||
-               (V_pre && !aligned16(V_pre))))
-    return fail(DG_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
-  if (taps && taps->p0 && !taps->lse)
-    return fail(DG_ERR_INVALID_ARG, "taps->p0 requires taps->lse");
-  if (taps && bf16) {
-    const void *tp[7] = {taps->h0, taps->q, taps->k, taps->v, taps->o, taps->h1, taps->p0E};
-    for (const void *p : tp)
-      if (p && !aligned16(p)) return fail(DG_ERR_INVALID_ARG, "bf16 taps must be 16-byte aligned");
-  }
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  std::vector<dg::StepParams> prm(s.B);
-  for (int b = 0; b < s.B; ++b) prm[b] = step_params(t[b], dt, m->cfg.schedule);
-  // a few canvases: the constants ride along with the embedding launch
-  const int n_inline = s.B <= dg::kInlineParams ? s.B : 0;
-  if (!n_inline)
-    if (dg_status e = upload_params(m, m->prm, prm, st)) return e;
-  return run_step(m, x_t, z_t, K_pre, V_pre, m->prm, prm.data(), n_inline, seed, x_out, z_out,
-                  taps, taps ? taps->lse : nullptr, taps ? taps->p0 : nullptr, st);
+  if (dg_status e = check_step_args(m, x_t, z_t, K_pre, V_pre, t, dt, x_out, z_out, taps)) return e;
+  std::vector<dg::StepParams> prm(m->s.B);
+  return launch_step(m, x_t, z_t, K_pre, V_pre, t, dt, seed, x_out, z_out, taps, stream, prm.data());
 }
 
 dg_status dg_set_ffw(dg_model *m, int32_t hidden, const void *W_gate, const void *W_up,
@@ -1046,6 +1107,61 @@ dg_status dg_denoise_step(dg_model *m, const int32_t *x_t, const void *z_t, cons
   taps.lse = lse_out;
   taps.p0 = p0_out;
   return dg_denoise_step_taps(m, x_t, z_t, K_pre, V_pre, t, dt, seed, x_out, z_out, &taps, stream);
+}
+
+dg_status dg_denoise_step_static(const dg_config *cfg, const dg_weights *w, const int32_t *x_t,
+                                 const void *z_t, const void *K_pre, const void *V_pre,
+                                 const float *t, float dt, uint64_t seed, int32_t *x_out,
+                                 void *z_out, float *lse_out, float *p0_out, void *stream) {
+  g_err.clear();
+  if (dg_status s = check_config(cfg)) return s;
+  if (!w) return fail(DG_ERR_INVALID_ARG, "weights is NULL");
+  if (!w->E || !w->Wq || !w->Wk || !w->Wv || !w->Wo)
+    return fail(DG_ERR_INVALID_ARG, "a weight pointer is NULL");
+  if (!aligned16(w->E) || !aligned16(w->Wq) || !aligned16(w->Wk) || !aligned16(w->Wv) ||
+      !aligned16(w->Wo))
+    return fail(DG_ERR_INVALID_ARG, "weight pointers must be 16-byte aligned");
+  if (p0_out && !lse_out) return fail(DG_ERR_INVALID_ARG, "p0_out requires lse_out");
+  if (cfg->B > kStaticMaxB)
+    return fail(DG_ERR_UNSUPPORTED, "dg_denoise_step_static supports B <= %d (got %d)", kStaticMaxB, cfg->B);
+  const StaticLayout S = static_layout_of(*cfg);
+  if (S.total > kStaticScratchBytes)
+    return fail(DG_ERR_UNSUPPORTED,
+                "the step needs %zu bytes of workspace; dg_denoise_step_static has %zu bytes of static "
+                "scratch per device (use dg_create and dg_denoise_step)", S.total, kStaticScratchBytes);
+  int dev = 0;
+  DG_HIP(hipGetDevice(&dev), "hipGetDevice");
+  char *p = nullptr;
+  if (dg_status e = scratch_address(dev, &p)) return e;
+  // a model on the stack that owns nothing: every buffer is carved from the
+  // scratch array; generation, entropy and block buffers stay NULL
+  dg_model m{};
+  m.cfg = *cfg;
+  m.w = *w;
+  m.s = shape_of(*cfg);
+  m.device = dev;
+  m.h0 = p; p += S.h0;
+  m.q = p; p += S.q;
+  m.k = p; p += S.k;
+  m.v = p; p += S.v;
+  m.o = p; p += S.o;
+  m.h1 = p; p += S.h1;
+  m.attn = p; p += S.attn;
+  m.lm = p; p += S.lm;
+  m.etm = p; p += S.etm;
+  m.prm = reinterpret_cast<dg::StepParams *>(p);
+  dg_taps taps;
+  std::memset(&taps, 0, sizeof(taps));
+  taps.lse = lse_out;
+  taps.p0 = p0_out;
+  if (dg_status e = check_step_args(&m, x_t, z_t, K_pre, V_pre, t, dt, x_out, z_out, &taps)) return e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (cfg->dtype == DG_DTYPE_BF16)
+    DG_HIP(dg::launch_lmhead_relayout(static_cast<const uint16_t *>(w->E), m.s,
+                                      static_cast<uint16_t *>(m.etm), st),
+           "copy of E for the LM head");
+  dg::StepParams prm_host[kStaticMaxB];
+  return launch_step(&m, x_t, z_t, K_pre, V_pre, t, dt, seed, x_out, z_out, &taps, stream, prm_host);
 }
 
 dg_status dg_generate_canvas(dg_model *m, const void *K_pre, const void *V_pre, int32_t steps,

@@ -161,6 +161,29 @@ dg_status dg_denoise_step_taps(dg_model *m, const int32_t *x_t, const void *z_t,
                                uint64_t seed, int32_t *x_out, void *z_out, const dg_taps *taps,
                                void *stream);
 
+/* dg_denoise_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no model object and no allocation of any kind in the call. The step's
+ * whole workspace (activations, attention and LM-head split partials, the LM
+ * head's tile-major copy of E, step constants) is carved from a static
+ * device array of 64 MiB that each GPU the library runs on holds until the
+ * process ends.
+ *   cfg, w: as dg_create (checked the same way); every other argument as
+ *   dg_denoise_step. The copy of E is remade on every call (V*d*2 bytes
+ *   read and written on `stream`), so E may change between calls.
+ *   Limits (DG_ERR_UNSUPPORTED, nothing launched): B <= 256 and a workspace
+ *   of at most 64 MiB (dg_workspace_bytes bounds it from above; roughly
+ *   V*d*2 bytes for the copy of E plus the activations, e.g. V*d <= 2^24
+ *   at small B*C).
+ *   Calls on one GPU share its array and it keeps the last call's contents
+ *   (every byte a step reads is written earlier in the same call): calls
+ *   that overlap in time on one GPU, on any streams, race and must be
+ *   serialised by the caller. */
+dg_status dg_denoise_step_static(const dg_config *cfg, const dg_weights *w, const int32_t *x_t,
+                                 const void *z_t, const void *K_pre, const void *V_pre,
+                                 const float *t, float dt, uint64_t seed, int32_t *x_out,
+                                 void *z_out, float *lse_out, float *p0_out, void *stream);
+
 /* Generate B canvases from noise (TR summary, Method, three-line update
  * iterated from t = 1; Experiments: about 12 and at most 48 steps).
  *   x_init = corruption of any canvas at kappa = 0 with `seed` (uniform),

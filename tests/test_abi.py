@@ -116,3 +116,27 @@ def test_single_hip_runtime_in_process():
     maps = open("/proc/self/maps").read()
     paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(paths) == 1, paths
+
+
+def test_static_step_rejects_on_the_host():
+    """dg_denoise_step_static checks its config, weights and the static scratch
+    limit before any HIP call (no device is touched here)."""
+    lib = _lib.load_library()
+    t = (ctypes.c_float * 256)(*([0.5] * 256))
+    w = _lib.dg_weights(16, 16, 16, 16, 16)
+
+    def call(cfg, w=w, lse=None, p0=None):
+        return lib.dg_denoise_step_static(ctypes.byref(cfg), ctypes.byref(w), 32, 64, 64, 64, t,
+                                          ctypes.c_float(0.1), 0, 96, 128, lse, p0, None)
+    # the standard canvas needs more workspace than the static scratch holds
+    assert call(_cfg()) == _lib.DG_ERR_UNSUPPORTED
+    assert "static" in dg.dg_last_error()
+    assert call(_cfg(B=257, C=16, P=8, d=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                     V=1024)) == _lib.DG_ERR_UNSUPPORTED
+    assert "B <= 256" in dg.dg_last_error()
+    assert call(_cfg(B=0)) == _lib.DG_ERR_INVALID_ARG
+    assert call(_cfg(), w=_lib.dg_weights(None, 16, 16, 16, 16)) == _lib.DG_ERR_INVALID_ARG
+    assert call(_cfg(), w=_lib.dg_weights(18, 16, 16, 16, 16)) == _lib.DG_ERR_INVALID_ARG
+    assert call(_cfg(), p0=256) == _lib.DG_ERR_INVALID_ARG
+    assert lib.dg_denoise_step_static(None, ctypes.byref(w), 32, 64, 64, 64, t, ctypes.c_float(0.1), 0,
+                                      96, 128, None, None, None) == _lib.DG_ERR_INVALID_ARG
