@@ -241,6 +241,9 @@ def workload_leg(name, steps, warmup, cpu_budget, with_cpu):
            "step_" + key: fl["total"] / (ms * 1e-3) / 1e12 / peak,
            "lmhead": {"avg_ms": lm_ms, "algorithmic_flop_per_launch": fl["lm"], "tflops": lm_tf,
                       key: lm_tf / peak},
+           "roofline": {"bound": "mfma" if cfg.dtype == "bf16" else "alu", "kernel": "lmhead_kernel",
+                        "achieved": lm_tf, "peak": peak, "unit": "TFLOP/s", "frac": lm_tf / peak,
+                        "traffic": _traffic(name) if cfg.dtype == "bf16" else None},
            "kernels": stage_rates(cfg, stages),
            "inputs": "seeded synthetic tensors of the workload's shapes and distributions, drawn on the GPU"}
     if with_cpu:
