@@ -25,6 +25,17 @@ family's pre-norm layout. Readings:
 Rounding points (act dtype): h0, each normalised activation, q, k, v, o, each
 residual sum, the MLP hidden activations, the final normalised activation;
 sums in float64.
+
+Causal encoder pass of the stack (encode_kv_stack): the pipeline figure's
+first and third stages run the clean tokens through the causal encoder, which
+fills and extends the KV cache; the encoder shares the decoder's weights
+(weight-shared encoder-decoder). Readings: the encoder is the same pre-norm
+stack run on h = E[x] (no self-conditioning input) with a causal mask: a new
+token at cache row p attends to every cache row below p (the history and the
+earlier new tokens) and to itself; layer l's cache entries are that layer's
+key and value projections k = a Wk_l^T, v = a Wv_l^T of a = rmsnorm(h) g_attn_l.
+The last layer's attention output and every MLP after it feed no cache entry
+and are not computed.
 """
 import numpy as np
 
@@ -125,3 +136,67 @@ def stack_step(cfg, w, sw, x_t, z_t, K_pre, V_pre, t, dt, seed, canvas_ids=None)
     out["p0E"] = head["z"]
     out["z_out"] = self_condition(w, head["z"], act)
     return out
+
+
+def causal_attention(q, k, v, K_hist, V_hist, act):
+    """o [B, n, Hq, hd]: new token i attends to the history rows and to new
+    tokens 0..i (one joint softmax, scale 1/sqrt(hd), head h reads kv head
+    h // G). k, v [B, Hkv, n, hd]; K_hist, V_hist [B, Hkv, pos, hd]."""
+    B, n, Hq, hd = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    pos = K_hist.shape[2]
+    o = np.empty((B, n, Hq, hd), dtype=np.float64)
+    scale = 1.0 / np.sqrt(hd)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            keys = np.concatenate([np.asarray(K_hist[b, g], np.float64), k[b, g]], axis=0)
+            vals = np.concatenate([np.asarray(V_hist[b, g], np.float64), v[b, g]], axis=0)
+            s = (q[b, :, h, :] @ keys.T) * scale                 # [n, pos + n]
+            visible = np.arange(pos + n)[None, :] <= pos + np.arange(n)[:, None]
+            s = np.where(visible, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            a = np.exp(s)
+            a /= a.sum(axis=1, keepdims=True)
+            o[b, :, h, :] = a @ vals
+    return round_act(o, act)
+
+
+def encode_kv_stack(cfg, E, sw, tokens, K_cache, V_cache, pos):
+    """Causal encoder pass of the stack over `tokens` [B, n] written at cache
+    rows [pos, pos + n) of every layer. K_cache, V_cache [L, B, Hkv, P_cap, hd]
+    hold the history in rows [0, pos). Returns copies of the caches with the
+    new rows filled in, and the per-layer entries k, v [L][B, Hkv, n, hd]."""
+    act = cfg.dtype
+    tokens = np.asarray(tokens)
+    B, n = tokens.shape
+    Hq, Hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    K = np.array(K_cache, dtype=np.float64, copy=True)
+    V = np.array(V_cache, dtype=np.float64, copy=True)
+    L = len(sw["Wq"])
+    h = embed(E, tokens, np.zeros((B, n, cfg.d)), act)
+    ks, vs = [], []
+    for l in range(L):
+        a = rmsnorm(h, sw["g_attn"][l], act)
+        x = a.reshape(B * n, cfg.d)
+        k = round_act(x @ np.asarray(sw["Wk"][l], np.float64).T, act).reshape(B, n, Hkv, hd).transpose(0, 2, 1, 3)
+        v = round_act(x @ np.asarray(sw["Wv"][l], np.float64).T, act).reshape(B, n, Hkv, hd).transpose(0, 2, 1, 3)
+        K[l, :, :, pos:pos + n] = k
+        V[l, :, :, pos:pos + n] = v
+        ks.append(k)
+        vs.append(v)
+        if l == L - 1:
+            break
+        q = round_act(x @ np.asarray(sw["Wq"][l], np.float64).T, act).reshape(B, n, Hq, hd)
+        o = causal_attention(q, k, v, K[l, :, :, :pos], V[l, :, :, :pos], act)
+        h = round_act(h + (o.reshape(B * n, Hq * hd) @ np.asarray(sw["Wo"][l], np.float64).T).reshape(B, n, cfg.d), act)
+        m = rmsnorm(h, sw["g_mlp"][l], act).reshape(B * n, cfg.d)
+        if sw.get("W_router") is not None:
+            y = moe_mlp(m, sw["W_router"][l], sw["W_gate"][l], sw["W_up"][l], sw["W_down"][l], sw["top_k"], act)
+        else:
+            g = m @ np.asarray(sw["W_gate"][l], np.float64).T
+            u = m @ np.asarray(sw["W_up"][l], np.float64).T
+            y = round_act(gelu_tanh(g) * u, act) @ np.asarray(sw["W_down"][l], np.float64).T
+        h = round_act(h + y.reshape(B, n, cfg.d), act)
+    return {"K": K, "V": V, "k": ks, "v": vs}
