@@ -263,57 +263,126 @@ dg_status run_ffw(dg_model *m, const void *u, void *z, const int32_t *frozen, co
   return DG_OK;
 }
 
+// The pieces of one attention block over the rows of shape sa (B canvases of
+// sa.C rows): q, k, v = x W^T (stage 1), attention over [prefix ; canvas]
+// (stage 2), out = res + o Wo^T (stage 3; res may equal x).
+dg_status qkv_part(dg_model *m, const void *x, const void *Wq, const void *Wk, const void *Wv,
+                   const dg::Shape &sa, void *q, void *k, void *v, hipStream_t st) {
+  StageTimer tm(m, 1, st);
+  if (m->cfg.dtype == DG_DTYPE_BF16) {
+    using u16 = uint16_t;
+    DG_HIP(dg::launch_qkv_bf16(static_cast<const u16 *>(x), static_cast<const u16 *>(Wq),
+                               static_cast<const u16 *>(Wk), static_cast<const u16 *>(Wv), sa,
+                               static_cast<u16 *>(q), static_cast<u16 *>(k), static_cast<u16 *>(v), st),
+           "qkv launch");
+  } else {
+    DG_HIP(dg::launch_qkv_f32(static_cast<const float *>(x), static_cast<const float *>(Wq),
+                              static_cast<const float *>(Wk), static_cast<const float *>(Wv), sa,
+                              static_cast<float *>(q), static_cast<float *>(k), static_cast<float *>(v), st),
+           "qkv launch");
+  }
+  return DG_OK;
+}
+
+dg_status attend_part(dg_model *m, const void *q, const void *k, const void *v, const void *Kp,
+                      const void *Vp, const dg::Shape &sa, void *o, hipStream_t st) {
+  StageTimer tm(m, 2, st);
+  if (m->cfg.dtype == DG_DTYPE_BF16) {
+    using u16 = uint16_t;
+    DG_HIP(dg::launch_attention_bf16(static_cast<const u16 *>(q), static_cast<const u16 *>(k),
+                                     static_cast<const u16 *>(v), static_cast<const u16 *>(Kp),
+                                     static_cast<const u16 *>(Vp), sa, m->attn, static_cast<u16 *>(o), st),
+           "attention launch");
+  } else {
+    DG_HIP(dg::launch_attention_f32(static_cast<const float *>(q), static_cast<const float *>(k),
+                                    static_cast<const float *>(v), static_cast<const float *>(Kp),
+                                    static_cast<const float *>(Vp), sa, static_cast<float *>(o), st),
+           "attention launch");
+  }
+  return DG_OK;
+}
+
+dg_status oproj_part(dg_model *m, const void *o, const void *Wo, const void *res, const dg::Shape &sa,
+                     void *out, hipStream_t st) {
+  StageTimer tm(m, 3, st);
+  if (m->cfg.dtype == DG_DTYPE_BF16) {
+    using u16 = uint16_t;
+    DG_HIP(dg::launch_residual_gemm_bf16(static_cast<const u16 *>(o), static_cast<const u16 *>(Wo),
+                                         static_cast<const u16 *>(res), sa.R(), sa.d, sa.Hq * sa.hd,
+                                         static_cast<u16 *>(out), st),
+           "out-projection launch");
+  } else {
+    DG_HIP(dg::launch_oproj_f32(static_cast<const float *>(o), static_cast<const float *>(Wo),
+                                static_cast<const float *>(res), sa, static_cast<float *>(out), st),
+           "out-projection launch");
+  }
+  return DG_OK;
+}
+
 // One attention block: q, k, v = x W^T; attention over [prefix ; canvas];
 // out = res + o Wo^T (res may equal x). Stages 1-3 of the profile.
 dg_status attn_block(dg_model *m, const void *x, const void *res, const void *Wq, const void *Wk,
                      const void *Wv, const void *Wo, const void *Kp, const void *Vp,
                      const dg::Shape &sa, void *q, void *k, void *v, void *o, void *out,
                      hipStream_t st) {
-  const dg::Shape &s = m->s;
-  if (m->cfg.dtype == DG_DTYPE_BF16) {
+  if (dg_status e = qkv_part(m, x, Wq, Wk, Wv, sa, q, k, v, st)) return e;
+  if (dg_status e = attend_part(m, q, k, v, Kp, Vp, sa, o, st)) return e;
+  return oproj_part(m, o, Wo, res, sa, out, st);
+}
+
+// The MLP of stack layer l on R rows (canvases of C rows): out = hin +
+// MLP(rmsnorm(hin) g_mlp), dense gated or routed experts; the norm goes
+// through st_a. Stage 9 of the profile.
+dg_status stack_mlp(dg_model *m, int l, int R, int C, const void *hin, void *out, hipStream_t st) {
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  const int d = m->s.d, F = m->st_F;
+  const dg_layer_weights &lw = m->st_w[l];
+  StageTimer tm(m, 9, st);
+  DG_HIP(dg::launch_rmsnorm(bf16, hin, lw.g_mlp, R, d, kRmsEps, m->st_a, st), "norm launch");
+  if (m->st_X) {
+    // mixture of experts: route, group, expert GEMMs, weighted combine
+    const int X = m->st_X, K = m->st_k;
+    DG_HIP(dg::launch_moe_route(bf16, m->st_a, m->st_wr[l], R, d, X, K, m->st_sel, m->st_wts,
+                                bf16 ? m->st_list : nullptr, m->st_offs, m->st_toff, st),
+           "router launch");
+    if (bf16) {
+      using u16 = uint16_t;
+      const u16 *gu = static_cast<const u16 *>(m->st_gu) + static_cast<size_t>(l) * X * 2 * F * d;
+      DG_HIP(dg::launch_moe_experts_bf16(static_cast<const u16 *>(m->st_a), gu,
+                                         static_cast<const u16 *>(lw.W_down), m->st_list, m->st_offs,
+                                         m->st_toff, R, K, X, d, F, static_cast<u16 *>(m->st_hid),
+                                         m->st_y, st),
+             "expert GEMM launch");
+    } else {
+      DG_HIP(dg::launch_moe_experts_f32(static_cast<const float *>(m->st_a), m->st_sel,
+                                        static_cast<const float *>(lw.W_gate),
+                                        static_cast<const float *>(lw.W_up),
+                                        static_cast<const float *>(lw.W_down), R * K, K, d, F,
+                                        static_cast<float *>(m->st_hid), m->st_y, st),
+             "expert launch");
+    }
+    DG_HIP(dg::launch_moe_combine(bf16, hin, m->st_y, m->st_wts, R, d, K, out, st), "combine launch");
+  } else if (bf16) {
     using u16 = uint16_t;
-    {
-      StageTimer tm(m, 1, st);
-      DG_HIP(dg::launch_qkv_bf16(static_cast<const u16 *>(x), static_cast<const u16 *>(Wq),
-                                 static_cast<const u16 *>(Wk), static_cast<const u16 *>(Wv), s,
-                                 static_cast<u16 *>(q), static_cast<u16 *>(k), static_cast<u16 *>(v), st),
-             "qkv launch");
-    }
-    {
-      StageTimer tm(m, 2, st);
-      DG_HIP(dg::launch_attention_bf16(static_cast<const u16 *>(q), static_cast<const u16 *>(k),
-                                       static_cast<const u16 *>(v), static_cast<const u16 *>(Kp),
-                                       static_cast<const u16 *>(Vp), sa, m->attn, static_cast<u16 *>(o), st),
-             "attention launch");
-    }
-    {
-      StageTimer tm(m, 3, st);
-      DG_HIP(dg::launch_residual_gemm_bf16(static_cast<const u16 *>(o), static_cast<const u16 *>(Wo),
-                                           static_cast<const u16 *>(res), s.R(), s.d, s.Hq * s.hd,
-                                           static_cast<u16 *>(out), st),
-             "out-projection launch");
-    }
+    const u16 *gu = static_cast<const u16 *>(m->st_gu) + static_cast<size_t>(l) * 2 * F * d;
+    DG_HIP(dg::launch_ffw_gate_up_bf16(static_cast<const u16 *>(m->st_a), gu, R, d, F,
+                                       static_cast<u16 *>(m->st_hid), st),
+           "MLP gate/up launch");
+    DG_HIP(dg::launch_residual_gemm_bf16(static_cast<const u16 *>(m->st_hid),
+                                         static_cast<const u16 *>(lw.W_down),
+                                         static_cast<const u16 *>(hin), R, d, F, static_cast<u16 *>(out), st),
+           "MLP down launch");
   } else {
-    {
-      StageTimer tm(m, 1, st);
-      DG_HIP(dg::launch_qkv_f32(static_cast<const float *>(x), static_cast<const float *>(Wq),
-                                static_cast<const float *>(Wk), static_cast<const float *>(Wv), s,
-                                static_cast<float *>(q), static_cast<float *>(k), static_cast<float *>(v), st),
-             "qkv launch");
-    }
-    {
-      StageTimer tm(m, 2, st);
-      DG_HIP(dg::launch_attention_f32(static_cast<const float *>(q), static_cast<const float *>(k),
-                                      static_cast<const float *>(v), static_cast<const float *>(Kp),
-                                      static_cast<const float *>(Vp), sa, static_cast<float *>(o), st),
-             "attention launch");
-    }
-    {
-      StageTimer tm(m, 3, st);
-      DG_HIP(dg::launch_oproj_f32(static_cast<const float *>(o), static_cast<const float *>(Wo),
-                                  static_cast<const float *>(res), s, static_cast<float *>(out), st),
-             "out-projection launch");
-    }
+    DG_HIP(dg::launch_ffw_gate_up_f32(static_cast<const float *>(m->st_a),
+                                      static_cast<const float *>(lw.W_gate),
+                                      static_cast<const float *>(lw.W_up), R, d, F,
+                                      static_cast<float *>(m->st_hid), st),
+           "MLP gate/up launch");
+    DG_HIP(dg::launch_ffw_down_f32(static_cast<const float *>(m->st_hid),
+                                   static_cast<const float *>(lw.W_down), R, d, F, C, nullptr,
+                                   nullptr, static_cast<float *>(out), st,
+                                   static_cast<const float *>(hin)),
+           "MLP down launch");
   }
   return DG_OK;
 }
@@ -329,7 +398,7 @@ dg_status run_stack(dg_model *m, const void *h0, const void *Kp, const void *Vp,
   const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
   const size_t es = bf16 ? 2 : 4;
   const size_t cache = static_cast<size_t>(s.B) * s.Hkv * s.P * s.hd * es;
-  const int R = s.R(), d = s.d, F = m->st_F;
+  const int R = s.R(), d = s.d;
   const void *h = h0;
   void *hb[2] = {m->st_hb, m->st_hc};
   for (int l = 0; l < m->st_L; ++l) {
@@ -342,59 +411,68 @@ dg_status run_stack(dg_model *m, const void *h0, const void *Kp, const void *Vp,
                                  static_cast<const char *>(Kp) + l * cache,
                                  static_cast<const char *>(Vp) + l * cache, sa, q, k, v, o, m->st_ha, st))
       return e;
-    StageTimer tm(m, 9, st);
-    DG_HIP(dg::launch_rmsnorm(bf16, m->st_ha, lw.g_mlp, R, d, kRmsEps, m->st_a, st), "norm launch");
     void *hn = hb[l & 1];
-    if (m->st_X) {
-      // mixture of experts: route, group, expert GEMMs, weighted combine
-      const int X = m->st_X, K = m->st_k;
-      DG_HIP(dg::launch_moe_route(bf16, m->st_a, m->st_wr[l], R, d, X, K, m->st_sel, m->st_wts,
-                                  bf16 ? m->st_list : nullptr, m->st_offs, m->st_toff, st),
-             "router launch");
-      if (bf16) {
-        using u16 = uint16_t;
-        const u16 *gu = static_cast<const u16 *>(m->st_gu) + static_cast<size_t>(l) * X * 2 * F * d;
-        DG_HIP(dg::launch_moe_experts_bf16(static_cast<const u16 *>(m->st_a), gu,
-                                           static_cast<const u16 *>(lw.W_down), m->st_list, m->st_offs,
-                                           m->st_toff, R, K, X, d, F, static_cast<u16 *>(m->st_hid),
-                                           m->st_y, st),
-               "expert GEMM launch");
-      } else {
-        DG_HIP(dg::launch_moe_experts_f32(static_cast<const float *>(m->st_a), m->st_sel,
-                                          static_cast<const float *>(lw.W_gate),
-                                          static_cast<const float *>(lw.W_up),
-                                          static_cast<const float *>(lw.W_down), R * K, K, d, F,
-                                          static_cast<float *>(m->st_hid), m->st_y, st),
-               "expert launch");
-      }
-      DG_HIP(dg::launch_moe_combine(bf16, m->st_ha, m->st_y, m->st_wts, R, d, K, hn, st), "combine launch");
-    } else if (bf16) {
-      using u16 = uint16_t;
-      const u16 *gu = static_cast<const u16 *>(m->st_gu) + static_cast<size_t>(l) * 2 * F * d;
-      DG_HIP(dg::launch_ffw_gate_up_bf16(static_cast<const u16 *>(m->st_a), gu, R, d, F,
-                                         static_cast<u16 *>(m->st_hid), st),
-             "MLP gate/up launch");
-      DG_HIP(dg::launch_residual_gemm_bf16(static_cast<const u16 *>(m->st_hid),
-                                           static_cast<const u16 *>(lw.W_down),
-                                           static_cast<const u16 *>(m->st_ha), R, d, F,
-                                           static_cast<u16 *>(hn), st),
-             "MLP down launch");
-    } else {
-      DG_HIP(dg::launch_ffw_gate_up_f32(static_cast<const float *>(m->st_a),
-                                        static_cast<const float *>(lw.W_gate),
-                                        static_cast<const float *>(lw.W_up), R, d, F,
-                                        static_cast<float *>(m->st_hid), st),
-             "MLP gate/up launch");
-      DG_HIP(dg::launch_ffw_down_f32(static_cast<const float *>(m->st_hid),
-                                     static_cast<const float *>(lw.W_down), R, d, F, s.C, nullptr,
-                                     nullptr, static_cast<float *>(hn), st,
-                                     static_cast<const float *>(m->st_ha)),
-             "MLP down launch");
-    }
+    if (dg_status e = stack_mlp(m, l, R, s.C, m->st_ha, hn, st)) return e;
     h = hn;
   }
   StageTimer tm(m, 9, st);
   DG_HIP(dg::launch_rmsnorm(bf16, h, m->st_gfinal, R, d, kRmsEps, hf, st), "norm launch");
+  return DG_OK;
+}
+
+// Causal encoder pass of the stack (prefill / commit with a stack attached):
+// tokens [B, ld] (columns [0, n)) into cache rows [pos, pos + n) of every
+// layer's slice of K, V ([L, B, Hkv, P, hd]). Chunks of at most C tokens;
+// per chunk h = E[x]; per layer a = rmsnorm(h) g_attn, q, k, v = a W^T, k and
+// v copied into the layer's cache rows, then (all but the last layer)
+// attention of the chunk over the cache rows before it and, causally, over
+// its own keys, h += o Wo^T and h += MLP. Stage 8 covers the embedding and
+// the copies; the layers' kernels count under stages 1-3 and 9.
+dg_status encode_stack(dg_model *m, const int32_t *tokens, int n, int ld, int pos, void *K, void *V,
+                       hipStream_t st) {
+  const dg::Shape &s = m->s;
+  const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
+  const size_t es = bf16 ? 2 : 4;
+  const size_t cache = static_cast<size_t>(s.B) * s.Hkv * s.P * s.hd * es;
+  const int d = s.d, L = m->st_L;
+  for (int c0 = 0; c0 < n; c0 += s.C) {
+    const int nc = n - c0 < s.C ? n - c0 : s.C;
+    dg::Shape sc = s;      // the chunk as a canvas of nc rows over cache rows [0, pos + c0)
+    sc.C = nc;
+    sc.P = pos + c0;
+    sc.Pst = s.P;
+    sc.causal = 1;
+    if (bf16 && dg::attention_workspace_bytes(sc) > m->L.attn)
+      return fail(DG_ERR_UNSUPPORTED, "internal: encoder attention partials exceed the workspace");
+    const int R = sc.R();
+    {
+      StageTimer tm(m, 8, st);
+      DG_HIP(dg::launch_embed_tokens(bf16, m->w.E, tokens + c0, ld, s.B, nc, d, s.V, m->h0, st),
+             "encoder embedding launch");
+    }
+    const void *h = m->h0;
+    void *hb[2] = {m->st_hb, m->st_hc};
+    for (int l = 0; l < L; ++l) {
+      const dg_layer_weights &lw = m->st_w[l];
+      char *Kl = static_cast<char *>(K) + l * cache;
+      char *Vl = static_cast<char *>(V) + l * cache;
+      {
+        StageTimer tm(m, 9, st);
+        DG_HIP(dg::launch_rmsnorm(bf16, h, lw.g_attn, R, d, kRmsEps, m->st_a, st), "norm launch");
+      }
+      if (dg_status e = qkv_part(m, m->st_a, lw.Wq, lw.Wk, lw.Wv, sc, m->q, m->k, m->v, st)) return e;
+      {
+        StageTimer tm(m, 8, st);
+        DG_HIP(dg::launch_kv_to_cache(bf16, m->k, m->v, sc, pos + c0, Kl, Vl, st), "cache copy launch");
+      }
+      if (l == L - 1) break;   // the last layer's output feeds no cache entry
+      if (dg_status e = attend_part(m, m->q, m->k, m->v, Kl, Vl, sc, m->o, st)) return e;
+      if (dg_status e = oproj_part(m, m->o, lw.Wo, h, sc, m->st_ha, st)) return e;
+      void *hn = hb[l & 1];
+      if (dg_status e = stack_mlp(m, l, R, nc, m->st_ha, hn, st)) return e;
+      h = hn;
+    }
+  }
   return DG_OK;
 }
 
@@ -616,6 +694,7 @@ dg_status generate_entropy(dg_model *m, const void *K_pre, const void *V_pre, in
 // [pos, pos + n): key and value projections of the token embeddings.
 dg_status encode_kv(dg_model *m, const int32_t *tokens, int n, int ld, int pos, void *K, void *V,
                     hipStream_t st) {
+  if (m->st_L) return encode_stack(m, tokens, n, ld, pos, K, V, st);
   const dg::Shape &s = m->s;
   StageTimer tm(m, 8, st);
   if (m->cfg.dtype == DG_DTYPE_BF16) {
@@ -1187,8 +1266,6 @@ dg_status dg_encode_kv(dg_model *m, const int32_t *tokens, int32_t n, int32_t po
   const dg::Shape &s = m->s;
   if (n < 0 || pos < 0 || static_cast<int64_t>(pos) + n > s.P)
     return fail(DG_ERR_INVALID_ARG, "need n >= 0, pos >= 0 and pos + n <= P (n=%d pos=%d P=%d)", n, pos, s.P);
-  if (m->st_L)
-    return fail(DG_ERR_UNSUPPORTED, "cache entries of a multi-layer stack need its causal encoder pass (not built)");
   if (n == 0) return DG_OK;
   if (!tokens || !K_cache || !V_cache) return fail(DG_ERR_INVALID_ARG, "tokens, K_cache and V_cache must be non-NULL");
   const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
@@ -1208,8 +1285,6 @@ dg_status dg_generate_blocks(dg_model *m, void *K_cache, void *V_cache, int32_t 
     return fail(DG_ERR_INVALID_ARG, "need n_canvases >= 1, P0 >= 0 and P0 + n_canvases * C <= P "
                 "(P0=%d n_canvases=%d C=%d P=%d)", P0, n_canvases, s.C, s.P);
   if (!K_cache || !V_cache) return fail(DG_ERR_INVALID_ARG, "K_cache and V_cache must be non-NULL");
-  if (m->st_L)
-    return fail(DG_ERR_UNSUPPORTED, "block generation with a multi-layer stack needs its causal encoder pass (not built)");
   if (steps < 1 || steps > kMaxSteps)
     return fail(DG_ERR_INVALID_ARG, "steps must be in [1, %d] (got %d)", kMaxSteps, steps);
   const bool bf16 = m->cfg.dtype == DG_DTYPE_BF16;
@@ -1312,8 +1387,6 @@ dg_status dg_generate_blocks_entropy(dg_model *m, void *K_cache, void *V_cache, 
     return fail(DG_ERR_INVALID_ARG, "need n_canvases >= 1, P0 >= 0 and P0 + n_canvases * C <= P "
                 "(P0=%d n_canvases=%d C=%d P=%d)", P0, n_canvases, s.C, s.P);
   if (!K_cache || !V_cache) return fail(DG_ERR_INVALID_ARG, "K_cache and V_cache must be non-NULL");
-  if (m->st_L)
-    return fail(DG_ERR_UNSUPPORTED, "block generation with a multi-layer stack needs its causal encoder pass (not built)");
   if (max_steps < 1 || max_steps > kMaxSteps)
     return fail(DG_ERR_INVALID_ARG, "max_steps must be in [1, %d] (got %d)", kMaxSteps, max_steps);
   if (s.C > dg::kSelectMaxC)

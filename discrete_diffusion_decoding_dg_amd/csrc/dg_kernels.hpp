@@ -20,6 +20,9 @@ struct StepParams {
 struct Shape {
   int B, C, P, d, Hq, Hkv, hd, V;
   int Pst = 0;   // cache rows per (canvas, kv head) slice; 0: P
+  // attention: canvas query i sees the P prefix keys and canvas keys 0..i
+  // only (the causal encoder pass); 0: every canvas key (the decoder)
+  int causal = 0;
   int R() const { return B * C; }
   int G() const { return Hq / Hkv; }
   int pstride() const { return Pst ? Pst : P; }
@@ -65,6 +68,10 @@ hipError_t launch_rmsnorm(bool bf16, const void *x, const void *g, int R, int d,
 // p0[r, v] = exp(p0[r, v] - lse[r]) in place (p0 holds scaled logits on entry).
 hipError_t launch_p0_from_logits(float *p0, const float *lse, int R, int V, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
+// Canvas-layout k, v [B, Hkv, C, hd] (act) into rows [row0, row0 + C) of
+// caches [B, Hkv, Pst, hd] (C, Pst from s; the encoder pass of a stack).
+hipError_t launch_kv_to_cache(bool bf16, const void *k, const void *v, const Shape &s, int row0,
+                              void *K, void *V, hipStream_t st);
 // Copy small host arrays to device memory through kernel arguments.
 hipError_t launch_set_params(StepParams *dst, const StepParams *src, int n, hipStream_t st);
 hipError_t launch_fill_i32(int32_t *p, size_t n, int32_t v, hipStream_t st);

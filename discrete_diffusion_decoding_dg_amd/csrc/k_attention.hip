@@ -59,6 +59,7 @@ struct AttnArgs {
   float2 *ml;     // [splits][R][Hq] (m, l), log2 units
   int B, C, P, Pst, Hq, Hkv, G, splits, tiles_per_split;   // Pst: cache rows per (b, g)
   int qblocks;                                              // query blocks per (b, g, split)
+  int causal;                                               // canvas key j visible to query i iff j <= i
   float scale_log2;   // log2(e) / sqrt(hd)
 };
 
@@ -130,7 +131,8 @@ __device__ __forceinline__ void lds_dma16_sa(const void *base, uint32_t voff, ui
       : "memory");
 }
 
-template <int HD, int NWA>
+// CAUSAL: the causal encoder pass (canvas query i sees canvas keys 0..i).
+template <int HD, int NWA, bool CAUSAL>
 __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
   constexpr int BQ = NWA * 32;                   // query rows per block
   using G_ = Geo<HD>;
@@ -302,6 +304,18 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
         for (int e = 0; e < 16; ++e)
           if (kv0 + mb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3) >= Lk) sv[mb][e] = -INFINITY;
     }
+    if constexpr (CAUSAL) {
+      // canvas keys after this lane's query drop out (a whole tile may, for
+      // some queries of the block)
+      if (kv0 + BK > a.P + qi + 1) {
+        const int last = a.P + qi;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (kv0 + mb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3) > last) sv[mb][e] = -INFINITY;
+      }
+    }
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -331,7 +345,9 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sv[mb][e], a.scale_log2, -m_ref));
+        float p = __builtin_amdgcn_exp2f(fmaf(sv[mb][e], a.scale_log2, -m_ref));
+        // no visible key yet for this query (whole tiles masked): nothing adds
+        if constexpr (CAUSAL) p = (m_ref == -INFINITY) ? 0.f : p;
         psum += p;
         pa[2 * mb + (e >> 3)][e & 7] = static_cast<__bf16>(p);
       }
@@ -513,6 +529,7 @@ hipError_t launch_attention_bf16(const uint16_t *q, const uint16_t *k, const uin
   AttnArgs a;
   a.q = q; a.k = k; a.v = v; a.Kp = Kp; a.Vp = Vp; a.o = o;
   a.B = s.B; a.C = s.C; a.P = s.P; a.Pst = s.pstride(); a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.G();
+  a.causal = s.causal;
   int nwa = 8;
   plan(s, nwa, a.splits, a.tiles_per_split);
   const size_t rows = static_cast<size_t>(s.R()) * s.Hq;
@@ -527,10 +544,16 @@ hipError_t launch_attention_bf16(const uint16_t *q, const uint16_t *k, const uin
   dim3 grid(static_cast<uint32_t>(nblocks));
 #define DG_ATT(HD_)                                                                       \
   case HD_:                                                                               \
-    if (nwa == 8)                                                                         \
-      hipLaunchKernelGGL((attn_fwd_kernel<HD_, 8>), grid, dim3(512), 0, st, a);           \
-    else                                                                                  \
-      hipLaunchKernelGGL((attn_fwd_kernel<HD_, 4>), grid, dim3(256), 0, st, a);           \
+    if (s.causal) {                                                                       \
+      if (nwa == 8)                                                                       \
+        hipLaunchKernelGGL((attn_fwd_kernel<HD_, 8, true>), grid, dim3(512), 0, st, a);   \
+      else                                                                                \
+        hipLaunchKernelGGL((attn_fwd_kernel<HD_, 4, true>), grid, dim3(256), 0, st, a);   \
+    } else if (nwa == 8) {                                                                \
+      hipLaunchKernelGGL((attn_fwd_kernel<HD_, 8, false>), grid, dim3(512), 0, st, a);    \
+    } else {                                                                              \
+      hipLaunchKernelGGL((attn_fwd_kernel<HD_, 4, false>), grid, dim3(256), 0, st, a);    \
+    }                                                                                     \
     break;
   switch (s.hd) {
     DG_ATT(64) DG_ATT(128) DG_ATT(176)

@@ -302,6 +302,49 @@ __global__ void __launch_bounds__(256) embed_tokens_kernel(const T *__restrict__
   for (int c = threadIdx.x; c < d; c += blockDim.x) hr[c] = in ? er[c] : T(0);
 }
 
+// One thread per unit U (16 or 4 bytes) of a (canvas, kv head, row) of k and of v.
+template <typename U>
+__global__ void __launch_bounds__(256) kv_to_cache_kernel(const U *__restrict__ k, const U *__restrict__ v,
+                                                          int64_t rows, int C, int Pst, int row0, int q,
+                                                          U *__restrict__ K, U *__restrict__ V) {
+  const int64_t half = rows * q;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < 2 * half;
+       t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const bool isv = t >= half;
+    const int64_t u = isv ? t - half : t;
+    const int64_t row = u / q;               // (slice, i) with slice = b * Hkv + g
+    const int e = static_cast<int>(u - row * q);
+    const int64_t slice = row / C;
+    const int i = static_cast<int>(row - slice * C);
+    const int64_t dst = (slice * Pst + row0 + i) * q + e;
+    if (isv)
+      V[dst] = v[u];
+    else
+      K[dst] = k[u];
+  }
+}
+
+hipError_t launch_kv_to_cache(bool bf16, const void *k, const void *v, const Shape &s, int row0,
+                              void *K, void *V, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(s.B) * s.Hkv * s.C;
+  const int bytes = s.hd * (bf16 ? 2 : 4);
+  if (rows == 0) return hipSuccess;
+  const auto a16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  const bool wide = bytes % 16 == 0 && a16(k) && a16(v) && a16(K) && a16(V);
+  const int q = wide ? bytes / 16 : bytes / 4;
+  int64_t blocks = (2 * rows * q + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (wide)
+    hipLaunchKernelGGL(kv_to_cache_kernel<uint4>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st,
+                       static_cast<const uint4 *>(k), static_cast<const uint4 *>(v), rows, s.C,
+                       s.pstride(), row0, q, static_cast<uint4 *>(K), static_cast<uint4 *>(V));
+  else
+    hipLaunchKernelGGL(kv_to_cache_kernel<uint32_t>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                       st, static_cast<const uint32_t *>(k), static_cast<const uint32_t *>(v), rows, s.C,
+                       s.pstride(), row0, q, static_cast<uint32_t *>(K), static_cast<uint32_t *>(V));
+  return hipGetLastError();
+}
+
 hipError_t launch_embed_tokens(bool bf16, const void *E, const int32_t *x, int ld, int B, int n,
                                int d, int V, void *h, hipStream_t st) {
   if (static_cast<int64_t>(B) * n == 0) return hipSuccess;

@@ -50,19 +50,20 @@ __global__ void __launch_bounds__(256) qkv_f32_kernel(const float *__restrict__ 
 }
 
 // One block per (row, head): scores over all P + C keys in LDS, then O.
+// causal: canvas query i sees canvas keys 0..i only (the encoder pass).
 __global__ void __launch_bounds__(256) attn_f32_kernel(const float *__restrict__ q,
                                                        const float *__restrict__ k,
                                                        const float *__restrict__ v,
                                                        const float *__restrict__ Kp,
                                                        const float *__restrict__ Vp, int C, int P,
                                                        int Pst, int Hq, int Hkv, int hd, float scale,
-                                                       float *__restrict__ o) {
+                                                       int causal, float *__restrict__ o) {
   extern __shared__ float sc[];   // P + C scores
   __shared__ float red[256];
   const int r = blockIdx.x, h = blockIdx.y;
   const int b = r / C;
   const int g = h / (Hq / Hkv);
-  const int Lk = P + C;
+  const int Lk = causal ? P + (r - b * C) + 1 : P + C;
   const float *qr = q + (static_cast<int64_t>(r) * Hq + h) * hd;
   const float *kp = Kp + (static_cast<int64_t>(b) * Hkv + g) * Pst * hd;
   const float *vp = Vp + (static_cast<int64_t>(b) * Hkv + g) * Pst * hd;
@@ -361,7 +362,7 @@ hipError_t launch_attention_f32(const float *q, const float *k, const float *v, 
   const size_t shm = static_cast<size_t>(s.P + s.C) * sizeof(float);
   hipLaunchKernelGGL(attn_f32_kernel, dim3(s.R(), s.Hq), dim3(256), shm, st, q, k, v, Kp, Vp,
                      s.C, s.P, s.pstride(), s.Hq, s.Hkv, s.hd,
-                     static_cast<float>(1.0 / sqrt((double)s.hd)), o);
+                     static_cast<float>(1.0 / sqrt((double)s.hd)), s.causal, o);
   return hipGetLastError();
 }
 

@@ -235,10 +235,17 @@ dg_status dg_generate_canvas_entropy(dg_model *m, const void *K_pre, const void 
  * entries of a token are its key and value projections with no
  * self-conditioning input, k = E[x] Wk^T and v = E[x] Wv^T (rounded to act),
  * so prefill and commit are one operation.
+ * With a decoder stack attached (dg_set_stack) the encoder is the stack's
+ * causal pass: h = E[x]; per layer a = rmsnorm(h) g_attn, the layer's cache
+ * entries k = a Wk^T, v = a Wv^T, and (every layer but the last) attention
+ * of each new token over the cache rows below it and the new tokens up to
+ * itself, h += o Wo^T, h += MLP(rmsnorm(h) g_mlp); tokens go through in
+ * chunks of at most C, each seeing the earlier chunks as history.
  *   tokens [B, n] int32 (a token outside [0, V) embeds as a zero row);
- *   K_cache, V_cache [B, Hkv, P, hd] act: the model's P is the cache
- *   capacity; rows [pos, pos + n) of every (canvas, kv head) slice are
- *   written, nothing else. Needs n >= 0, pos >= 0 and pos + n <= P. */
+ *   K_cache, V_cache [B, Hkv, P, hd] act ([L, B, Hkv, P, hd] with a stack
+ *   of L layers): the model's P is the cache capacity; rows [pos, pos + n)
+ *   of every (layer, canvas, kv head) slice are written, nothing else.
+ *   Needs n >= 0, pos >= 0 and pos + n <= P. */
 dg_status dg_encode_kv(dg_model *m, const int32_t *tokens, int32_t n, int32_t pos, void *K_cache,
                        void *V_cache, void *stream);
 
@@ -249,7 +256,8 @@ dg_status dg_encode_kv(dg_model *m, const int32_t *tokens, int32_t n, int32_t po
  * `steps` steps and seed seed + j * steps, attending to cache rows
  * [0, P0 + j C) only; its final tokens are then encoded into rows
  * [P0 + j C, P0 + (j + 1) C) (dg_encode_kv).
- *   K_cache, V_cache [B, Hkv, P, hd] act, read and extended in place;
+ *   K_cache, V_cache [B, Hkv, P, hd] act ([L, B, Hkv, P, hd] with a stack),
+ *   read and extended in place;
  *   P0 + n_canvases * C <= P; x_out [B, n_canvases, C] int32. */
 dg_status dg_generate_blocks(dg_model *m, void *K_cache, void *V_cache, int32_t P0,
                              int32_t n_canvases, int32_t steps, uint64_t seed, int32_t *x_out,
@@ -306,9 +314,8 @@ dg_status dg_set_ffw(dg_model *m, int32_t hidden, const void *W_gate, const void
  * The library allocates the stack's activations and, for bf16, a copy of
  * each layer's W_gate/W_up with rows interleaved in groups of 32; waits for
  * the device (set-up call). bf16 needs mlp_hidden % 64 == 0
- * (DG_ERR_UNSUPPORTED). dg_encode_kv and dg_generate_blocks return
- * DG_ERR_UNSUPPORTED while a stack is attached (its cache entries need the
- * stack's causal encoder pass, which is not built). */
+ * (DG_ERR_UNSUPPORTED). dg_encode_kv and block generation then run the
+ * stack's causal encoder pass (see dg_encode_kv). */
 typedef struct dg_layer_weights {
   const void *Wq, *Wk, *Wv, *Wo;
   const void *g_attn, *g_mlp;
