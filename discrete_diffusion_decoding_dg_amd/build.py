@@ -53,6 +53,51 @@ def build(verbose=False, extra=()):
     return LIB
 
 
+# Host-side sanitizers for the C ABI layer (argument checking, workspace
+# carving): dg_api.cpp is rebuilt with AddressSanitizer and
+# UndefinedBehaviorSanitizer on its host code only (-Xarch_host), and linked
+# with the other objects into a separate library; a process loading it needs
+# the ASan runtime preloaded (sanitizer_runtime()).
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+            "-g"]
+
+
+def sanitizer_runtime():
+    """Path of the ASan runtime that a process must preload to load the
+    sanitized library."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin", "clang++")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang++"
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def build_sanitized(out_dir):
+    """libdg.so with the host code of dg_api.cpp under ASan/UBSan, in out_dir."""
+    os.makedirs(out_dir, exist_ok=True)
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        lang = ["-x", "hip"] if src.endswith(".cpp") else []
+        extra = SANITIZE if src == "dg_api.cpp" else []
+        cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile of {src} failed:\n{' '.join(cmd)}\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(one, SOURCES))
+    lib = os.path.join(out_dir, "libdg_sanitized.so")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", lib, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     extra = sys.argv[1:]
     print(build(verbose=True, extra=extra))

@@ -809,7 +809,11 @@ dg_status scratch_address(int dev, char **out) {
 extern "C" {
 
 const char *dg_status_string(dg_status s) {
-  switch (s) {
+  // C callers may pass any int: read the raw value (loading a value outside
+  // the enumerators as the C++ enum type is undefined behaviour)
+  int v;
+  std::memcpy(&v, &s, sizeof(v));
+  switch (v) {
     case DG_OK: return "DG_OK";
     case DG_ERR_INVALID_ARG: return "DG_ERR_INVALID_ARG";
     case DG_ERR_UNSUPPORTED: return "DG_ERR_UNSUPPORTED";

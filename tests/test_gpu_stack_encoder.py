@@ -163,3 +163,52 @@ def test_stack_generate_blocks(name):
     end = P0 + nb * cfg.C
     assert np.array_equal(Kh[:, :, :, end:], Kstart[:, :, :, end:])
     del keep
+
+
+def test_stack_generate_blocks_entropy():
+    """The recommended sampler's block generation through a stack: every canvas
+    and its step count equal a single-canvas adaptive generation over exactly
+    its prefix; every commit holds the stack encoder's entries."""
+    import math
+
+    import torch
+    import discrete_diffusion_decoding_dg_amd as dg
+    cfg, ex = _split(BLOCKS["bf16-L2"])
+    P0, nb = ex["P0"], ex["n_canvases"]
+    max_steps, seed = 6, 9
+    eps_a, eps_s = 2.0 * math.log(cfg.V), 1.0
+    inp = make_inputs(cfg)
+    m = GpuModel(cfg, inp)
+    keep = _attach(m, cfg, inp)
+    K = to_dev(inp, "S_K_pre", cfg).clone()
+    V = to_dev(inp, "S_V_pre", cfg).clone()
+    K[:, :, :, P0:] = 100.0
+    V[:, :, :, P0:] = -100.0
+    x = torch.empty((cfg.B, nb, cfg.C), dtype=torch.int32, device="cuda")
+    steps = torch.empty((cfg.B, nb), dtype=torch.int32, device="cuda")
+    print(f"[gpu] stack adaptive blocks P0={P0} canvases={nb} max_steps={max_steps}", flush=True)
+    dg.dg_generate_blocks_entropy(m.model, K, V, P0, nb, max_steps, seed, eps_a, eps_s, x, steps)
+    torch.cuda.synchronize()
+    m.close()
+    xh, sh, Kh, Vh = x.cpu().numpy(), steps.cpu().numpy(), to_host(K), to_host(V)
+    rt, prt = _tol(cfg)
+    sw = _sw(cfg, inp)
+    for j in range(nb):
+        Pj = P0 + j * cfg.C
+        mj = GpuModel(cfg.with_(P=Pj), inp)
+        kj = _attach(mj, cfg, inp)
+        Kj = torch.from_numpy(Kh[:, :, :, :Pj].copy()).to(torch.bfloat16).cuda()
+        Vj = torch.from_numpy(Vh[:, :, :, :Pj].copy()).to(torch.bfloat16).cuda()
+        xj = torch.empty((cfg.B, cfg.C), dtype=torch.int32, device="cuda")
+        sj = torch.empty((cfg.B,), dtype=torch.int32, device="cuda")
+        dg.dg_generate_canvas_entropy(mj.model, Kj, Vj, max_steps, seed + j * max_steps, eps_a, eps_s, xj, sj)
+        torch.cuda.synchronize()
+        mj.close()
+        del kj
+        assert np.array_equal(xh[:, j], xj.cpu().numpy()), f"canvas {j} differs from adaptive generation"
+        assert np.array_equal(sh[:, j], sj.cpu().numpy())
+        o = encode_kv_stack(cfg, inp["E"], sw, xh[:, j], Kh, Vh, Pj)
+        for l in range(cfg.n_layers):
+            assert_close(f"layer {l} k rows of canvas {j}", Kh[l][:, :, Pj:Pj + cfg.C], o["k"][l], rt,
+                         plain_rtol=prt)
+    del keep
