@@ -23,14 +23,16 @@
 //   3. z[m, slice] += P[m, tile] E[tile, slice] with v_mfma_f32_32x32x16_bf16
 //      (16x16x16 for 16-row blocks), E read transposed from LDS by
 //      ds_read_b64_tr_b16.
-// E tiles reach LDS by direct global->LDS loads (no register staging) from a
-// tile-major copy of E made when the model is created: each 16-id x 32-column
-// chunk is 1 KB contiguous, already in the chunk's LDS order, so one direct
-// load reads whole cache lines. With
-// two tile buffers (d <= 2048) the next tile is requested in two halves
-// between the contractions (after the scores and after the epilogue), where
-// its LDS writes do not compete with the contractions' LDS reads; a single
-// buffer (d = 2816) refills chunk by chunk behind the z contraction.
+// E is read from a tile-major copy made when the model is created: each
+// 16-id x 32-column chunk is 1 KB contiguous, already in the chunk's LDS
+// order, so every load reads whole cache lines. With two tile buffers
+// (d <= 2048) tiles reach LDS by direct global->LDS loads, and the next tile
+// is requested in two halves between the contractions (after the scores and
+// after the epilogue), where its LDS writes do not compete with the
+// contractions' LDS reads. Where only one buffer fits (d = 2816) each wave
+// loads its slice of the next tile into registers a whole tile ahead; the
+// score contraction takes its A operand from those registers, which are then
+// written to LDS once for the transposed reads of the z contraction.
 //
 // Gumbel noise: the Philox block of lane (row, position j) for the aligned
 // group of four tiles g holds the noise of ids 64 g + j + {0, 16, 32, 48}, one
@@ -204,9 +206,24 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
     const uint16_t *tb = a.E + (static_cast<int64_t>(tile) * (a.d / 32) + dcol0 / 32 + c) * (VT * 32);
     lds_dma16(tb, dma_off, ebuf(tile) + c * CHUNK_B);
   };
-  if (t_begin < t_end)
+  // one buffer: the wave's slice of the next tile waits in registers, lane l
+  // holding row l & 15, piece l >> 4 of each chunk (the score A operand)
+  const uint32_t a_off = static_cast<uint32_t>(eoff(lane & 15, 8 * (lane >> 4)));
+  bf16x8 ereg[NBUF == 1 ? NKS : 1];
+  auto load_tile_regs = [&](int tile) {
+    const uint8_t *tb = reinterpret_cast<const uint8_t *>(
+        a.E + (static_cast<int64_t>(tile) * (a.d / 32) + dcol0 / 32) * (VT * 32));
 #pragma unroll
-    for (int c = 0; c < NKS; ++c) dma_chunk(t_begin, c);
+    for (int c = 0; c < NKS; ++c) ereg[c] = *reinterpret_cast<const bf16x8 *>(tb + c * CHUNK_B + a_off);
+  };
+  if (t_begin < t_end) {
+    if constexpr (NBUF == 2) {
+#pragma unroll
+      for (int c = 0; c < NKS; ++c) dma_chunk(t_begin, c);
+    } else {
+      load_tile_regs(t_begin);
+    }
+  }
 
   // h1 slice as the B operand of S^T: lane holds canvas row 16 rb + (lane & 15),
   // columns dcol0 + 32 c + 8 (lane >> 4) + [0, 8)
@@ -283,7 +300,7 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
     // Each batch goes into the buffer of the previous tile, whose reads by
     // this wave's own z contraction have all returned (they fed its MFMAs).
     constexpr int kB1 = NKS / 2;   // chunk ranges [0,kB1) and [kB1,NKS)
-    const uint8_t *eb = ebuf(tile);
+    uint8_t *eb = ebuf(tile);
 
     // ---- S^T partial over this wave's slice (two accumulator sets break the
     // dependency chain of the 16-pass MFMAs)
@@ -294,10 +311,15 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
       for (int rb = 0; rb < RB; ++rb) sacc[s][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NKS; ++c) {
-      // chunk c of this tile has landed once at most its NKS-1-c younger
-      // siblings are outstanding (no load of the next tile is issued yet)
-      wait_vmcnt_le_rt<63>(NKS - 1 - c);
-      const bf16x8 ef = *reinterpret_cast<const bf16x8 *>(eb + c * CHUNK_B + eoff(lane & 15, 8 * (lane >> 4)));
+      bf16x8 ef;
+      if constexpr (NBUF == 2) {
+        // chunk c of this tile has landed once at most its NKS-1-c younger
+        // siblings are outstanding (no load of the next tile is issued yet)
+        wait_vmcnt_le_rt<63>(NKS - 1 - c);
+        ef = *reinterpret_cast<const bf16x8 *>(eb + c * CHUNK_B + a_off);
+      } else {
+        ef = ereg[c];
+      }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
         sacc[c & 1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ef, hreg[rb][c], sacc[c & 1][rb], 0, 0, 0);
@@ -315,6 +337,13 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
 #pragma unroll
         for (int c = 0; c < kB1; ++c) dma_chunk(tile + 1, c);
       }
+    } else {
+      // the buffer's previous contents fed this wave's own z contraction of
+      // the previous tile, whose reads have all returned
+#pragma unroll
+      for (int c = 0; c < NKS; ++c)
+        *reinterpret_cast<bf16x8 *>(eb + c * CHUNK_B + a_off) = ereg[c];
+      if (more) load_tile_regs(tile + 1);
     }
     __syncthreads();
 
@@ -404,12 +433,6 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
         // B operand: column lane & 31 of the chunk, ids 8 (lane >> 5) + [0, 8)
         const bf16x8 b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         zacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, b, zacc[c], 0, 0, 0);
-        if constexpr (NBUF == 1) {
-          if (more) {
-            wait_lgkm0();
-            dma_chunk(tile + 1, c);
-          }
-        }
       }
     } else {
       // A operand: row lane & 15, ids 4 (lane >> 4) + [0, 4)
@@ -421,12 +444,6 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
         const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4 *)(ch + eoff(tr_row, 16 * (n & 1) + tr_col)));
         zacc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, b, zacc[n], 0, 0, 0);
-        if constexpr (NBUF == 1) {
-          if ((n & 1) && more) {
-            wait_lgkm0();
-            dma_chunk(tile + 1, n >> 1);
-          }
-        }
       }
     }
     // noise of the next tile, off the epilogue's path
