@@ -1,0 +1,262 @@
+// Hardware probes behind the kernel designs (MI355X, gfx950): the issue cost
+// of vector-memory loads per CU, the MFMA instruction rates, LDS read
+// bandwidth, and the back-to-back launch interval. Every access stays inside
+// its buffer; every loop has a fixed trip count. Times in shader clocks come
+// from s_memtime, wall times from HIP events.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#define CHECK(x)                                                               \
+  do {                                                                         \
+    hipError_t e_ = (x);                                                       \
+    if (e_ != hipSuccess) {                                                    \
+      std::fprintf(stderr, "%s: %s\n", #x, hipGetErrorString(e_));             \
+      std::exit(1);                                                            \
+    }                                                                          \
+  } while (0)
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+
+// ---- A: vector-memory issue. Every wave of a 512-thread block issues NL
+// loads of 16 bytes per lane (1 KB per instruction) back to back, either
+// straight into LDS (global_load_lds_dwordx4) or into registers; the wave's
+// clocks from the first issue to the last, and to all data landed, are kept.
+constexpr int NL = 8, NWV = 8;
+template <bool DIRECT>
+__global__ void __launch_bounds__(512) vmem_issue(const unsigned char *buf, unsigned long long *out,
+                                                  unsigned *sink) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[NWV * NL * 1024];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)lds;
+  const unsigned char *src = buf + ((size_t)(blockIdx.x * NWV + wave) * NL) * 1024 + lane * 16;
+  u32x4 r[NL];
+  __syncthreads();
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int n = 0; n < NL; ++n) {
+    if (DIRECT) {
+      const unsigned m0 = __builtin_amdgcn_readfirstlane(base + (wave * NL + n) * 1024);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :: "s"(m0), "v"(src + n * 1024) : "memory", "m0");
+    } else {
+      r[n] = *(const u32x4 *)(src + n * 1024);
+    }
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const unsigned long long t2 = __builtin_amdgcn_s_memtime();
+  __syncthreads();
+  unsigned acc = 0;
+  if (DIRECT) {
+    acc = lds[threadIdx.x * 16];
+  } else {
+#pragma unroll
+    for (int n = 0; n < NL; ++n) acc ^= r[n].x ^ r[n].w;
+  }
+  if (acc == 0xdeadbeefu) sink[0] = acc;
+  if (lane == 0 && blockIdx.x == 0) {
+    out[wave * 2] = t1 - t0;
+    out[wave * 2 + 1] = t2 - t0;
+  }
+}
+
+// ---- B: MFMA rate. Each wave runs ITER rounds of 4 independent accumulator
+// chains of one MFMA shape with register operands.
+constexpr int MITER = 2048;
+template <int SHAPE>   // 0: 32x32x16 bf16, 1: 16x16x32 bf16, 2: 16x16x16 bf16 (1k)
+__global__ void __launch_bounds__(256) mfma_rate(const float *in, float *out) {
+  const int lane = threadIdx.x & 63;
+  const float x = in[lane];
+  bf16x8 a8, b8;
+  bf16x4 a4, b4;
+  for (int i = 0; i < 8; ++i) {
+    a8[i] = (__bf16)(x + i);
+    b8[i] = (__bf16)(x - i);
+  }
+  for (int i = 0; i < 4; ++i) {
+    a4[i] = (__bf16)(x + i);
+    b4[i] = (__bf16)(x - i);
+  }
+  float s = 0.f;
+  if constexpr (SHAPE == 0) {
+    f32x16 c0{}, c1{}, c2{}, c3{};
+    for (int it = 0; it < MITER; ++it) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, b8, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, b8, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, b8, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, b8, c3, 0, 0, 0);
+    }
+    for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  } else if constexpr (SHAPE == 1) {
+    f32x4 c0{}, c1{}, c2{}, c3{};
+    for (int it = 0; it < MITER; ++it) {
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, c3, 0, 0, 0);
+    }
+    for (int i = 0; i < 4; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  } else {
+    f32x4 c0{}, c1{}, c2{}, c3{};
+    for (int it = 0; it < MITER; ++it) {
+      c0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a4, b4, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a4, b4, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a4, b4, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a4, b4, c3, 0, 0, 0);
+    }
+    for (int i = 0; i < 4; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// ---- C: LDS read bandwidth. 8 waves read a 64 KB LDS array LITER times per
+// instruction kind: 16-byte reads (1 KB per instruction, consecutive lanes on
+// consecutive 16-byte pieces) or transposing 8-byte reads (512 B). Clocks of
+// the whole block from one barrier to the next.
+constexpr int LITER = 1024, LDS_B = 64 * 1024;
+template <bool TR>
+__global__ void __launch_bounds__(512) lds_rate(unsigned long long *out, unsigned *sink) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_B];
+  for (int i = threadIdx.x; i < LDS_B / 4; i += blockDim.x) reinterpret_cast<unsigned *>(lds)[i] = i * 2654435761u;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  unsigned acc = 0;
+  if (TR) {
+    for (int it = 0; it < LITER; ++it) {
+      const unsigned off = ((wave * 8 + it) * 512 + lane * 8) & (LDS_B - 1);
+      const bf16x4 v = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4 *)(lds + off)));
+      acc ^= __builtin_bit_cast(unsigned, __builtin_shufflevector(v, v, 0, 1));
+    }
+  } else {
+    for (int it = 0; it < LITER; ++it) {
+      const unsigned off = ((wave * 8 + it) * 1024 + lane * 16) & (LDS_B - 1);
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + off);
+      acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+  }
+  __syncthreads();
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  if (acc == 0xdeadbeefu) sink[0] = acc;
+  if (threadIdx.x == 0) out[blockIdx.x] = t1 - t0;
+}
+
+__global__ void empty_kernel() {}
+
+int main() {
+  unsigned *sink;
+  CHECK(hipMalloc(&sink, 4));
+  // A
+  {
+    const int blocks = 256;
+    const size_t bytes = (size_t)blocks * NWV * NL * 1024;
+    unsigned char *buf;
+    unsigned long long *out;
+    CHECK(hipMalloc(&buf, bytes));
+    CHECK(hipMemset(buf, 1, bytes));
+    CHECK(hipMalloc(&out, NWV * 2 * 8));
+    for (int direct = 1; direct >= 0; --direct) {
+      for (int rep = 0; rep < 3; ++rep) {
+        if (direct)
+          hipLaunchKernelGGL(vmem_issue<true>, dim3(blocks), dim3(512), 0, 0, buf, out, sink);
+        else
+          hipLaunchKernelGGL(vmem_issue<false>, dim3(blocks), dim3(512), 0, 0, buf, out, sink);
+        CHECK(hipGetLastError());
+        CHECK(hipDeviceSynchronize());
+      }
+      std::vector<unsigned long long> h(NWV * 2);
+      CHECK(hipMemcpy(h.data(), out, h.size() * 8, hipMemcpyDeviceToHost));
+      std::printf("vmem_issue %-6s 8 waves x %d loads x 1 KB, clocks to issue per wave:", direct ? "direct" : "vgpr",
+                  NL);
+      for (int w = 0; w < NWV; ++w) std::printf(" %llu", h[w * 2]);
+      std::printf(" | to landed:");
+      for (int w = 0; w < NWV; ++w) std::printf(" %llu", h[w * 2 + 1]);
+      std::printf("\n");
+    }
+    CHECK(hipFree(buf));
+    CHECK(hipFree(out));
+  }
+  // B
+  {
+    const int blocks = 4096, threads = 256;
+    float *in, *out;
+    CHECK(hipMalloc(&in, 64 * 4));
+    CHECK(hipMemset(in, 0, 64 * 4));
+    CHECK(hipMalloc(&out, (size_t)blocks * threads * 4));
+    hipEvent_t e0, e1;
+    CHECK(hipEventCreate(&e0));
+    CHECK(hipEventCreate(&e1));
+    const char *names[3] = {"v_mfma_f32_32x32x16_bf16", "v_mfma_f32_16x16x32_bf16", "v_mfma_f32_16x16x16_bf16"};
+    const double flop[3] = {32.0 * 32 * 16 * 2, 16.0 * 16 * 32 * 2, 16.0 * 16 * 16 * 2};
+    for (int shp = 0; shp < 3; ++shp) {
+      float best = 1e30f;
+      for (int rep = 0; rep < 3; ++rep) {
+        CHECK(hipEventRecord(e0));
+        if (shp == 0) hipLaunchKernelGGL(mfma_rate<0>, dim3(blocks), dim3(threads), 0, 0, in, out);
+        if (shp == 1) hipLaunchKernelGGL(mfma_rate<1>, dim3(blocks), dim3(threads), 0, 0, in, out);
+        if (shp == 2) hipLaunchKernelGGL(mfma_rate<2>, dim3(blocks), dim3(threads), 0, 0, in, out);
+        CHECK(hipGetLastError());
+        CHECK(hipEventRecord(e1));
+        CHECK(hipEventSynchronize(e1));
+        float ms;
+        CHECK(hipEventElapsedTime(&ms, e0, e1));
+        if (ms < best) best = ms;
+      }
+      const double total = flop[shp] * 4.0 * MITER * (blocks * threads / 64);
+      std::printf("mfma_rate %-26s %8.1f TFLOP/s (%.3f of 2500)\n", names[shp], total / (best * 1e-3) / 1e12,
+                  total / (best * 1e-3) / 1e12 / 2500.0);
+    }
+    CHECK(hipFree(in));
+    CHECK(hipFree(out));
+    // D
+    for (int i = 0; i < 100; ++i) hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, 0);
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    const int nl = 2000;
+    for (int i = 0; i < nl; ++i) hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, 0);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    float ms;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    std::printf("launch_interval empty kernels back to back: %.2f us each\n", ms * 1e3 / nl);
+  }
+  // C
+  {
+    const int blocks = 256;
+    unsigned long long *out;
+    CHECK(hipMalloc(&out, blocks * 8));
+    for (int tr = 0; tr < 2; ++tr) {
+      for (int rep = 0; rep < 3; ++rep) {
+        if (tr)
+          hipLaunchKernelGGL(lds_rate<true>, dim3(blocks), dim3(512), 0, 0, out, sink);
+        else
+          hipLaunchKernelGGL(lds_rate<false>, dim3(blocks), dim3(512), 0, 0, out, sink);
+        CHECK(hipGetLastError());
+        CHECK(hipDeviceSynchronize());
+      }
+      std::vector<unsigned long long> h(blocks);
+      CHECK(hipMemcpy(h.data(), out, blocks * 8, hipMemcpyDeviceToHost));
+      unsigned long long mn = ~0ull, mx = 0;
+      for (auto v : h) {
+        mn = v < mn ? v : mn;
+        mx = v > mx ? v : mx;
+      }
+      const double bytes = 8.0 * LITER * (tr ? 512 : 1024);
+      std::printf("lds_rate %-13s 8 waves: %.1f-%.1f bytes/clock per CU\n", tr ? "ds_read_tr_b64" : "ds_read_b128",
+                  bytes / mx, bytes / mn);
+    }
+    CHECK(hipFree(out));
+  }
+  CHECK(hipFree(sink));
+  return 0;
+}
