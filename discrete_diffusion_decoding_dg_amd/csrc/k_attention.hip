@@ -303,9 +303,12 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
   // u - LAG (its P V done before the barrier) takes tile u + NS - LAG
   auto sync_tile = [&](int u) __attribute__((always_inline)) {
     if constexpr (PIPE) {
-      // direct loads are pending only for the first NS - LAG tiles; later
-      // tiles were written to LDS by this wave before the barrier
-      if (u < tile0 + NS - LAG) wait_vmcnt_steps<MINL, NS - 1 - LAG>(tile0 + NS - LAG - 1 - u);
+      // direct loads are pending only for the first NS - LAG tiles (fewer
+      // when the split is shorter); later tiles were written to LDS by this
+      // wave before the barrier. Tile u has landed once at most the loads of
+      // the direct-load tiles issued after it are outstanding.
+      const int last_direct = (tile0 + NS - LAG < tile_end ? tile0 + NS - LAG : tile_end) - 1;
+      if (u <= last_direct) wait_vmcnt_steps<MINL, NS - 1 - LAG>(last_direct - u);
       __syncthreads();
       kvgo = u + NS - LAG < tile_end;
       if (kvgo) load_regs(u + NS - LAG);

@@ -210,12 +210,17 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
   // holding row l & 15, piece l >> 4 of each chunk (the score A operand)
   const uint32_t a_off = static_cast<uint32_t>(eoff(lane & 15, 8 * (lane >> 4)));
   bf16x8 ereg[NBUF == 1 ? NKS : 1];
-  auto load_tile_regs = [&](int tile) {
+  auto load_tile_regs = [&](int tile) __attribute__((always_inline)) {
     const uint8_t *tb = reinterpret_cast<const uint8_t *>(
         a.E + (static_cast<int64_t>(tile) * (a.d / 32) + dcol0 / 32) * (VT * 32));
 #pragma unroll
     for (int c = 0; c < NKS; ++c) ereg[c] = *reinterpret_cast<const bf16x8 *>(tb + c * CHUNK_B + a_off);
   };
+  // a CU accepts about 71 B/clk of load requests and a wave waits at issue
+  // until its own are taken: the epilogue waves (16-row blocks: 16 x 16
+  // lanes are four waves) request the next tile before the barrier, the
+  // others while the epilogue runs, so that each burst is half a tile
+  constexpr int EPW = MT * VT / 64;
   if (t_begin < t_end) {
     if constexpr (NBUF == 2) {
 #pragma unroll
@@ -343,9 +348,12 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
 #pragma unroll
       for (int c = 0; c < NKS; ++c)
         *reinterpret_cast<bf16x8 *>(eb + c * CHUNK_B + a_off) = ereg[c];
-      if (more) load_tile_regs(tile + 1);
+      if (more && wave < EPW) load_tile_regs(tile + 1);
     }
     __syncthreads();
+    if constexpr (NBUF == 1) {
+      if (more && wave >= EPW) load_tile_regs(tile + 1);
+    }
 
     // ---- epilogue: one lane per (row er, id v0 + j)
     if (epi) {
