@@ -29,8 +29,6 @@
 // fills one piece for all 64 keys; the XOR keeps the score-operand reads (32
 // keys of one piece) and the transposed 4-key reads of V free of bank
 // conflicts for 32 and 64 banks, for any head dimension.
-#include <type_traits>
-
 #include "dg_device.hpp"
 #include "dg_kernels.hpp"
 
@@ -245,16 +243,7 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
   // would wait for every outstanding load (vmcnt 0) before the first score
   // MFMA of each tile, which would drain the pipeline every tile
   wait_vmcnt<0>();
-  // Software pipeline (PIPE): iteration t issues the scores of tile t + 1
-  // next to the softmax of tile t (the MFMAs run while the VALU
-  // exponentiates), then O += P V for tile t. Tiles t and t + 1 are in use
-  // during iteration t, so the loads issued at its barrier go to the stage of
-  // tile t - 1, and NS - 2 tiles are requested ahead. Without PIPE (head dims
-  // above 128, whose registers do not hold a second score tile) iteration t
-  // computes the scores of tile t itself and NS - 1 tiles are requested ahead.
-  constexpr bool PIPE = HD <= 128;
-  constexpr int LAG = PIPE ? 2 : 1;   // stages in use besides those loading
-  for (int t = tile0; t < tile_end && t < tile0 + NS - LAG; ++t) issue_tile(t);
+  for (int t = tile0; t < tile_end && t < tile0 + NS - 1; ++t) issue_tile(t);
 
   f32x16 oacc[NB];
 #pragma unroll
@@ -264,259 +253,125 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
   const int tr_key = 4 * (g4 >> 1) + ((lane & 15) >> 2);
   const int tr_col = 16 * (g4 & 1) + 4 * (lane & 3);
 
-  // With PIPE the tiles after the first NS - LAG do not come by direct
-  // global->LDS loads: a wave that issues one of those stalls until the load
-  // path has accepted it (measured: about 1K clocks per tile and wave). Each
-  // wave instead loads its pieces of the tile into registers at the barrier
-  // and writes them to the free stage at the end of the iteration; the next
-  // barrier publishes them.
-  bf16x8 kvreg[MAXL];
-  uint32_t kvdst[MAXL];
-  bool kvgo = false;
-  auto load_regs = [&](int tile) __attribute__((always_inline)) {
-    const uint32_t st = (tile % NS) * 2 * TILE_B;
+  for (int tile = tile0; tile < tile_end; ++tile) {
+    // this wave's loads of `tile` have landed once at most those of the
+    // tiles issued after it are outstanding (MINL or MINL + 1 per tile and
+    // wave; MINL is the safe bound); the barrier makes every wave's loads
+    // visible and frees the stage read during the previous tile
+    int after = tile_end - 1 - tile;
+    if (after > NS - 2) after = NS - 2;
+    wait_vmcnt_steps<MINL, NS - 2>(after);
+    __syncthreads();
+    if (tile + NS - 1 < tile_end) issue_tile(tile + NS - 1);
+    const uint8_t *Ks = stage_mem + (tile % NS) * 2 * TILE_B;
+    const uint8_t *Vs = Ks + TILE_B;
+
+    // ---- S^T for 64 keys (two 32-key blocks); SCH accumulator chains per
+    // block shorten the MFMA dependency chains where registers allow
+    constexpr int SCH = (HD > 128) ? 1 : 2;
+    f32x16 sacc[2][2];
 #pragma unroll
-    for (int n = 0; n < MAXL; ++n) {
-      const int u = wave + n * NWA;
-      if (u < NDMA) {
-        const int tensor = u >= NPR, p = tensor ? u - NPR : u;
-        // lane i fills slot i of the piece: key i ^ 4 (p & 3) of the tile,
-        // clamped to the last key (keys past the end are masked in the scores)
-        int j = tile * BK + kslot(lane, p);
-        if (j > Lk - 1) j = Lk - 1;
-        const uint16_t *src = (j < a.P)
-                                  ? (tensor ? a.Vp : a.Kp) + kvp_base + static_cast<int64_t>(j) * HD + p * 8
-                                  : (tensor ? a.v : a.k) + kvc_base + static_cast<int64_t>(j - a.P) * HD + p * 8;
-        kvreg[n] = *reinterpret_cast<const bf16x8 *>(src);
-        kvdst[n] = st + tensor * TILE_B + p * BK * 16 + lane * 16;
+    for (int mb = 0; mb < 2; ++mb) {
+      sacc[mb][0] = f32x16{};
+      sacc[mb][1] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int p = 2 * ks + hl;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8 *>(Ks + p * BK * 16 + kslot(mb * 32 + (lane & 31), p) * 16);
+        sacc[mb][ks % SCH] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], sacc[mb][ks % SCH], 0, 0, 0);
       }
     }
-  };
-  auto store_regs = [&]() __attribute__((always_inline)) {
-    if (kvgo) {
+    // element e = 4 jj + i of block mb: key 32 mb + 8 jj + 4 hl + i of this
+    // tile. Raw scores here; the scale folds into the exponent below
+    // (scale_log2 > 0, so the max commutes with it).
+    float sv[2][16];
+    float rmax = -INFINITY;
+    const int kv0 = tile * BK;
 #pragma unroll
-      for (int n = 0; n < MAXL; ++n)
-        if (wave + n * NWA < NDMA) *reinterpret_cast<bf16x8 *>(stage_mem + kvdst[n]) = kvreg[n];
-    }
-  };
-  // tile u's loads are visible to every wave after this; the stage of tile
-  // u - LAG (its P V done before the barrier) takes tile u + NS - LAG
-  auto sync_tile = [&](int u) __attribute__((always_inline)) {
-    if constexpr (PIPE) {
-      // direct loads are pending only for the first NS - LAG tiles (fewer
-      // when the split is shorter); later tiles were written to LDS by this
-      // wave before the barrier. Tile u has landed once at most the loads of
-      // the direct-load tiles issued after it are outstanding.
-      const int last_direct = (tile0 + NS - LAG < tile_end ? tile0 + NS - LAG : tile_end) - 1;
-      if (u <= last_direct) wait_vmcnt_steps<MINL, NS - 1 - LAG>(last_direct - u);
-      __syncthreads();
-      kvgo = u + NS - LAG < tile_end;
-      if (kvgo) load_regs(u + NS - LAG);
-    } else {
-      // this wave's loads of tile u have landed once at most those of the
-      // tiles issued after it are outstanding (MINL or MINL + 1 per tile and
-      // wave; MINL is the safe bound)
-      int after = tile_end - 1 - u;
-      if (after > NS - 1 - LAG) after = NS - 1 - LAG;
-      wait_vmcnt_steps<MINL, NS - 1 - LAG>(after);
-      __syncthreads();
-      if (u + NS - LAG < tile_end) issue_tile(u + NS - LAG);
-    }
-  };
-  // K fragment of 16-wide step ks, 32-key block mb of the tile in stage Ks
-  auto kfrag = [&](const uint8_t *Ks, int ks, int mb) __attribute__((always_inline)) -> bf16x8 {
-    const int p = 2 * ks + hl;
-    return *reinterpret_cast<const bf16x8 *>(Ks + p * BK * 16 + kslot(mb * 32 + (lane & 31), p) * 16);
-  };
-  // S^T for the 64 keys of tile u (two 32-key blocks), not interleaved. Element
-  // e = 4 jj + i of block mb: key 32 mb + 8 jj + 4 hl + i of the tile; raw
-  // scores (the scale folds into the exponent: scale_log2 > 0, so the max
-  // commutes with it)
-  auto scores = [&](int u, f32x16 (&sc)[2]) __attribute__((always_inline)) {
-    const uint8_t *Ks = stage_mem + (u % NS) * 2 * TILE_B;
-    sc[0] = f32x16{};
-    sc[1] = f32x16{};
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(Ks, ks, mb), qreg[ks], sc[mb], 0, 0, 0);
-  };
-  // keys past the end, and (causal) canvas keys after this lane's query, drop out
-  auto mask = [&](int u, f32x16 (&sc)[2]) __attribute__((always_inline)) {
-    const int kv0 = u * BK;
-    if (kv0 + BK > Lk) {
+      for (int e = 0; e < 16; ++e) {
+        sv[mb][e] = (SCH == 2) ? sacc[mb][0][e] + sacc[mb][1][e] : sacc[mb][0][e];
+      }
+    if (kv0 + BK > Lk) {   // the last, partial tile: keys past the end drop out
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (kv0 + mb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3) >= Lk) sc[mb][e] = -INFINITY;
+          if (kv0 + mb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3) >= Lk) sv[mb][e] = -INFINITY;
     }
     if constexpr (CAUSAL) {
+      // canvas keys after this lane's query drop out (a whole tile may, for
+      // some queries of the block)
       if (kv0 + BK > a.P + qi + 1) {
         const int last = a.P + qi;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int e = 0; e < 16; ++e)
-            if (kv0 + mb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3) > last) sc[mb][e] = -INFINITY;
+            if (kv0 + mb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3) > last) sv[mb][e] = -INFINITY;
       }
     }
-  };
-  // one probability: P in the k-slot order of the PV contraction, i.e. for
-  // the 16-key step kk (block mb = kk / 2, half kk2 = kk % 2) the A operand is
-  // elements 8 kk2 .. 8 kk2 + 7 of block mb (keys 16 kk + 4 hl + [0, 4) and
-  // 16 kk + 8 + 4 hl + [0, 4))
-  auto prob = [&](float sv) __attribute__((always_inline)) -> float {
-    float p = __builtin_amdgcn_exp2f(fmaf(sv, a.scale_log2, -m_ref));
-    // no visible key yet for this query (whole tiles masked): nothing adds
-    if constexpr (CAUSAL) p = (m_ref == -INFINITY) ? 0.f : p;
-    return p;
-  };
-  // V fragment (B operand, read transposed) of column block nb and 16-key
-  // step kk: source lane S supplies key 16 kk + 4 (g / 2) + j (+ 8 for the
-  // second read) at columns 32 nb + 16 (g % 2) + 4 q, with g = S / 16,
-  // j = (S % 16) / 4, q = S % 4
-  auto vfrag = [&](const uint8_t *Vs, int kk, int nb) __attribute__((always_inline)) -> bf16x8 {
-    const int col = 32 * nb + tr_col;
-    const int p = col >> 3;
-    const uint8_t *pb = Vs + p * BK * 16 + ((col & 7) >> 2) * 8;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4 *)(pb + kslot(16 * kk + tr_key, p) * 16));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4 *)(pb + kslot(16 * kk + 8 + tr_key, p) * 16));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-  // Softmax and O += P V of tile u from its scores cur; with NEXT the scores
-  // of tile u + 1 go to nxt meanwhile. The instruction order is fixed by hand
-  // (scheduling barriers between chunks): each chunk issues two MFMAs and a
-  // share of the softmax's VALU work, with LDS fragments read two chunks
-  // ahead, so one wave's exponentials run under its own MFMAs.
-  auto step = [&](auto next_tag, int u, f32x16 (&cur)[2], f32x16 (&nxt)[2]) __attribute__((always_inline)) {
-    constexpr bool NEXT = decltype(next_tag)::value;
-    if constexpr (NEXT) sync_tile(u + 1);
-    mask(u, cur);
-    // softmax pieces: 0-1 the two blocks' maxima, 2 the reference update, 3-6
-    // the exponentials of block 0 (4 each)
-    float mx0 = -INFINITY, mx1 = -INFINITY, alpha = 1.f, psum = 0.f;
-    float pv0[16];
-    auto piece = [&](int pc) __attribute__((always_inline)) {
-      if (pc == 0) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx0 = fmaxf(mx0, cur[0][e]);
-      } else if (pc == 1) {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx1 = fmaxf(mx1, cur[1][e]);
-      } else if (pc == 2) {
-        // both halves of the wave hold the same 32 queries: lanes l and l ^ 32
-        // exchange their maxima without LDS
-        const float m = fmaxf(mx0, mx1);
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-        const float rmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        const float tmax = rmax * a.scale_log2;
-        // reference update without branches: alpha rescales l and O (1
-        // unless the tile's maximum exceeds the reference by more than 2^8;
-        // 0 on the first tile)
-        const bool up = tmax > m_ref + kSlack;
-        alpha = up ? __builtin_amdgcn_exp2f(m_ref - tmax) : 1.f;
-        m_ref = up ? tmax : m_ref;
-      } else if (pc <= 6) {
-#pragma unroll
-        for (int e = 4 * (pc - 3); e < 4 * (pc - 2); ++e) {
-          pv0[e] = prob(cur[0][e]);
-          psum += pv0[e];
-          // keep the exponential in this chunk (the compiler would otherwise
-          // sink it below the rescale branch, out of the MFMAs' shadow)
-          asm volatile("" ::"v"(pv0[e]));
-        }
+      for (int e = 0; e < 16; ++e) rmax = fmaxf(rmax, sv[mb][e]);
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));   // both halves of the query
+    const float tmax = rmax * a.scale_log2;
+    if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kSlack)) {
+      float alpha = 1.f;
+      if (tmax > m_ref + kSlack) {
+        alpha = __builtin_amdgcn_exp2f(m_ref - tmax);   // 0 on the first tile
+        m_ref = tmax;
       }
-    };
-    if constexpr (NEXT) {
-      const uint8_t *Ks = stage_mem + ((u + 1) % NS) * 2 * TILE_B;
-      bf16x8 kf[KS][2];
-#pragma unroll
-      for (int ks = 0; ks < KS && ks < 2; ++ks) {
-        kf[ks][0] = kfrag(Ks, ks, 0);
-        kf[ks][1] = kfrag(Ks, ks, 1);
-      }
-      nxt[0] = f32x16{};
-      nxt[1] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 2 < KS) {
-          kf[ks + 2][0] = kfrag(Ks, ks + 2, 0);
-          kf[ks + 2][1] = kfrag(Ks, ks + 2, 1);
-        }
-        nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][0], qreg[ks], nxt[0], 0, 0, 0);
-        nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][1], qreg[ks], nxt[1], 0, 0, 0);
-        // pieces [7 ks / KS, 7 (ks + 1) / KS) run in this chunk
-#pragma unroll
-        for (int pc = 7 * ks / KS; pc < 7 * (ks + 1) / KS; ++pc) piece(pc);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-#pragma unroll
-      for (int pc = 0; pc < 7; ++pc) piece(pc);
-    }
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+      l_lane *= alpha;
       // every O^T element of this lane belongs to its own query
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[nb][e] *= alpha;
     }
+    // P in the k-slot order of the PV contraction: for the 16-key step kk
+    // (block mb = kk / 2, half kk2 = kk % 2) the A operand is elements
+    // 8 kk2 .. 8 kk2 + 7 of block mb, i.e. keys 16 kk + 4 hl + [0, 4) and
+    // 16 kk + 8 + 4 hl + [0, 4)
     bf16x8 pa[4];
+    float psum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) pa[e >> 3][e & 7] = static_cast<__bf16>(pv0[e]);
-    // O^T += V^T P^T (the V fragment as A operand, row = head column; P as B
-    // operand, column = query; the k slots are the same as for P V), with
-    // the exponentials of block 1 under the first half
-    const uint8_t *Vs = stage_mem + (u % NS) * 2 * TILE_B + TILE_B;
-    constexpr int NPV = 4 * NB;   // MFMAs: 16-key steps x column blocks
-    bf16x8 vf[NPV];
-    vf[0] = vfrag(Vs, 0, 0);
-    vf[1] = vfrag(Vs, 1 / NB, 1 % NB);
-    float pv1[16];
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      const int kk = i / NB, nb = i % NB;
-      if (i + 2 < NPV) vf[i + 2] = vfrag(Vs, (i + 2) / NB, (i + 2) % NB);
-      if (kk == 2 && nb == 0) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) pa[2 + (e >> 3)][e & 7] = static_cast<__bf16>(pv1[e]);
+      for (int e = 0; e < 16; ++e) {
+        float p = __builtin_amdgcn_exp2f(fmaf(sv[mb][e], a.scale_log2, -m_ref));
+        // no visible key yet for this query (whole tiles masked): nothing adds
+        if constexpr (CAUSAL) p = (m_ref == -INFINITY) ? 0.f : p;
+        psum += p;
+        pa[2 * mb + (e >> 3)][e & 7] = static_cast<__bf16>(p);
       }
-      oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pa[kk], oacc[nb], 0, 0, 0);
-      if (i < 2 * NB) {
-        // exponentials of block 1 spread over the first 2 NB MFMAs
-#pragma unroll
-        for (int e = 16 * i / (2 * NB); e < 16 * (i + 1) / (2 * NB); ++e) {
-          pv1[e] = prob(cur[1][e]);
-          psum += pv1[e];
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (NEXT) store_regs();
-    l_lane = l_lane * alpha + psum;
-  };
+    l_lane += psum;
 
-  if (tile0 < tile_end) {
-    f32x16 sa[2], sb[2];
-    if constexpr (PIPE) {
-      sync_tile(tile0);
-      scores(tile0, sa);
-      store_regs();
-      for (int t = tile0; t + 1 < tile_end; ++t) {
-        step(std::true_type{}, t, sa, sb);
-        sa[0] = sb[0];
-        sa[1] = sb[1];
-      }
-      step(std::false_type{}, tile_end - 1, sa, sb);
-    } else {
-      for (int t = tile0; t < tile_end; ++t) {
-        sync_tile(t);
-        scores(t, sa);
-        step(std::false_type{}, t, sa, sb);
+    // ---- O += P V; the B operand of column block nb and step kk is read
+    // transposed: source lane S supplies key 16 kk + 4 (g / 2) + j (+ 8 for
+    // the second read) at columns 32 nb + 16 (g % 2) + 4 q, with g = S / 16,
+    // j = (S % 16) / 4, q = S % 4
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = 32 * nb + tr_col;
+        const int p = col >> 3;
+        const uint8_t *pb = Vs + p * BK * 16 + ((col & 7) >> 2) * 8;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(pb + kslot(16 * kk + tr_key, p) * 16));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(pb + kslot(16 * kk + 8 + tr_key, p) * 16));
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        // O^T = V^T P^T: the V fragment as A operand (row = head column), P
+        // as B operand (column = query); the k slots are the same as for P V
+        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, pa[kk], oacc[nb], 0, 0, 0);
       }
     }
   }
