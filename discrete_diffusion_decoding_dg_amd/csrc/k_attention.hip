@@ -138,7 +138,12 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
   using G_ = Geo<HD>;
   constexpr int HDP = G_::HDP, NPC = G_::NPC, NPR = G_::NPR, KS = G_::KS, NB = G_::NB;
   constexpr int TILE_B = G_::TILE_B, NS = G_::NS, NDMA = G_::NDMA;
-  constexpr int MAXL = (NDMA + NWA - 1) / NWA;   // loads per wave and tile, at most
+  // With 8 waves only the first four issue the direct loads: each SIMD's
+  // older wave, which otherwise waits at the barrier for the younger one,
+  // takes the stall of issuing them (a CU accepts about 71 B/clk of load
+  // requests, and the issuing wave waits until its own are taken)
+  constexpr int LW = (NWA == 8) ? 4 : NWA;       // waves that issue loads
+  constexpr int MAXL = (NDMA + LW - 1) / LW;     // loads per loading wave and tile, at most
   __shared__ __attribute__((aligned(16))) uint8_t stage_mem[NS * 2 * TILE_B];
   // LDS byte address of the stage (the M0 operand of the direct loads)
   const uint32_t stage_lds = static_cast<uint32_t>(
@@ -196,8 +201,8 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
   if (tile_end > total_tiles) tile_end = total_tiles;
 
   // direct loads of one tile: load u in [0, NDMA) fills piece u % NPR of K
-  // (u < NPR) or of V; wave w issues loads w, w + NWA, ...
-  constexpr int MINL = NDMA / NWA;               // loads per wave and tile, at least
+  // (u < NPR) or of V; wave w < LW issues loads w, w + LW, ...
+  constexpr int MINL = NDMA / LW;                // loads per loading wave and tile, at least
   // byte offset of this lane's key row inside a tile, for each piece phase
   uint32_t koff[4];
 #pragma unroll
@@ -214,8 +219,8 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
                                : a.v + kvc_base + static_cast<int64_t>(j0 - a.P) * HD;
 #pragma unroll
       for (int n = 0; n < MAXL; ++n) {
-        const int u = wave + n * NWA;
-        if (u < NDMA) {
+        const int u = wave + n * LW;
+        if (wave < LW && u < NDMA) {
           const int tensor = u >= NPR, p = tensor ? u - NPR : u;
           lds_dma16_sa((tensor ? vb : kb) + p * 8, koff[p & 3], st + tensor * TILE_B + p * BK * 16);
         }
@@ -224,8 +229,8 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int n = 0; n < MAXL; ++n) {
-      const int u = wave + n * NWA;
-      if (u < NDMA) {
+      const int u = wave + n * LW;
+      if (wave < LW && u < NDMA) {
         const int tensor = u >= NPR, p = tensor ? u - NPR : u;
         // lane i fills slot i of the piece: key i ^ 4 (p & 3) of the tile,
         // clamped to the last key (keys past the end are masked in the scores)
@@ -255,9 +260,10 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
 
   for (int tile = tile0; tile < tile_end; ++tile) {
     // this wave's loads of `tile` have landed once at most those of the
-    // tiles issued after it are outstanding (MINL or MINL + 1 per tile and
-    // wave; MINL is the safe bound); the barrier makes every wave's loads
-    // visible and frees the stage read during the previous tile
+    // tiles issued after it are outstanding (MINL or MINL + 1 per tile for a
+    // loading wave, none for the others; MINL is the safe bound); the barrier
+    // makes every wave's loads visible and frees the stage read during the
+    // previous tile
     int after = tile_end - 1 - tile;
     if (after > NS - 2) after = NS - 2;
     wait_vmcnt_steps<MINL, NS - 2>(after);
