@@ -395,6 +395,30 @@ def main():
     torch.cuda.synchronize()
     gen_ms = g0.elapsed_time(g1)
 
+    # one step captured into a HIP graph and replayed K times (the replays
+    # repeat the captured arguments: the same t and seed every time), for
+    # comparison with the launched steps; not part of `value`
+    gxo, gzo = torch.empty_like(x), torch.empty_like(z)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dg.dg_denoise_step(model, xs[0], zs[0], Kp, Vp, tvec(0), dt, 1000, gxo, gzo)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dg.dg_denoise_step(model, xs[0], zs[0], Kp, Vp, tvec(0), dt, 1000, gxo, gzo)
+    graph.replay()
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    r1.record()
+    torch.cuda.synchronize()
+    graph_ms = r0.elapsed_time(r1) / args.steps
+    del graph, gxo, gzo
+
     # the entropy-bounded step (the pages' recommended sampler) on the same
     # workload: per-step time, and adaptive generation with at most 48 steps
     # (thresholds in nats; with random weights the entropies sit near ln V, so
@@ -605,6 +629,7 @@ def main():
         "step_tflops": fl["total"] / (ms_per_step * 1e-3) / 1e12,
         "step_frac_mfma": fl["total"] / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "generate_canvas_ms": gen_ms,
+        "graph_replay_ms_per_step": graph_ms,
         "ms_per_step_with_lmhead_events": ms_per_step_profiled,
         "step_ms_distribution": step_dist,
         "roofline": {"bound": "mfma", "kernel": "lmhead_kernel", "achieved": achieved,
