@@ -182,7 +182,6 @@ __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restri
       }
     } else if (active) {
       const ZP *zp = zpart + rowoff + c0;
-#pragma unroll 8
       for (int sp = q; sp < splits; sp += groups) {
         float v[kCols];
         load8(zp + sp * sstride, v);
