@@ -408,7 +408,24 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
     }
     __syncthreads();
 
-    // ---- z += P E over this wave's slice
+    // ---- z += P E over this wave's slice. The P operand and the first
+    // chunk's E operand are requested before the rescale flag is examined
+    // (independent LDS reads: one round trip instead of two)
+    constexpr int NPF = (MT == 32) ? 1 : 0;   // prefetched chunks
+    bf16x8 pa32{};
+    bf16x8 bpf[NPF > 0 ? NPF : 1];
+    if constexpr (MT == 32) {
+      pa32 = *reinterpret_cast<const bf16x8 *>(Pb + poff<MT>(lane & 31, 8 * (lane >> 5)));
+#pragma unroll
+      for (int c = 0; c < NPF; ++c) {
+        const uint8_t *ch = eb + c * CHUNK_B;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(ch + eoff(tr_row, tr_col)));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(ch + eoff(tr_row + 4, tr_col)));
+        bpf[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
     if (__builtin_amdgcn_readfirstlane(last_resc) == tile) {
       if constexpr (MT == 32) {
         f32x4 f[4];
@@ -430,16 +447,21 @@ __global__ void __launch_bounds__(512) lmhead_kernel(LmArgs a, int rblocks) {
     }
     if constexpr (MT == 32) {
       // A operand: row lane & 31, ids 8 (lane >> 5) + [0, 8)
-      const bf16x8 pa = *reinterpret_cast<const bf16x8 *>(Pb + poff<MT>(lane & 31, 8 * (lane >> 5)));
+      const bf16x8 pa = pa32;
 #pragma unroll
       for (int c = 0; c < NKS; ++c) {
-        const uint8_t *ch = eb + c * CHUNK_B;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)(ch + eoff(tr_row, tr_col)));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)(ch + eoff(tr_row + 4, tr_col)));
-        // B operand: column lane & 31 of the chunk, ids 8 (lane >> 5) + [0, 8)
-        const bf16x8 b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        bf16x8 b;
+        if (c < NPF) {
+          b = bpf[c < NPF ? c : 0];
+        } else {
+          const uint8_t *ch = eb + c * CHUNK_B;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4 *)(ch + eoff(tr_row, tr_col)));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4 *)(ch + eoff(tr_row + 4, tr_col)));
+          // B operand: column lane & 31 of the chunk, ids 8 (lane >> 5) + [0, 8)
+          b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
         zacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, b, zacc[c], 0, 0, 0);
       }
     } else {
