@@ -22,6 +22,12 @@
 // ...) over a strip of 512 columns, whose sums meet in LDS; with few, one
 // group over 2048 columns.
 // z partials are bf16 from the MFMA LM head and fp32 from the fp32 path.
+//
+// Up to 32 bf16 splits (every MFMA workload here) take a second kernel: each
+// lane merges all splits of its 8 columns, so the partial sums never meet in
+// LDS and no barrier is needed; the split statistics are reduced with DPP
+// and lane-swap instructions instead of LDS permutes, and an exact tie of
+// the Gumbel maxima is resolved with one ballot.
 #include "dg_device.hpp"
 #include "dg_kernels.hpp"
 
@@ -60,6 +66,56 @@ __device__ __forceinline__ float load1(const float *p) { return *p; }
 __device__ __forceinline__ float load1(const uint16_t *p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ float lane_value(float v, int s) {   // s wave-uniform
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), s));
+}
+
+// ---- wave-wide reductions without LDS: DPP within rows of 16 lanes (quad
+// swaps, then the half-row and row mirrors), then the gfx950 row and half
+// swaps (v_permlane16_swap, v_permlane32_swap); every lane gets the result
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1, 0, 3, 2]
+constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2, 3, 0, 1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+__device__ __forceinline__ float swap_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float swap_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float wave_max_x(float v) {
+  v = fmaxf(v, dpp<kQuadSwap1>(v));
+  v = fmaxf(v, dpp<kQuadSwap2>(v));
+  v = fmaxf(v, dpp<kRowHalfMirror>(v));
+  v = fmaxf(v, dpp<kRowMirror>(v));
+  return swap_max(v);
+}
+__device__ __forceinline__ float wave_sum_x(float v) {
+  v += dpp<kQuadSwap1>(v);
+  v += dpp<kQuadSwap2>(v);
+  v += dpp<kRowHalfMirror>(v);
+  v += dpp<kRowMirror>(v);
+  return swap_sum(v);
+}
+// word 3 of a raw buffer resource on gfx950 (32-bit data format, no
+// swizzle); loads past the stated size return zero
+constexpr int kBufferFlags = 0x00020000;
+// id of the lowest lane whose candidate (valid, value) attains the wave's
+// maximum value, read from `id` on that lane; -1 if no lane is valid
+__device__ __forceinline__ int wave_argmax_lowest(bool valid, float value, int id) {
+  const float v = valid ? value : -INFINITY;
+  const float mx = wave_max_x(v);
+  const uint64_t hit = __ballot(valid && v == mx);
+  if (hit == 0) return -1;
+  return __builtin_amdgcn_readlane(id, static_cast<int>(__builtin_ctzll(hit)));
 }
 
 // NPRE: bf16 partial loads per thread issued before the split statistics are
@@ -219,6 +275,117 @@ __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restri
   }
 }
 
+
+// At most 32 bf16 splits, d % 8 == 0. Grid (row, group of 2048 columns);
+// lane (wave w, l) of block (r, y) owns columns 8 (64 (4 y + w) + l) + [0, 8)
+// of row r and sums every split of them in split order. Every wave reduces
+// the row's split statistics itself (lane s holds split s); wave 0 of the
+// first column group also writes the per-row results. NP >= splits: the
+// row records are requested first and then NP partial loads (the surplus
+// ones re-read the last split and are not summed), so the statistics are
+// reduced while the partials are in flight.
+template <int NP>
+__global__ void __launch_bounds__(256) combine_wide_kernel(const RowPartial *__restrict__ part,
+                                                           const uint16_t *__restrict__ zpart, int splits,
+                                                           const int32_t *__restrict__ x_t,
+                                                           const StepParams *__restrict__ prm, int R,
+                                                           int C, int d, uint32_t k0, uint32_t k1,
+                                                           int32_t *__restrict__ x_out,
+                                                           uint16_t *__restrict__ z_out,
+                                                           float *__restrict__ lse,
+                                                           int32_t *__restrict__ best, EntropyRows ent,
+                                                           const int32_t *__restrict__ frozen,
+                                                           const uint16_t *__restrict__ z_t) {
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cr = ((blockIdx.y * 4 + wave) * 64 + lane) * kCols;
+  const bool active = cr + kCols <= d;
+  const int c0 = active ? cr : 0;   // inactive lanes read valid addresses and store nothing
+  const int64_t rowoff = static_cast<int64_t>(r) * d;
+  RowPartial p;
+  p.m = -INFINITY;
+  p.l = 0.f;
+  p.best = -INFINITY;
+  p.arg = -1;
+  p.s1 = 0.f;
+  p.dbest = -INFINITY;
+  p.darg = -1;
+  p.pad = 0;
+  const bool has = lane < splits;
+  if (has) p = part[static_cast<int64_t>(lane) * R + r];
+  // buffer loads: the partials as one buffer resource (all splits hold fewer
+  // than 2^31 bytes), the split's byte offset in a scalar register and the
+  // lane's in a vector register, so no 64-bit address is formed per load
+  const int sbytes = R * d * 2;
+  const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(zpart), 0, splits * sbytes, kBufferFlags);
+  const int loff = static_cast<int>((rowoff + c0) * 2);
+  uint4 raw[NP];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const int sp = k < splits ? k : splits - 1;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(zr, loff, sp * sbytes, 0);
+    raw[k] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  if (frozen && frozen[r / C]) {
+    // a stopped canvas keeps its self-conditioning signal
+    if (active)
+      *reinterpret_cast<uint4 *>(z_out + rowoff + c0) = *reinterpret_cast<const uint4 *>(z_t + rowoff + c0);
+    return;
+  }
+  // the row's Bernoulli decision while the loads are in flight
+  const bool head = blockIdx.y == 0 && wave == 0;
+  bool rs = false;
+  if (head && !ent.H) {
+    const int b = r / C, i = r - b * C;
+    const u32x4 u = philox4x32_10(0u, static_cast<uint32_t>(i), static_cast<uint32_t>(b),
+                                  kStreamBernoulli, k0, k1);
+    rs = u01(u.x) < prm[b].lam;
+  }
+  const float M = wave_max_x(p.m);
+  const float w = has ? exp2f(p.m - M) : 0.f;
+  const float L = wave_sum_x(w * p.l);
+  if (head) {
+    // the Gumbel draw over splits (an exact tie goes to the lower split)
+    const int y = wave_argmax_lowest(has && p.arg >= 0, p.best, p.arg);
+    if (ent.H) {
+      const float S1 = wave_sum_x((has && p.l > 0.f) ? w * (p.s1 + (p.m - M) * p.l) : 0.f);
+      const int det = wave_argmax_lowest(has && p.darg >= 0, p.dbest, p.darg);
+      if (lane == 0) {
+        ent.H[r] = 0.6931471805599453f * (log2f(L) - S1 / L);
+        ent.y[r] = y;
+        ent.det[r] = det;
+        if (lse) lse[r] = (M + log2f(L)) * 0.6931471805599453f;
+        if (best) best[r] = y;
+      }
+    } else if (lane == 0) {
+      x_out[r] = rs ? y : x_t[r];
+      if (lse) lse[r] = (M + log2f(L)) * 0.6931471805599453f;
+      if (best) best[r] = rs ? y : -1;
+    }
+  }
+  if (!active) return;
+  float acc[kCols];
+#pragma unroll
+  for (int i = 0; i < kCols; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    if (k < splits) {
+      const float ws = lane_value(w, k);
+      const uint32_t wd[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += ws * __uint_as_float(wd[i] << 16);
+        acc[2 * i + 1] += ws * __uint_as_float(wd[i] & 0xFFFF0000u);
+      }
+    }
+  }
+  const float il = 1.f / L;
+#pragma unroll
+  for (int i = 0; i < kCols; ++i) acc[i] *= il;
+  store8(z_out + rowoff + c0, acc);
+}
+
 }  // namespace
 
 hipError_t launch_combine(bool bf16, const void *work, int splits, const int32_t *x_t,
@@ -237,6 +404,33 @@ hipError_t launch_combine(bool bf16, const void *work, int splits, const int32_t
   const dim3 grid(R, (s.d + strip - 1) / strip);
   const EntropyRows er = ent ? *ent : EntropyRows{nullptr, nullptr, nullptr};
   if (frozen && !z_t) return hipErrorInvalidValue;
+  // 16-byte rows: z_out and z_t (and the partials, carved at 256-byte
+  // offsets of the workspace) take 16-byte accesses at every 8th column
+  const bool aligned16 = ((reinterpret_cast<uintptr_t>(z_out) | reinterpret_cast<uintptr_t>(z_t) |
+                           reinterpret_cast<uintptr_t>(zbase)) & 15) == 0;
+  const bool fits31 = static_cast<int64_t>(splits) * R * s.d * 2 < (int64_t{1} << 31);
+  if (bf16 && s.d % kCols == 0 && splits <= 32 && aligned16 && fits31) {
+    const dim3 wgrid(R, (s.d + 4 * 64 * kCols - 1) / (4 * 64 * kCols));
+#define DG_WIDE(NP)                                                                                   \
+  hipLaunchKernelGGL((combine_wide_kernel<NP>), wgrid, dim3(256), 0, st, part,                        \
+                     reinterpret_cast<const uint16_t *>(zbase), splits, x_t, prm, R, s.C, s.d, k0, k1, \
+                     x_out, static_cast<uint16_t *>(z_out), lse, best, er, frozen,                    \
+                     static_cast<const uint16_t *>(z_t))
+    if (splits <= 1)
+      DG_WIDE(1);
+    else if (splits <= 2)
+      DG_WIDE(2);
+    else if (splits <= 4)
+      DG_WIDE(4);
+    else if (splits <= 8)
+      DG_WIDE(8);
+    else if (splits <= 16)
+      DG_WIDE(16);
+    else
+      DG_WIDE(32);
+#undef DG_WIDE
+    return hipGetLastError();
+  }
   // bf16 partials with d % 8 == 0 are prefetched: 8 or 16 loads per thread
   const int per_group = (splits + groups - 1) / groups;
   const bool pre = bf16 && s.d % kCols == 0 && per_group <= 16;
