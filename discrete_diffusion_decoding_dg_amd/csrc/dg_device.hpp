@@ -95,6 +95,10 @@ __device__ __forceinline__ float gumbel(uint32_t w) {
 
 enum : uint32_t { kStreamGumbel = 0, kStreamBernoulli = 1, kStreamCorrupt = 2 };
 
+// word 3 of a raw buffer resource on gfx950 (32-bit data format, no
+// swizzle); loads past the resource's size return zero
+constexpr int kBufferFlags = 0x00020000;
+
 // Gumbel-stream counter layout: vocabulary id v uses word (v >> 4) & 3 of
 // block 16 (v >> 6) + (v & 15), so block j of each aligned group of 64 ids
 // serves ids j, j + 16, j + 32, j + 48.

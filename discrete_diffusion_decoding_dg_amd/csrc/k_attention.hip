@@ -489,6 +489,61 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const uint16_t *__res
   }
 }
 
+// hd % 8 == 0, at most 16 splits: one thread per 8 consecutive columns of a
+// (row, head) pair, NP == splits (exact instantiations). The (m, l) records
+// are requested first, then the partials as 16-byte buffer loads (one
+// resource, the split offset in a scalar register), all before the maximum;
+// up to 128 registers per lane keep every load in flight.
+template <int NP>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) attn_combine_wide_kernel(const uint16_t *__restrict__ opart,
+                                                                const float2 *__restrict__ ml,
+                                                                int64_t rows, int hd,
+                                                                uint16_t *__restrict__ o) {
+  // rows * hd < 2^30 (the launch checks that all splits hold < 2^31 bytes)
+  const int q8 = hd / 8;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= static_cast<int>(rows) * q8) return;
+  const int row = t / q8;
+  const int idx = row * hd + 8 * (t - row * q8);
+  const int sbytes = static_cast<int>(rows) * hd * 2;
+  const __amdgpu_buffer_rsrc_t pr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(opart), 0, NP * sbytes, kBufferFlags);
+  float2 mr[NP];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) mr[k] = ml[k * rows + row];   // < 2^31 records
+  uint32_t xr[NP][4];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(pr, idx * 2, k * sbytes, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr[k][i] = v[i];
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NP; ++k) M = fmaxf(M, mr[k].x);
+  float num[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) num[i] = 0.f;
+  float den = 0.f;
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const float w = exp2f(mr[k].x - M);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      num[2 * i] += w * __uint_as_float(xr[k][i] << 16);
+      num[2 * i + 1] += w * __uint_as_float(xr[k][i] & 0xFFFF0000u);
+    }
+    den += w * mr[k].y;
+  }
+  const float inv = 1.f / den;
+  uint4 out;
+  out.x = pack_bf16x2(num[0] * inv, num[1] * inv);
+  out.y = pack_bf16x2(num[2] * inv, num[3] * inv);
+  out.z = pack_bf16x2(num[4] * inv, num[5] * inv);
+  out.w = pack_bf16x2(num[6] * inv, num[7] * inv);
+  *reinterpret_cast<uint4 *>(o + idx) = out;
+}
+
 void plan_waves(const Shape &s, int nwa, int &splits, int &tps) {
   const int bq = nwa * 32;
   const int tiles = (s.P + s.C + BK - 1) / BK;
@@ -568,6 +623,23 @@ hipError_t launch_attention_bf16(const uint16_t *q, const uint16_t *k, const uin
 #undef DG_ATT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
+  const bool fits31 = static_cast<int64_t>(a.splits) * rows * s.hd * 2 < (int64_t{1} << 31);
+  const bool aligned16 = ((reinterpret_cast<uintptr_t>(a.opart) | reinterpret_cast<uintptr_t>(o)) & 15) == 0;
+  if (s.hd % 8 == 0 && a.splits <= 16 && fits31 && aligned16) {
+    const int64_t total8 = static_cast<int64_t>(rows) * (s.hd / 8);
+    const dim3 wgrid(static_cast<uint32_t>((total8 + 255) / 256));
+#define DG_ACW(NP_)                                                                              \
+  case NP_:                                                                                      \
+    hipLaunchKernelGGL(attn_combine_wide_kernel<NP_>, wgrid, dim3(256), 0, st, a.opart, a.ml,    \
+                       static_cast<int64_t>(rows), s.hd, o);                                     \
+    return hipGetLastError();
+    switch (a.splits) {
+      DG_ACW(2) DG_ACW(3) DG_ACW(4) DG_ACW(5) DG_ACW(6) DG_ACW(7) DG_ACW(8) DG_ACW(9) DG_ACW(10)
+      DG_ACW(11) DG_ACW(12) DG_ACW(13) DG_ACW(14) DG_ACW(15) DG_ACW(16)
+      default: break;
+    }
+#undef DG_ACW
+  }
   const int64_t total4 = static_cast<int64_t>(rows) * (s.hd / 4);
   int64_t blocks = (total4 + 255) / 256;
   if (blocks > 8192) blocks = 8192;

@@ -105,9 +105,6 @@ __device__ __forceinline__ float wave_sum_x(float v) {
   v += dpp<kRowMirror>(v);
   return swap_sum(v);
 }
-// word 3 of a raw buffer resource on gfx950 (32-bit data format, no
-// swizzle); loads past the stated size return zero
-constexpr int kBufferFlags = 0x00020000;
 // id of the lowest lane whose candidate (valid, value) attains the wave's
 // maximum value, read from `id` on that lane; -1 if no lane is valid
 __device__ __forceinline__ int wave_argmax_lowest(bool valid, float value, int id) {
