@@ -24,11 +24,24 @@ constexpr int BM = 64, BN = 64, BK = 64;
 constexpr int PAD = 8;                  // bf16 elements of row padding in LDS
 constexpr int LDW = BK + PAD;           // LDS row pitch (elements)
 
+// Eight fp32 values rounded to bf16 and packed for one 16-byte store.
+__device__ __forceinline__ uint4 pack8(const float (&a)[8]) {
+  return make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]),
+                    pack_bf16x2(a[6], a[7]));
+}
+__device__ __forceinline__ bool aligned16(const void *p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+}
+
 // Where row n of the virtual B matrix comes from, and where C goes.
 // kPair: the tile's output columns come in gate/up pairs (see GegluEpi) and
 // are stored through store_pair(m, n, gate, up) instead of store(m, n, acc).
+// kVec8: store8(m, n, a) writes columns n .. n + 7 (n % 8 == 0) of row m as
+// one 16-byte access with the same rounding as store(), whenever vec8_ok()
+// (every column group of 8 then stays within one destination row segment).
 struct QkvEpi {
   static constexpr bool kPair = false;
+  static constexpr bool kVec8 = true;
   const uint16_t *Wq, *Wk, *Wv;
   uint16_t *q, *k, *v;
   int Nq, Nkv, C, Hkv, hd;
@@ -55,10 +68,30 @@ struct QkvEpi {
     const int g = n / hd, e = n - g * hd;
     dst[((static_cast<int64_t>(b) * Hkv + g) * C + i) * hd + e] = val;
   }
+  __device__ bool vec8_ok() const {
+    return ((Nq | Nkv | hd) & 7) == 0 && aligned16(q) && aligned16(k) && aligned16(v);
+  }
+  __device__ void store8(int m, int n, const float (&a)[8]) const {
+    const uint4 val = pack8(a);
+    if (n < Nq) {
+      *reinterpret_cast<uint4 *>(q + static_cast<int64_t>(m) * Nq + n) = val;
+      return;
+    }
+    n -= Nq;
+    uint16_t *dst = k;
+    if (n >= Nkv) {
+      n -= Nkv;
+      dst = v;
+    }
+    const int b = m / C, i = m - b * C;
+    const int g = n / hd, e = n - g * hd;
+    *reinterpret_cast<uint4 *>(dst + ((static_cast<int64_t>(b) * Hkv + g) * C + i) * hd + e) = val;
+  }
 };
 
 struct ResidualEpi {
   static constexpr bool kPair = false;
+  static constexpr bool kVec8 = true;
   const uint16_t *W;
   const uint16_t *res;
   uint16_t *out;
@@ -68,6 +101,19 @@ struct ResidualEpi {
     const int64_t idx = static_cast<int64_t>(m) * N + n;
     out[idx] = f32_to_bf16(bf16_to_f32(res[idx]) + acc);
   }
+  __device__ bool vec8_ok() const { return (N & 7) == 0 && aligned16(res) && aligned16(out); }
+  __device__ void store8(int m, int n, const float (&a)[8]) const {
+    const int64_t idx = static_cast<int64_t>(m) * N + n;
+    const uint4 r = *reinterpret_cast<const uint4 *>(res + idx);
+    const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = bf16_to_f32(static_cast<uint16_t>(rw[i] & 0xFFFFu)) + a[2 * i];
+      o[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(rw[i] >> 16)) + a[2 * i + 1];
+    }
+    *reinterpret_cast<uint4 *>(out + idx) = pack8(o);
+  }
 };
 
 // Encoder cache entries: rows m = b * n + i of the token embeddings, columns
@@ -75,6 +121,7 @@ struct ResidualEpi {
 // row pos + i of the (b, kv head) slices of the caches [B, Hkv, Pst, hd].
 struct KvCacheEpi {
   static constexpr bool kPair = false;
+  static constexpr bool kVec8 = true;
   const uint16_t *Wk, *Wv;
   uint16_t *K, *V;
   int Nkv, n, pos, Pst, Hkv, hd;
@@ -91,11 +138,23 @@ struct KvCacheEpi {
     const int g = c / hd, e = c - g * hd;
     dst[((static_cast<int64_t>(b) * Hkv + g) * Pst + pos + i) * hd + e] = f32_to_bf16(acc);
   }
+  __device__ bool vec8_ok() const { return ((Nkv | hd) & 7) == 0 && aligned16(K) && aligned16(V); }
+  __device__ void store8(int m, int c, const float (&a)[8]) const {
+    uint16_t *dst = K;
+    if (c >= Nkv) {
+      c -= Nkv;
+      dst = V;
+    }
+    const int b = m / n, i = m - b * n;
+    const int g = c / hd, e = c - g * hd;
+    *reinterpret_cast<uint4 *>(dst + ((static_cast<int64_t>(b) * Hkv + g) * Pst + pos + i) * hd + e) = pack8(a);
+  }
 };
 
 // Plain fp32 store of C = A B^T [M, N] (expert down projections).
 struct F32StoreEpi {
   static constexpr bool kPair = false;
+  static constexpr bool kVec8 = false;
   const uint16_t *W;
   float *out;
   int N;
@@ -110,6 +169,7 @@ struct F32StoreEpi {
 // same units sit side by side in every tile. hid[m, f] = round(gelu(g) * u).
 struct GegluEpi {
   static constexpr bool kPair = true;
+  static constexpr bool kVec8 = false;
   const uint16_t *W;
   uint16_t *hid;
   int F;
@@ -125,6 +185,7 @@ struct GegluEpi {
 // canvases marked in `frozen` (nullable) copy z_t instead.
 struct DownEpi {
   static constexpr bool kPair = false;
+  static constexpr bool kVec8 = true;
   const uint16_t *W;
   uint16_t *out;
   const uint16_t *zt;
@@ -134,6 +195,12 @@ struct DownEpi {
   __device__ void store(int m, int n, float acc) const {
     const int64_t idx = static_cast<int64_t>(m) * N + n;
     out[idx] = (frozen && frozen[m / C]) ? zt[idx] : f32_to_bf16(acc);
+  }
+  __device__ bool vec8_ok() const { return (N & 7) == 0 && aligned16(out) && aligned16(zt); }
+  __device__ void store8(int m, int n, const float (&a)[8]) const {
+    const int64_t idx = static_cast<int64_t>(m) * N + n;
+    *reinterpret_cast<uint4 *>(out + idx) =
+        (frozen && frozen[m / C]) ? *reinterpret_cast<const uint4 *>(zt + idx) : pack8(a);
   }
 };
 
@@ -735,6 +802,46 @@ __global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__rest
       if (m >= 0 && n < N) epi.store_pair(m, n, sum8(r, col), sum8(r, col + 32));
     }
   } else {
+    if constexpr (Epi::kVec8) {
+      if ((N & 7) == 0 && epi.vec8_ok()) {
+        // one thread per 8 consecutive columns of a tile row: 16-byte
+        // partial reads, one destination computation and one 16-byte store;
+        // the partials are summed in the same order as sum8
+        for (int e = tid; e < BMT * BN / 8; e += 512) {
+          const int r = e / (BN / 8), col = 8 * (e - r * (BN / 8));
+          const int m = rows.out(r), n = n0 + col;
+          if (m < 0 || n >= N) continue;
+          float a[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a[i] = 0.f;
+          const float *base;
+          int nw, wstride;
+          if constexpr (BMT == BM) {
+            base = red + r * PITCH + col;
+            nw = 8;
+            wstride = BM * PITCH;
+          } else {
+            base = red + (r >> 6) * 4 * BM * PITCH + (r & 63) * PITCH + col;
+            nw = 4;
+            wstride = BM * PITCH;
+          }
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            if (w < nw) {
+              const f32x4 lo = *reinterpret_cast<const f32x4 *>(base + w * wstride);
+              const f32x4 hi = *reinterpret_cast<const f32x4 *>(base + w * wstride + 4);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                a[i] += lo[i];
+                a[4 + i] += hi[i];
+              }
+            }
+          }
+          epi.store8(m, n, a);
+        }
+        return;
+      }
+    }
     for (int e = tid; e < BMT * BN; e += 512) {
       const int r = e / BN, col = e - r * BN;
       const int m = rows.out(r), n = n0 + col;
