@@ -384,34 +384,51 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
 
   // ---- normalise, or write the split partials. oacc[nb] holds O^T: lane
   // (hl, q) has query q = lane & 31 and, per element 4 jj + i, head column
-  // 32 nb + 8 jj + 4 hl + i, so each jj gives four consecutive columns (one
-  // 8-byte store)
+  // 32 nb + 8 jj + 4 hl + i. Each wave stages its 32 x HD tile row-major in
+  // the (now free) K/V stages and then stores whole 16-byte pieces of its
+  // rows, consecutive lanes along a row: every store instruction writes
+  // contiguous row segments instead of a 16-byte piece in each of 32 rows.
   {
     const float l_q = l_lane + __shfl_xor(l_lane, 32, 64);   // lanes q and q + 32 hold query q
-    const int row = qb * BQ + wave * 32 + (lane & 31);
-    if (row < GC) {
+    const bool whole = a.splits == 1;
+    const float sc = whole ? 1.f / l_q : 1.f;
+    // staged row pitch: 16 bytes of padding put consecutive rows four banks apart
+    constexpr int OP = HDP + 8;
+    static_assert(NWA * 32 * OP * 2 <= NS * 2 * TILE_B, "output staging fits in the stages");
+    __syncthreads();   // every wave has finished reading the K/V stages
+    uint16_t *stg = reinterpret_cast<uint16_t *>(stage_mem) + wave * 32 * OP;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int col = 32 * nb + 8 * jj + 4 * hl;
+        if (HDP == HD || col < HD) {
+          // partials travel in bf16: the merge rescales and sums them in
+          // fp32 and rounds the result to bf16 anyway; half the bytes of fp32
+          uint2 v;
+          v.x = pack_bf16x2(oacc[nb][4 * jj] * sc, oacc[nb][4 * jj + 1] * sc);
+          v.y = pack_bf16x2(oacc[nb][4 * jj + 2] * sc, oacc[nb][4 * jj + 3] * sc);
+          *reinterpret_cast<uint2 *>(stg + (lane & 31) * OP + col) = v;
+        }
+      }
+    const int row0 = qb * BQ + wave * 32;
+    constexpr int PPR = HD / 8;   // 16-byte pieces per row
+    for (int e = lane; e < 32 * PPR; e += 64) {
+      const int q = e / PPR, pc = e - q * PPR;
+      const int row = row0 + q;
+      if (row < GC) {
+        const int h = g * a.G + row / a.C, ii = row % a.C;
+        const int64_t r = static_cast<int64_t>(b) * a.C + ii;
+        uint16_t *dst = whole ? a.o + r * qcols + h * HD
+                              : a.opart + ((split * (static_cast<int64_t>(a.B) * a.C) + r) * a.Hq + h) * HD;
+        *reinterpret_cast<uint4 *>(dst + 8 * pc) = *reinterpret_cast<const uint4 *>(stg + q * OP + 8 * pc);
+      }
+    }
+    const int row = row0 + (lane & 31);
+    if (!whole && hl == 0 && row < GC) {
       const int h = g * a.G + row / a.C, ii = row % a.C;
       const int64_t r = static_cast<int64_t>(b) * a.C + ii;
-      const bool whole = a.splits == 1;
-      const float sc = whole ? 1.f / l_q : 1.f;
-      // partials travel in bf16: the merge rescales and sums them in fp32
-      // and rounds the result to bf16 anyway; half the bytes of fp32
-      uint16_t *dst = whole ? a.o + r * qcols + h * HD
-                            : a.opart + ((split * (static_cast<int64_t>(a.B) * a.C) + r) * a.Hq + h) * HD;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int col = 32 * nb + 8 * jj + 4 * hl;
-          if (HDP == HD || col < HD) {
-            uint2 v;
-            v.x = pack_bf16x2(oacc[nb][4 * jj] * sc, oacc[nb][4 * jj + 1] * sc);
-            v.y = pack_bf16x2(oacc[nb][4 * jj + 2] * sc, oacc[nb][4 * jj + 3] * sc);
-            *reinterpret_cast<uint2 *>(dst + col) = v;
-          }
-        }
-      if (!whole && hl == 0)
-        a.ml[(split * (static_cast<int64_t>(a.B) * a.C) + r) * a.Hq + h] = make_float2(m_ref, l_q);
+      a.ml[(split * (static_cast<int64_t>(a.B) * a.C) + r) * a.Hq + h] = make_float2(m_ref, l_q);
     }
   }
 }
