@@ -169,7 +169,6 @@ struct F32StoreEpi {
 // same units sit side by side in every tile. hid[m, f] = round(gelu(g) * u).
 struct GegluEpi {
   static constexpr bool kPair = true;
-  static constexpr bool kVec8 = false;
   const uint16_t *W;
   uint16_t *hid;
   int F;
