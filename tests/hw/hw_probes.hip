@@ -45,8 +45,11 @@ __global__ void __launch_bounds__(512) vmem_issue(const unsigned char *buf, unsi
   for (int n = 0; n < NL; ++n) {
     if (DIRECT) {
       const unsigned m0 = __builtin_amdgcn_readfirstlane(base + (wave * NL + n) * 1024);
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                   :: "s"(m0), "v"(src + n * 1024) : "memory", "m0");
+      // M0 is reserved by the compiler: keep its value across the block
+      unsigned saved;
+      asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                   "global_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+                   : "=&s"(saved) : "s"(m0), "v"(src + n * 1024) : "memory");
     } else {
       r[n] = *(const u32x4 *)(src + n * 1024);
     }
