@@ -14,7 +14,8 @@ pytestmark = pytest.mark.gpu
 SMALL = {
     # fp32 workload exactly as configured (C=16, P=8, d=32, MHA 2x16, V=64)
     "c1": dict(base="c1"),
-    # bf16, ragged rows (C=40 vs 32-row LM-head blocks), ragged keys (P+C=140)
+    # bf16, ragged rows (C=40 vs 32-row LM-head blocks), ragged keys (P+C=140);
+    # 64 vocabulary splits, more than the wide LM-head merge takes (32)
     "bf16-hd64": dict(base="c2", B=2, C=40, P=100, d=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
                       V=4096),
     "bf16-hd128": dict(base="c2", B=1, C=72, P=130, d=512, n_q_heads=4, n_kv_heads=2,
@@ -29,7 +30,7 @@ SMALL = {
     "bf16-vocab-1040-p0": dict(base="c2", B=2, C=40, P=0, d=256, n_q_heads=4, n_kv_heads=2,
                                head_dim=64, V=1040),
     # few query rows against a long prefix: 63 key tiles in 32 splits of two,
-    # more splits than the merge kernel prefetches (16)
+    # more splits than the wide attention merge takes (16): the general merge
     "bf16-long-prefix-32-splits": dict(base="c3", B=1, C=8, P=4000, d=256, n_q_heads=4, n_kv_heads=2,
                                        head_dim=64, V=512),
     # enough rows (2250 = 8 x 256 + 202) for the 256 x 256-tile projections,
