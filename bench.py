@@ -291,7 +291,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures the denoising step on exactly one GPU; this build has no "
+        print("bench.py measures the denoising step on exactly one GPU; the library has no "
               "multi-GPU path (no sharding, no collectives). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
