@@ -488,7 +488,7 @@ dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void 
                    int n_inline, uint64_t seed, int32_t *x_out, void *z_out,
                    const dg_taps *taps, float *lse, float *p0, hipStream_t st,
                    const dg::EntropyRows *ent = nullptr, const int32_t *frozen = nullptr,
-                   int P_cur = -1) {
+                   int P_cur = -1, bool h0_ready = false, void *h0_next = nullptr) {
   const dg::Shape &s = m->s;
   // attention over the first P_cur rows of caches with s.P rows per slice
   dg::Shape sa = s;
@@ -512,7 +512,10 @@ dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void 
     zc = taps && taps->p0E ? taps->p0E : m->ffw_u;
     frozen_c = nullptr;
   }
-  {
+  if (h0_ready) {
+    // the previous step's merge already wrote this step's embedding
+    if (n_inline || taps) return fail(DG_ERR_INVALID_ARG, "internal: a precomputed embedding with inline parameters or taps");
+  } else {
     StageTimer tm(m, 0, st);
     DG_HIP(dg::launch_embed(bf16, m->w.E, x_t, z_t, s.R(), s.d, s.V, h0, prm, inline_prm, n_inline,
                             st),
@@ -536,7 +539,7 @@ dg_status run_step(dg_model *m, const int32_t *x_t, const void *z_t, const void 
     {
       StageTimer tm(m, 5, st);
       DG_HIP(dg::launch_combine(true, m->lm, dg::lmhead_splits(s), x_t, prm, s, seed, x_out, zc,
-                              lse, best, ent, frozen_c, z_t, st),
+                              lse, best, ent, frozen_c, z_t, st, m->w.E, h0_next),
            "combine launch");
     }
   } else {
@@ -613,15 +616,24 @@ dg_status generate_steps(dg_model *m, const void *K_pre, const void *V_pre, int 
   DG_HIP(dg::launch_fill_zero(xb[0], R * sizeof(int32_t), st), "fill");
   DG_HIP(dg::launch_corrupt(xb[0], m->kappa, s.B, s.C, s.V, seed, xb[0], st), "corrupt launch");
   DG_HIP(dg::launch_fill_zero(zb[0], nz, st), "fill");
+  // Every step's constants are uploaded above, so the embedding pass only
+  // computes h0 = round(E[x] + z) from the previous step's outputs: where the
+  // merge can, it writes that for the next step itself (one pass fewer per
+  // step; the bf16 Step sampler without a feed-forward block, whose output
+  // z only exists after the merge).
+  bool h0_ready = false;
   for (int k = 0; k < steps; ++k) {
     const int cur = k & 1, nxt = cur ^ 1;
     const bool last = k == steps - 1;
     int32_t *xo = last ? x_out : xb[nxt];
     void *zo = (last && z_out) ? z_out : zb[nxt];
+    const bool fuse = !last && bf16 && !m->ffw_F &&
+                      dg::combine_embeds_next(true, m->lm, dg::lmhead_splits(s), s, zo);
     if (dg_status e = run_step(m, xb[cur], zb[cur], K_pre, V_pre, m->prm + static_cast<size_t>(k) * s.B,
                                nullptr, 0, seed + static_cast<uint64_t>(k), xo, zo, nullptr, nullptr,
-                               nullptr, st, nullptr, nullptr, P_cur))
+                               nullptr, st, nullptr, nullptr, P_cur, h0_ready, fuse ? m->h0 : nullptr))
       return e;
+    h0_ready = fuse;
   }
   return DG_OK;
 }

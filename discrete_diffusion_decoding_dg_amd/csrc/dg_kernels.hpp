@@ -184,10 +184,17 @@ hipError_t launch_lmhead_f32(const float *h1, const float *E, const StepParams *
 // With `ent` (entropy-bounded step) the per-row entropy, draw and argmax go
 // to ent instead of a Step select into x_out; rows of canvases marked in
 // `frozen` (nullable) copy z_t to z_out instead.
+// With `h0_next` (Step sampler only: no ent, no frozen) the merge also writes
+// the next step's embedding h0_next = round(E[x_out] + z_out) (E row-major
+// [V, d], tokens outside [0, V) as zero rows), exactly what the embedding
+// pass would compute from x_out and z_out; combine_embeds_next tells whether
+// it can for these arguments (bf16, the many-lane merge).
+bool combine_embeds_next(bool bf16, const void *work, int splits, const Shape &s, const void *z_out);
 hipError_t launch_combine(bool bf16, const void *work, int splits, const int32_t *x_t,
                           const StepParams *prm, const Shape &s, uint64_t seed, int32_t *x_out,
                           void *z_out, float *lse, int32_t *best, const EntropyRows *ent,
-                          const int32_t *frozen, const void *z_t, hipStream_t st);
+                          const int32_t *frozen, const void *z_t, hipStream_t st,
+                          const void *E = nullptr, void *h0_next = nullptr);
 
 // ---- k_select.hip ----
 constexpr int kSelectMaxC = 1024;   // canvas positions the select kernel sorts in LDS

@@ -280,7 +280,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const RowPartial *__restri
 // first column group also writes the per-row results. NP >= splits: the
 // row records are requested first and then NP partial loads (the surplus
 // ones re-read the last split and are not summed), so the statistics are
-// reduced while the partials are in flight.
+// reduced while the partials are in flight. With h0n every wave also settles
+// the row's token and writes its columns of the next step's embedding.
 template <int NP>
 __global__ void __launch_bounds__(256) combine_wide_kernel(const RowPartial *__restrict__ part,
                                                            const uint16_t *__restrict__ zpart, int splits,
@@ -292,7 +293,9 @@ __global__ void __launch_bounds__(256) combine_wide_kernel(const RowPartial *__r
                                                            float *__restrict__ lse,
                                                            int32_t *__restrict__ best, EntropyRows ent,
                                                            const int32_t *__restrict__ frozen,
-                                                           const uint16_t *__restrict__ z_t) {
+                                                           const uint16_t *__restrict__ z_t,
+                                                           const uint16_t *__restrict__ E, int V,
+                                                           uint16_t *__restrict__ h0n) {
   const int r = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cr = ((blockIdx.y * 4 + wave) * 64 + lane) * kCols;
@@ -332,8 +335,9 @@ __global__ void __launch_bounds__(256) combine_wide_kernel(const RowPartial *__r
   }
   // the row's Bernoulli decision while the loads are in flight
   const bool head = blockIdx.y == 0 && wave == 0;
+  const bool need_tok = head || h0n != nullptr;   // wave-uniform
   bool rs = false;
-  if (head && !ent.H) {
+  if (need_tok && !ent.H) {
     const int b = r / C, i = r - b * C;
     const u32x4 u = philox4x32_10(0u, static_cast<uint32_t>(i), static_cast<uint32_t>(b),
                                   kStreamBernoulli, k0, k1);
@@ -342,9 +346,9 @@ __global__ void __launch_bounds__(256) combine_wide_kernel(const RowPartial *__r
   const float M = wave_max_x(p.m);
   const float w = has ? exp2f(p.m - M) : 0.f;
   const float L = wave_sum_x(w * p.l);
+  // the Gumbel draw over splits (an exact tie goes to the lower split)
+  const int y = need_tok ? wave_argmax_lowest(has && p.arg >= 0, p.best, p.arg) : -1;
   if (head) {
-    // the Gumbel draw over splits (an exact tie goes to the lower split)
-    const int y = wave_argmax_lowest(has && p.arg >= 0, p.best, p.arg);
     if (ent.H) {
       const float S1 = wave_sum_x((has && p.l > 0.f) ? w * (p.s1 + (p.m - M) * p.l) : 0.f);
       const int det = wave_argmax_lowest(has && p.darg >= 0, p.dbest, p.darg);
@@ -362,6 +366,12 @@ __global__ void __launch_bounds__(256) combine_wide_kernel(const RowPartial *__r
     }
   }
   if (!active) return;
+  // the next step's embedding row piece, requested before the sums
+  uint4 e = make_uint4(0, 0, 0, 0);
+  if (h0n) {
+    const int tok = rs ? y : x_t[r];
+    if (tok >= 0 && tok < V) e = *reinterpret_cast<const uint4 *>(E + static_cast<int64_t>(tok) * d + c0);
+  }
   float acc[kCols];
 #pragma unroll
   for (int i = 0; i < kCols; ++i) acc[i] = 0.f;
@@ -381,14 +391,45 @@ __global__ void __launch_bounds__(256) combine_wide_kernel(const RowPartial *__r
 #pragma unroll
   for (int i = 0; i < kCols; ++i) acc[i] *= il;
   store8(z_out + rowoff + c0, acc);
+  if (h0n) {
+    // h0 = round(E[token] + z), z as stored (bf16), as the embedding pass
+    const uint32_t ew[4] = {e.x, e.y, e.z, e.w};
+    uint32_t hw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = bf16_to_f32(static_cast<uint16_t>(ew[i] & 0xFFFFu)) + bf16_to_f32(f32_to_bf16(acc[2 * i]));
+      const float hi = bf16_to_f32(static_cast<uint16_t>(ew[i] >> 16)) + bf16_to_f32(f32_to_bf16(acc[2 * i + 1]));
+      hw[i] = pack_bf16x2(lo, hi);
+    }
+    *reinterpret_cast<uint4 *>(h0n + rowoff + c0) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  }
 }
 
 }  // namespace
 
+namespace {
+// the many-lane merge applies: bf16 partials, at most 32 splits, whole
+// 16-byte column groups, aligned buffers, all splits below 2^31 bytes
+bool wide_merge(bool bf16, const void *work, int splits, const Shape &s, const void *z_out,
+                const void *z_t) {
+  const int R = s.R();
+  const char *zbase = static_cast<const char *>(work) + static_cast<size_t>(splits) * R * sizeof(RowPartial);
+  const bool aligned16 = ((reinterpret_cast<uintptr_t>(z_out) | reinterpret_cast<uintptr_t>(z_t) |
+                           reinterpret_cast<uintptr_t>(zbase)) & 15) == 0;
+  const bool fits31 = static_cast<int64_t>(splits) * R * s.d * 2 < (int64_t{1} << 31);
+  return bf16 && s.d % kCols == 0 && splits >= 1 && splits <= 32 && aligned16 && fits31;
+}
+}  // namespace
+
+bool combine_embeds_next(bool bf16, const void *work, int splits, const Shape &s, const void *z_out) {
+  return wide_merge(bf16, work, splits, s, z_out, nullptr);
+}
+
 hipError_t launch_combine(bool bf16, const void *work, int splits, const int32_t *x_t,
                           const StepParams *prm, const Shape &s, uint64_t seed, int32_t *x_out,
                           void *z_out, float *lse, int32_t *best, const EntropyRows *ent,
-                          const int32_t *frozen, const void *z_t, hipStream_t st) {
+                          const int32_t *frozen, const void *z_t, hipStream_t st, const void *E,
+                          void *h0_next) {
   const int R = s.R();
   if (R == 0) return hipSuccess;
   if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
@@ -401,18 +442,19 @@ hipError_t launch_combine(bool bf16, const void *work, int splits, const int32_t
   const dim3 grid(R, (s.d + strip - 1) / strip);
   const EntropyRows er = ent ? *ent : EntropyRows{nullptr, nullptr, nullptr};
   if (frozen && !z_t) return hipErrorInvalidValue;
+  if (h0_next && (ent || frozen || !E || (reinterpret_cast<uintptr_t>(E) & 15) ||
+                  (reinterpret_cast<uintptr_t>(h0_next) & 15) || !wide_merge(bf16, work, splits, s, z_out, z_t)))
+    return hipErrorInvalidValue;
   // 16-byte rows: z_out and z_t (and the partials, carved at 256-byte
   // offsets of the workspace) take 16-byte accesses at every 8th column
-  const bool aligned16 = ((reinterpret_cast<uintptr_t>(z_out) | reinterpret_cast<uintptr_t>(z_t) |
-                           reinterpret_cast<uintptr_t>(zbase)) & 15) == 0;
-  const bool fits31 = static_cast<int64_t>(splits) * R * s.d * 2 < (int64_t{1} << 31);
-  if (bf16 && s.d % kCols == 0 && splits <= 32 && aligned16 && fits31) {
+  if (wide_merge(bf16, work, splits, s, z_out, z_t)) {
     const dim3 wgrid(R, (s.d + 4 * 64 * kCols - 1) / (4 * 64 * kCols));
 #define DG_WIDE(NP)                                                                                   \
   hipLaunchKernelGGL((combine_wide_kernel<NP>), wgrid, dim3(256), 0, st, part,                        \
                      reinterpret_cast<const uint16_t *>(zbase), splits, x_t, prm, R, s.C, s.d, k0, k1, \
                      x_out, static_cast<uint16_t *>(z_out), lse, best, er, frozen,                    \
-                     static_cast<const uint16_t *>(z_t))
+                     static_cast<const uint16_t *>(z_t), static_cast<const uint16_t *>(E), s.V,       \
+                     static_cast<uint16_t *>(h0_next))
     if (splits <= 1)
       DG_WIDE(1);
     else if (splits <= 2)
