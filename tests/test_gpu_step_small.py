@@ -33,6 +33,18 @@ SMALL = {
     # more splits than the wide attention merge takes (16): the general merge
     "bf16-long-prefix-32-splits": dict(base="c3", B=1, C=8, P=4000, d=256, n_q_heads=4, n_kv_heads=2,
                                        head_dim=64, V=512),
+    # four query heads per kv head (400 stacked query rows per head), three
+    # ragged canvases: 17 vocabulary splits (the wide merge reading 15 surplus
+    # loads) and 13 attention splits
+    "bf16-gqa4-splits-17-13": dict(base="c2", B=3, C=100, P=1500, d=256, n_q_heads=4, n_kv_heads=1,
+                                   head_dim=64, V=2064),
+    # 25 vocabulary splits and 7 attention splits, two canvases
+    "bf16-gqa4-splits-25-7": dict(base="c2", B=2, C=100, P=700, d=256, n_q_heads=4, n_kv_heads=1,
+                                  head_dim=64, V=3136),
+    # 33 vocabulary splits, one more than the wide LM-head merge takes (the
+    # general merge), and 13 attention splits
+    "bf16-gqa4-splits-33-13": dict(base="c2", B=1, C=40, P=1500, d=256, n_q_heads=4, n_kv_heads=1,
+                                   head_dim=64, V=2064),
     # enough rows (2250 = 8 x 256 + 202) for the 256 x 256-tile projections,
     # with a ragged last row tile
     "bf16-many-rows": dict(base="c5", B=9, C=250, P=70, d=256, n_q_heads=4, n_kv_heads=4,
