@@ -44,7 +44,7 @@ struct Geo {
   static constexpr int HDP = (HD + 31) / 32 * 32;   // padded head dim
   static constexpr int NPC = HDP / 8;               // 16-byte pieces per row incl. padding
   static constexpr int NPR = HD / 8;                // pieces carrying data
-  static constexpr int KS = HDP / 16;               // k-steps of the score contraction
+  static constexpr int KS = (HD + 15) / 16;         // k-steps of the score contraction (data columns only)
   static constexpr int NB = HDP / 32;               // 32-column blocks of O
   static constexpr int TILE_B = NPC * BK * 16;      // bytes per tensor and stage
   static constexpr int NS = (2 * TILE_B * 4 <= kLdsBudget) ? 4 : 3;   // stages
@@ -167,7 +167,9 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
   const int qcols = a.Hq * HD;
 
   // padding pieces (head dims that are not a multiple of 32) are read by the
-  // contractions against zero Q / into discarded O columns and must be finite
+  // P V contraction into discarded O columns (and, for a head dim that ends in
+  // half a 16-wide k-step, by the score contraction against zero Q): they must
+  // be finite
   if constexpr (NPC > NPR) {
     for (int c = tid; c < NS * 2 * (NPC - NPR) * BK; c += NWA * 64) {
       const int key = c % BK, rest = c / BK;
