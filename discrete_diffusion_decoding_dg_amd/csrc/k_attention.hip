@@ -252,6 +252,12 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
   wait_vmcnt<0>();
   for (int t = tile0; t < tile_end && t < tile0 + NS - 1; ++t) issue_tile(t);
 
+  // byte offsets of this lane's K fragments inside a stage: piece p = 2 ks +
+  // hl starts at p * BK * 16, and its key slot XOR 4 (p & 3) takes one value
+  // for even ks and one for odd ks; key block mb adds 32 keys (bit 5 of the
+  // key, which the XOR leaves alone). Everything else is an immediate.
+  const uint32_t koff_e = hl * BK * 16 + ((lane & 31) ^ (4 * (hl & 3))) * 16;
+  const uint32_t koff_o = hl * BK * 16 + ((lane & 31) ^ (4 * ((2 + hl) & 3))) * 16;
   f32x16 oacc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x16{};
@@ -274,23 +280,17 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
     const uint8_t *Ks = stage_mem + (tile % NS) * 2 * TILE_B;
     const uint8_t *Vs = Ks + TILE_B;
 
-    // ---- S^T for 64 keys (two 32-key blocks); SCH accumulator chains per
-    // block shorten the MFMA dependency chains where registers allow
-    constexpr int SCH = (HD > 128) ? 1 : 2;
-    f32x16 sacc[2][2];
+    // ---- S^T for 64 keys (two 32-key blocks, one accumulator chain each)
+    const uint8_t *Ke = Ks + koff_e, *Ko = Ks + koff_o;
+    f32x16 sacc[2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      sacc[mb][0] = f32x16{};
-      sacc[mb][1] = f32x16{};
-    }
+    for (int mb = 0; mb < 2; ++mb) sacc[mb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int p = 2 * ks + hl;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8 *>(Ks + p * BK * 16 + kslot(mb * 32 + (lane & 31), p) * 16);
-        sacc[mb][ks % SCH] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], sacc[mb][ks % SCH], 0, 0, 0);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(((ks & 1) ? Ko : Ke) + ks * 2 * BK * 16 + mb * 32 * 16);
+        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], sacc[mb], 0, 0, 0);
       }
     }
     // element e = 4 jj + i of block mb: key 32 mb + 8 jj + 4 hl + i of this
@@ -302,9 +302,7 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        sv[mb][e] = (SCH == 2) ? sacc[mb][0][e] + sacc[mb][1][e] : sacc[mb][0][e];
-      }
+      for (int e = 0; e < 16; ++e) sv[mb][e] = sacc[mb][e];
     if (kv0 + BK > Lk) {   // the last, partial tile: keys past the end drop out
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
