@@ -1,6 +1,7 @@
 // Hardware probes behind the kernel designs (MI355X, gfx950): the issue cost
 // of vector-memory loads per CU, the MFMA instruction rates, LDS read
-// bandwidth, and the back-to-back launch interval. Every access stays inside
+// bandwidth, the back-to-back launch interval, and how MFMAs and VALU
+// instructions share a SIMD. Every access stays inside
 // its buffer; every loop has a fixed trip count. Times in shader clocks come
 // from s_memtime, wall times from HIP events.
 #include <hip/hip_runtime.h>
@@ -156,6 +157,87 @@ __global__ void __launch_bounds__(512) lds_rate(unsigned long long *out, unsigne
 
 __global__ void empty_kernel() {}
 
+// ---- E: MFMA and VALU sharing a SIMD. Each wave runs EITER rounds of 4
+// independent v_mfma_f32_32x32x16_bf16 chains with NV independent v_fma_f32
+// after each MFMA (the order pinned by scheduling groups). ROLES: the four
+// older waves (one per SIMD) issue only the MFMAs and the four younger only the
+// FMAs. Clocks per round over each CU, from the first wave's start to the last
+// wave's end, averaged over the blocks.
+constexpr int EITER = 2000;
+template <int NV, bool ROLES>
+__global__ void __launch_bounds__(512) mfma_valu(float *out, unsigned long long *stamps) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (tid + i));
+    b[i] = (__bf16)(0.002f * (tid - i));
+  }
+  f32x16 c0{}, c1{}, c2{}, c3{};
+  float x[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) x[k] = tid * 0.01f + k;
+  const bool mf = !ROLES || wave < 4, va = !ROLES || wave >= 4;
+  const unsigned long long t0 = __builtin_readcyclecounter();
+  if (mf && va) {
+    for (int it = 0; it < EITER; ++it) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        f32x16 &c = m == 0 ? c0 : m == 1 ? c1 : m == 2 ? c2 : c3;
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) x[(m * NV + k) & 31] = fmaf(x[(m * NV + k) & 31], 1.0001f, 0.5f);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+      }
+    }
+  } else if (mf) {
+    for (int it = 0; it < EITER; ++it) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+  } else {
+    for (int it = 0; it < EITER; ++it) {
+#pragma unroll
+      for (int k = 0; k < 4 * NV; ++k) x[k & 31] = fmaf(x[k & 31], 1.0001f, 0.5f);
+    }
+  }
+  const unsigned long long t1 = __builtin_readcyclecounter();
+  float s = 0.f;
+  for (int e = 0; e < 16; ++e) s += c0[e] + c1[e] + c2[e] + c3[e];
+  for (int k = 0; k < 32; ++k) s += x[k];
+  out[blockIdx.x * blockDim.x + tid] = s;
+  if ((tid & 63) == 0) {
+    stamps[(blockIdx.x * 8 + wave) * 2] = t0;
+    stamps[(blockIdx.x * 8 + wave) * 2 + 1] = t1;
+  }
+}
+
+// one E configuration: 256 blocks of `threads` (one block per CU: 100 KB of
+// dynamic LDS each), clocks per round over the CU
+template <int NV, bool ROLES>
+static double mfma_valu_span(int threads, float *out, unsigned long long *stamps) {
+  const int blocks = 256;
+  for (int rep = 0; rep < 2; ++rep) {
+    hipLaunchKernelGGL((mfma_valu<NV, ROLES>), dim3(blocks), dim3(threads), 100 * 1024, 0, out, stamps);
+    CHECK(hipGetLastError());
+    CHECK(hipDeviceSynchronize());
+  }
+  std::vector<unsigned long long> h(blocks * 16);
+  CHECK(hipMemcpy(h.data(), stamps, h.size() * 8, hipMemcpyDeviceToHost));
+  double span = 0;
+  for (int b = 0; b < blocks; ++b) {
+    unsigned long long lo = ~0ull, hi = 0;
+    for (int w = 0; w < threads / 64; ++w) {
+      lo = h[(b * 8 + w) * 2] < lo ? h[(b * 8 + w) * 2] : lo;
+      hi = h[(b * 8 + w) * 2 + 1] > hi ? h[(b * 8 + w) * 2 + 1] : hi;
+    }
+    span += static_cast<double>(hi - lo);
+  }
+  return span / blocks / EITER;
+}
+
 int main() {
   unsigned *sink;
   CHECK(hipMalloc(&sink, 4));
@@ -259,6 +341,27 @@ int main() {
                   bytes / mx, bytes / mn);
     }
     CHECK(hipFree(out));
+  }
+  // E
+  {
+    float *out;
+    unsigned long long *stamps;
+    CHECK(hipMalloc(&out, 256 * 512 * 4));
+    CHECK(hipMalloc(&stamps, 256 * 16 * 8));
+    for (int threads : {256, 512}) {
+      std::printf("mfma_valu %d wave(s)/SIMD, 4 MFMA 32x32x16 + 4 NV FMA per wave and round, CU clocks per round:",
+                  threads / 256);
+      std::printf(" NV=0 %.0f", mfma_valu_span<0, false>(threads, out, stamps));
+      std::printf(" NV=4 %.0f", mfma_valu_span<4, false>(threads, out, stamps));
+      std::printf(" NV=8 %.0f", mfma_valu_span<8, false>(threads, out, stamps));
+      std::printf(" NV=16 %.0f\n", mfma_valu_span<16, false>(threads, out, stamps));
+    }
+    std::printf("mfma_valu split roles (per SIMD one wave 4 MFMA, one wave 4 NV FMA per round), CU clocks per round:");
+    std::printf(" NV=4 %.0f", mfma_valu_span<4, true>(512, out, stamps));
+    std::printf(" NV=8 %.0f", mfma_valu_span<8, true>(512, out, stamps));
+    std::printf(" NV=16 %.0f\n", mfma_valu_span<16, true>(512, out, stamps));
+    CHECK(hipFree(out));
+    CHECK(hipFree(stamps));
   }
   CHECK(hipFree(sink));
   return 0;
