@@ -250,7 +250,6 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
   // would wait for every outstanding load (vmcnt 0) before the first score
   // MFMA of each tile, which would drain the pipeline every tile
   wait_vmcnt<0>();
-  for (int t = tile0; t < tile_end && t < tile0 + NS - 1; ++t) issue_tile(t);
 
   // byte offsets of this lane's K fragments inside a stage: piece p = 2 ks +
   // hl starts at p * BK * 16, and its key slot XOR 4 (p & 3) takes one value
@@ -266,23 +265,12 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
   const int tr_key = 4 * (g4 >> 1) + ((lane & 15) >> 2);
   const int tr_col = 16 * (g4 & 1) + 4 * (lane & 3);
 
-  for (int tile = tile0; tile < tile_end; ++tile) {
-    // this wave's loads of `tile` have landed once at most those of the
-    // tiles issued after it are outstanding (MINL or MINL + 1 per tile for a
-    // loading wave, none for the others; MINL is the safe bound); the barrier
-    // makes every wave's loads visible and frees the stage read during the
-    // previous tile
-    int after = tile_end - 1 - tile;
-    if (after > NS - 2) after = NS - 2;
-    wait_vmcnt_steps<MINL, NS - 2>(after);
-    __syncthreads();
-    if (tile + NS - 1 < tile_end) issue_tile(tile + NS - 1);
+  // ---- S^T for the 64 keys of a tile (two 32-key blocks, one accumulator
+  // chain each) into sacc
+  f32x16 sacc[2];
+  auto scores = [&](const int tile) __attribute__((always_inline)) {
     const uint8_t *Ks = stage_mem + (tile % NS) * 2 * TILE_B;
-    const uint8_t *Vs = Ks + TILE_B;
-
-    // ---- S^T for 64 keys (two 32-key blocks, one accumulator chain each)
     const uint8_t *Ke = Ks + koff_e, *Ko = Ks + koff_o;
-    f32x16 sacc[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) sacc[mb] = f32x16{};
 #pragma unroll
@@ -293,6 +281,12 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
         sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[ks], sacc[mb], 0, 0, 0);
       }
     }
+  };
+
+  // ---- the scores of a tile (in sacc) to P: row max, lazy rescale of O and
+  // l, exponentials
+  bf16x8 pa[4];
+  auto softmax = [&](const int tile) __attribute__((always_inline)) {
     // element e = 4 jj + i of block mb: key 32 mb + 8 jj + 4 hl + i of this
     // tile. Raw scores here; the scale folds into the exponent below
     // (scale_log2 > 0, so the max commutes with it).
@@ -345,7 +339,6 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
     // (block mb = kk / 2, half kk2 = kk % 2) the A operand is elements
     // 8 kk2 .. 8 kk2 + 7 of block mb, i.e. keys 16 kk + 4 hl + [0, 4) and
     // 16 kk + 8 + 4 hl + [0, 4)
-    bf16x8 pa[4];
     float psum = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -358,11 +351,14 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
         pa[2 * mb + (e >> 3)][e & 7] = static_cast<__bf16>(p);
       }
     l_lane += psum;
+  };
 
-    // ---- O += P V; the B operand of column block nb and step kk is read
-    // transposed: source lane S supplies key 16 kk + 4 (g / 2) + j (+ 8 for
-    // the second read) at columns 32 nb + 16 (g % 2) + 4 q, with g = S / 16,
-    // j = (S % 16) / 4, q = S % 4
+  // ---- O += P V; the B operand of column block nb and step kk is read
+  // transposed: source lane S supplies key 16 kk + 4 (g / 2) + j (+ 8 for
+  // the second read) at columns 32 nb + 16 (g % 2) + 4 q, with g = S / 16,
+  // j = (S % 16) / 4, q = S % 4
+  auto pv = [&](const int tile) __attribute__((always_inline)) {
+    const uint8_t *Vs = stage_mem + (tile % NS) * 2 * TILE_B + TILE_B;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
@@ -380,6 +376,50 @@ __global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
         oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, pa[kk], oacc[nb], 0, 0, 0);
       }
     }
+  };
+
+  // Skewed schedule (8-wave blocks, at least four stages): waves w and w + 4
+  // share a SIMD, and phases in which both issue only MFMAs or only VALU work
+  // add up. The older waves take each tile in order (scores, softmax, P V);
+  // the younger ones run the softmax and P V of the previous tile and then the
+  // scores of this one, so each SIMD's two waves are in different phases for
+  // two of the three. The younger waves read V of tile - 1 during step tile:
+  // after the barrier of step tile the free stage is that of tile - 2, which
+  // takes tile + NS - 2 (two tiles of lookahead instead of three).
+  constexpr bool SKEW = NWA == 8 && NS >= 4;
+  constexpr int AHEAD = SKEW ? NS - 2 : NS - 1;   // tiles issued ahead of the current one, plus it
+  const bool lag = SKEW && wave >= 4;
+  for (int t = tile0; t < tile_end && t < tile0 + AHEAD; ++t) issue_tile(t);
+  // this wave's loads of `tile` have landed once at most those of the tiles
+  // issued after it are outstanding (MINL or MINL + 1 per tile for a loading
+  // wave, none for the others; MINL is the safe bound); the barrier makes
+  // every wave's loads visible and frees the stage read last. Both loops
+  // pass the same barriers.
+  auto top = [&](const int tile) __attribute__((always_inline)) {
+    int after = tile_end - 1 - tile;
+    if (after > AHEAD - 1) after = AHEAD - 1;
+    wait_vmcnt_steps<MINL, AHEAD - 1>(after);
+    __syncthreads();
+    if (tile + AHEAD < tile_end) issue_tile(tile + AHEAD);
+  };
+  if (!lag) {
+    for (int tile = tile0; tile < tile_end; ++tile) {
+      top(tile);
+      scores(tile);
+      softmax(tile);
+      pv(tile);
+    }
+  } else if (tile0 < tile_end) {
+    top(tile0);
+    scores(tile0);
+    for (int tile = tile0 + 1; tile < tile_end; ++tile) {
+      top(tile);
+      softmax(tile - 1);
+      pv(tile - 1);
+      scores(tile);
+    }
+    softmax(tile_end - 1);
+    pv(tile_end - 1);
   }
 
   // ---- normalise, or write the split partials. oacc[nb] holds O^T: lane
