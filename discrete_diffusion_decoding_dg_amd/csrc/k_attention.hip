@@ -14,10 +14,14 @@
 // loads, NS tiles in flight. Per tile and wave:
 //   S^T[key, query] = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as the
 //   A operand, the wave's Q rows held in registers as B). A lane then holds 16
-//   keys of one query, and the k-slot order of the O += P V contraction is
-//   chosen to match, so P goes from the score accumulators to the A operand
-//   without leaving registers; V is read transposed from LDS
-//   (ds_read_b64_tr_b16) as the B operand.
+//   keys of one query, and the k-slot order of the O^T += V^T P^T contraction
+//   is chosen to match, so P goes from the score accumulators to the B
+//   operand without leaving registers; V is read transposed from LDS
+//   (ds_read_b64_tr_b16) as the A operand. Accumulating O^T gives each lane
+//   one query and four consecutive head columns per accumulator group.
+// In 8-wave blocks the younger wave of each SIMD runs one tile behind in its
+// softmax and P V (skewed schedule), so that the SIMD's two waves are not in
+// the same phase (MFMA or VALU) at the same time.
 // The online softmax runs in log2 units with a reference maximum that moves
 // only when a score exceeds it by more than 2^8 (one ballot per tile; the
 // rare move rescales O), so P <= 2^8 and no per-tile O rescale is needed.
