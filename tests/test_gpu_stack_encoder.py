@@ -27,6 +27,11 @@ CASES = {
     # width 2816, head_dim 176
     "bf16-hd176-L2": dict(base="c4", B=1, C=24, P=64, d=2816, n_q_heads=16, n_kv_heads=8,
                           head_dim=176, V=1024, n_layers=2, mlp_hidden=128, pos=10, n=30),
+    # a 256-token chunk after 300 history rows with four query heads per kv
+    # head: 8-wave causal attention blocks (the skewed schedule, 5 splits of
+    # two key tiles), then a 44-token chunk
+    "bf16-L2-8-wave-skew": dict(base="c2", B=4, C=256, P=640, d=512, n_q_heads=8, n_kv_heads=2,
+                                head_dim=64, V=2048, n_layers=2, mlp_hidden=256, pos=300, n=300),
     # experts in every layer, all selected (no routing decision to drift)
     "bf16-moe-L2-all": dict(base="c2", B=2, C=40, P=100, d=256, n_q_heads=4, n_kv_heads=2,
                             head_dim=64, V=4096, n_layers=2, mlp_hidden=128, n_experts=4, top_k=4,

@@ -49,6 +49,11 @@ SMALL = {
     # with a ragged last row tile
     "bf16-many-rows": dict(base="c5", B=9, C=250, P=70, d=256, n_q_heads=4, n_kv_heads=4,
                            head_dim=64, V=4096),
+    # enough query blocks for 8-wave attention blocks at head_dim 64 (144
+    # blocks): the skewed schedule, in splits of two key tiles (the younger
+    # waves' loop runs once) with a ragged last tile (500 keys)
+    "bf16-hd64-8-wave-skew": dict(base="c2", B=9, C=200, P=300, d=256, n_q_heads=4, n_kv_heads=2,
+                                  head_dim=64, V=1024),
 }
 
 
