@@ -136,8 +136,13 @@ __device__ __forceinline__ void lds_dma16_sa(const void *base, uint32_t voff, ui
 }
 
 // CAUSAL: the causal encoder pass (canvas query i sees canvas keys 0..i).
-template <int HD, int NWA, bool CAUSAL>
-__global__ void __launch_bounds__(NWA * 64) attn_fwd_kernel(AttnArgs a) {
+// LB: the launch bound the registers are allocated for. 4-wave blocks run
+// one wave per SIMD, but given 512 registers the compiler parks the score
+// accumulators in AGPRs and copies them to VGPRs and back every tile; at head
+// dims up to 128 they are compiled as for 8-wave blocks (256 registers, all
+// of them VGPRs) and launched with 256 threads.
+template <int HD, int NWA, bool CAUSAL, int LB = (NWA == 4 && HD <= 128) ? 512 : NWA * 64>
+__global__ void __launch_bounds__(LB) attn_fwd_kernel(AttnArgs a) {
   constexpr int BQ = NWA * 32;                   // query rows per block
   using G_ = Geo<HD>;
   constexpr int HDP = G_::HDP, NPC = G_::NPC, NPR = G_::NPR, KS = G_::KS, NB = G_::NB;
